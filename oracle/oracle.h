@@ -1,0 +1,128 @@
+/*
+ * oracle.h -- plain, slow CPU oracle for the DynamiQ hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and
+ * the CPU-baseline leg of the benchmark may load this library.  The product
+ * path (the HIP library and its Python binding) never calls it, and the two
+ * share no code, headers, tables or constants.
+ *
+ * What is computed follows the DynamiQ pages:
+ *   - scribe notes (everythinginsigcomm), "Key idea and contribution":
+ *     groups of 16 and super-groups of 256 consecutive coordinates, per
+ *     super-group mean and squared l2 norm all-reduced, identical bit
+ *     allocation on every worker, reorder by bitwidth, hop-by-hop
+ *     decompress-accumulate-recompress, restore order and add back the mean,
+ *     non-uniform levels, hierarchical UINT8 group scales, correlated rounding;
+ *   - pith.science review, "What carries the argument" and Fig. 3 caption:
+ *     widths {2,4,8}, thresholds locked by T12 = 5/32 T24, T24 = 17/512 T48,
+ *     one scalar selects the allocation.
+ * Every step the pages leave open is fixed by a stated reading (the design
+ * document lists them); the oracle implements those readings literally.
+ *
+ * Floating point: IEEE fp32, round to nearest even, no contraction (built with
+ * -ffp-contract=off, no fast-math), denormals preserved.
+ *
+ * Threading: OpenMP over super-groups; every per-super-group computation is
+ * independent and every reduction is sequential or integer, so results do not
+ * depend on the thread count.
+ */
+#ifndef DQ_ORACLE_H
+#define DQ_ORACLE_H
+#include <stdint.h>
+#include <stddef.h>
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { OR_SG = 256, OR_GROUP = 16, OR_NGROUPS = 16 };
+enum { OR_RING = 0, OR_BUTTERFLY = 1 };
+enum { OR_BF16 = 0, OR_F32 = 1, OR_PACKED = 2 };
+enum { OR_CORRELATED = 0, OR_INDEPENDENT = 1 };
+
+typedef struct or_ctx or_ctx;
+
+/* threads (0 = OpenMP default) */
+void or_set_threads(int n);
+int or_get_threads(void);
+
+/* Philox4x32 with R rounds (the oracle uses R = 10). */
+void or_philox4x32(const uint32_t ctr[4], const uint32_t key[2], int rounds,
+                   uint32_t out[4]);
+
+/* Level table for width q with shape parameter eps (the method uses 1/2):
+ *   L[r], r = 0..2^q-1;  W[r] = fl32(65536 / (L[r+1] - L[r])), r = 0..2^q-2. */
+void or_levels(int q, double eps, float *L, float *W);
+
+/* Context for one simulated round.  n_coords % 256 == 0. */
+or_ctx *or_create(int64_t n_coords, int32_t n_workers, int32_t topology,
+                  float avg_bits);
+void or_destroy(or_ctx *c);
+void or_set_seed(or_ctx *c, uint64_t seed);
+void or_set_round(or_ctx *c, uint32_t round);
+void or_set_rounding(or_ctx *c, int32_t mode);
+void or_set_eps(or_ctx *c, double eps);
+
+/* Stage 1: per-worker statistics, called in rank order 0..n-1. */
+int or_stats(or_ctx *c, int32_t worker, const void *grad, int32_t dtype);
+/* Stage 2: global mean, allocation scalar rho and widths. */
+int or_allocate(or_ctx *c);
+/* Stage 3: stable partition by width. */
+int or_reorder(or_ctx *c);
+
+/* Accessors (host copies). */
+void or_get_stats(const or_ctx *c, float *sum, float *F, float *mu);
+uint32_t or_get_rho_bits(const or_ctx *c);
+void or_get_widths(const or_ctx *c, uint8_t *w);
+void or_get_perm(const or_ctx *c, int32_t *perm, int32_t *inv);
+void or_get_class_counts(const or_ctx *c, int64_t counts[3]);
+int64_t or_budget_bits(const or_ctx *c);
+int64_t or_count_bits(const or_ctx *c, uint32_t rho_bits);
+/* T12, T24, T48 for the scalar with bit pattern rho_bits. */
+void or_thresholds(uint32_t rho_bits, float out[3]);
+
+/* Region of part (m, part): bytes and per-class counts. */
+int64_t or_region_bytes(const or_ctx *c, int64_t m, int64_t part,
+                        int64_t counts_out[3]);
+
+/* Schedule steps.  `filter` (sorted global stream positions, may be NULL)
+ * restricts the work to those super-groups; other bytes are left untouched.
+ *   ring:      compress at step 0, hop at steps 1..n-1
+ *   butterfly: compress at level 1 (step 1), hop at levels 1..log2 n
+ *   n == 1:    compress at step 0 only */
+int or_compress(or_ctx *c, int32_t worker, int32_t step, const void *grad,
+                int32_t dtype, uint8_t *region_out, const int64_t *filter,
+                int64_t n_filter);
+int or_hop(or_ctx *c, int32_t worker, int32_t step, const uint8_t *region_in,
+           const void *local, int32_t local_kind, uint8_t *out0, uint8_t *out1,
+           const int64_t *filter, int64_t n_filter);
+int or_finalize(or_ctx *c, int64_t part, const uint8_t *region, float *out,
+                const int64_t *filter, int64_t n_filter);
+
+/* Part that worker `worker` ends the reduction with. */
+int64_t or_final_part(const or_ctx *c, int32_t worker);
+
+/* Whole simulated round (stats .. finalize); grads[w] are n_coords each. */
+int or_allreduce(or_ctx *c, const void *const *grads, int32_t dtype,
+                 float *out);
+
+/* Codec on one super-group with explicit 16-bit dithers (for statistical
+ * pins): encodes y[256] at width q and returns the decoded values. */
+void or_roundtrip_sg(const float *y, int32_t q, const uint16_t *dither,
+                     double eps, float *decoded, uint8_t *codes, float *scale,
+                     uint8_t *cg);
+/* Batch: K rows of y and dithers -> K rows of decoded values. */
+void or_roundtrip_batch(const float *y, int64_t K, int32_t q,
+                        const uint16_t *dither, double eps, float *decoded);
+/* The 256 dithers the oracle uses for super-group j in one quantisation
+ * event (mode, worker rank, event index). */
+void or_dithers(uint64_t seed, uint32_t round, int64_t j, int32_t mode,
+                int32_t worker, int32_t n_workers, int32_t event,
+                uint16_t *d);
+
+/* MXFP8 (OCP MX v1.0: block 32, E8M0 shared scale, E4M3 elements). */
+void or_mxfp8_roundtrip(const float *x, int64_t n, float *out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
