@@ -1,0 +1,624 @@
+// dq_api.cpp -- the C ABI of include/dq.h: plan state, argument checks, the
+// ring / butterfly schedules and launch sequencing.  All device work is
+// enqueued on the caller's stream; nothing here synchronises except
+// dq_get_info and dq_timing_read.
+#include "dq.h"
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "dq_internal.h"
+
+using namespace dq;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Launch {
+    int kind;
+    int64_t m, part;     // part processed (for coordinate counts), m = 0: whole vector
+    hipEvent_t e0, e1;
+};
+
+}  // namespace
+
+struct dq_plan {
+    int64_t d = 0, J = 0;
+    int32_t n = 1, topo = DQ_RING, L = 0;
+    float budget = 5.0f;
+    long long budget_bits = 0;
+    uint64_t seed = 1;
+    uint32_t round = 0;
+    int32_t rounding = DQ_ROUND_CORRELATED;
+    bool timing = false;
+
+    uint8_t *ws = nullptr;
+    size_t ws_bytes = 0;
+    dq_layout lay{};
+    int64_t nblk = 0;
+
+    int32_t stats_done = 0;
+    bool allocated = false, reordered = false;
+
+    std::vector<Launch> launches;
+    std::vector<hipEvent_t> pool;
+    dq_timing acc{};
+    int64_t host_counts[3] = {0, 0, 0};
+};
+
+namespace {
+
+Ctrl *ctrl_of(dq_plan *p) { return reinterpret_cast<Ctrl *>(p->ws + p->lay.ctrl); }
+float *f32_at(dq_plan *p, size_t off) { return reinterpret_cast<float *>(p->ws + off); }
+int32_t *i32_at(dq_plan *p, size_t off) { return reinterpret_cast<int32_t *>(p->ws + off); }
+int32_t *blkcnt_of(dq_plan *p) {
+    return reinterpret_cast<int32_t *>(p->ws + p->lay.ctrl + align_up(sizeof(Ctrl), kAlign));
+}
+
+void compute_layout(dq_plan *p) {
+    const size_t J = (size_t)p->J;
+    size_t off = 0;
+    p->lay.sum = off; off = align_up(off + 4 * J, kAlign);
+    p->lay.sumsq = off; off = align_up(off + 4 * J, kAlign);
+    p->lay.widths = off; off = align_up(off + J, kAlign);
+    p->lay.perm = off; off = align_up(off + 4 * J, kAlign);
+    p->lay.inv = off; off = align_up(off + 4 * J, kAlign);
+    p->lay.mu_stream = off; off = align_up(off + 4 * J, kAlign);
+    p->lay.ctrl = off;
+    off = align_up(off + sizeof(Ctrl), kAlign);
+    off = align_up(off + 4 * 3 * (size_t)p->nblk, kAlign);
+    p->lay.total = off;
+}
+
+hipError_t timed_begin(dq_plan *p, int kind, int64_t m, int64_t part, hipStream_t s, Launch &L) {
+    L.kind = kind;
+    L.m = m;
+    L.part = part;
+    L.e0 = L.e1 = nullptr;
+    if (!p->timing) return hipSuccess;
+    for (hipEvent_t *e : {&L.e0, &L.e1}) {
+        if (!p->pool.empty()) {
+            *e = p->pool.back();
+            p->pool.pop_back();
+        } else {
+            hipError_t err = hipEventCreate(e);
+            if (err != hipSuccess) return err;
+        }
+    }
+    return hipEventRecord(L.e0, s);
+}
+
+hipError_t timed_end(dq_plan *p, Launch &L, hipStream_t s) {
+    if (!p->timing) return hipSuccess;
+    hipError_t err = hipEventRecord(L.e1, s);
+    p->launches.push_back(L);
+    return err;
+}
+
+dq_status hip_status(hipError_t e) { return e == hipSuccess ? DQ_OK : DQ_EHIP; }
+
+// schedule: part written by a compress / processed by a hop
+struct SchedPart {
+    int64_t m, part;
+    bool two_children;
+};
+
+bool compress_part(const dq_plan *p, int32_t w, int32_t step, SchedPart &sp) {
+    sp.two_children = false;
+    if (p->n == 1) {
+        if (step != 0) return false;
+        sp.m = 1;
+        sp.part = 0;
+        return true;
+    }
+    if (p->topo == DQ_RING) {
+        if (step != 0) return false;
+        sp.m = p->n;
+        sp.part = w;
+        return true;
+    }
+    if (step != 1) return false;
+    sp.m = 2;
+    sp.part = ((int64_t)w >> (p->L - 1)) ^ 1;
+    return true;
+}
+
+bool hop_part(const dq_plan *p, int32_t w, int32_t step, SchedPart &sp) {
+    if (p->n == 1) return false;
+    if (p->topo == DQ_RING) {
+        if (step < 1 || step >= p->n) return false;
+        sp.m = p->n;
+        sp.part = ((int64_t)w - step % p->n + p->n) % p->n;
+        sp.two_children = false;
+        return true;
+    }
+    if (step < 1 || step > p->L) return false;
+    sp.m = (int64_t)1 << step;
+    sp.part = (int64_t)w >> (p->L - step);
+    sp.two_children = step < p->L;
+    return true;
+}
+
+int32_t event_of(const dq_plan *p, int32_t w, int32_t step) {
+    if (p->topo == DQ_BUTTERFLY && p->n > 1) return (step - 1) * p->n + w;
+    return w;
+}
+
+void fill_rng(const dq_plan *p, int32_t w, int32_t step, CodecArgs &a) {
+    a.key0 = (uint32_t)(p->seed & 0xFFFFFFFFu);
+    a.key1 = (uint32_t)(p->seed >> 32);
+    a.round = p->round;
+    if (p->rounding == DQ_ROUND_CORRELATED) {
+        a.tag = 0u;
+        a.stagger = (uint32_t)(((uint64_t)w * 65536u) / (uint64_t)p->n);
+    } else {
+        a.tag = (uint32_t)(1 + event_of(p, w, step));
+        a.stagger = 0u;
+    }
+}
+
+void fill_common(dq_plan *p, CodecArgs &a) {
+    std::memset(&a, 0, sizeof(a));
+    a.class_counts = ctrl_of(p)->class_counts;
+    a.perm = i32_at(p, p->lay.perm);
+    a.mu_stream = f32_at(p, p->lay.mu_stream);
+    a.n_workers_f = (float)p->n;
+}
+
+int64_t max_part_sg(const dq_plan *p, int64_t m) { return p->J / m + 3; }
+
+int local_of_kind(int32_t kind) {
+    if (kind == DQ_BF16) return kLocalBF16;
+    if (kind == DQ_F32) return kLocalF32;
+    if (kind == DQ_PACKED) return kLocalPacked;
+    return -1;
+}
+
+bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+}  // namespace
+
+namespace {
+
+struct ArenaPlan {
+    std::vector<size_t> off;  // slot offsets
+    size_t total = 0;
+};
+
+// ring: 2n slots of m = n; butterfly: per worker one compress slot (m = 2),
+// two child slots per level below the last, one slot for the last level;
+// n == 1: one slot of m = 1.
+ArenaPlan arena_plan(const dq_plan *p) {
+    ArenaPlan ap;
+    auto add = [&](int64_t m) {
+        ap.off.push_back(ap.total);
+        ap.total += dq_region_bytes_max(p, m);
+    };
+    if (p->n == 1) {
+        add(1);
+    } else if (p->topo == DQ_RING) {
+        for (int i = 0; i < 2 * p->n; i++) add(p->n);
+    } else {
+        for (int w = 0; w < p->n; w++) {
+            add(2);
+            for (int s = 1; s <= p->L; s++) {
+                if (s < p->L) {
+                    add((int64_t)1 << (s + 1));
+                    add((int64_t)1 << (s + 1));
+                } else {
+                    add(p->n);
+                }
+            }
+        }
+    }
+    return ap;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dq_status_string(int32_t s) {
+    switch (s) {
+        case DQ_OK: return "ok";
+        case DQ_EINVAL: return "invalid argument";
+        case DQ_EBUDGET: return "bit budget below 2 or NaN";
+        case DQ_ESTATE: return "call out of stage order";
+        case DQ_EWORKSPACE: return "workspace missing, too small or misaligned";
+        case DQ_ENULL: return "null pointer";
+        case DQ_EHIP: return "HIP runtime error";
+        case DQ_ENONFINITE: return "non-finite gradient value";
+        default: return "unknown status";
+    }
+}
+
+int32_t dq_version(void) { return 1; }
+
+dq_status dq_plan_create(int64_t n_coords, int32_t n_workers, int32_t topology, float avg_bits,
+                         dq_plan **out) {
+    if (!out) return DQ_ENULL;
+    *out = nullptr;
+    if (n_coords <= 0 || n_coords % kSG != 0 || n_workers < 1 || n_workers > 65536)
+        return DQ_EINVAL;
+    if (n_coords / kSG > (int64_t)0x7FFFFFFF - 4) return DQ_EINVAL;
+    if (topology != DQ_RING && topology != DQ_BUTTERFLY) return DQ_EINVAL;
+    int32_t L = 0;
+    while ((1 << L) < n_workers) L++;
+    if (topology == DQ_BUTTERFLY && (1 << L) != n_workers) return DQ_EINVAL;
+    if (!(avg_bits >= 2.0f)) return DQ_EBUDGET;
+    dq_plan *p = new (std::nothrow) dq_plan();
+    if (!p) return DQ_EINVAL;
+    p->d = n_coords;
+    p->J = n_coords / kSG;
+    p->n = n_workers;
+    p->topo = topology;
+    p->L = L;
+    p->budget = avg_bits;
+    p->budget_bits = (long long)std::floor((double)avg_bits * (double)p->J);
+    p->nblk = (p->J + kReorderSGPerBlock - 1) / kReorderSGPerBlock;
+    compute_layout(p);
+    *out = p;
+    return DQ_OK;
+}
+
+void dq_plan_destroy(dq_plan *p) {
+    if (!p) return;
+    for (auto &L : p->launches) {
+        if (L.e0) (void)hipEventDestroy(L.e0);
+        if (L.e1) (void)hipEventDestroy(L.e1);
+    }
+    for (auto e : p->pool) (void)hipEventDestroy(e);
+    delete p;
+}
+
+dq_status dq_plan_set_u64(dq_plan *p, int32_t option, uint64_t v) {
+    if (!p) return DQ_ENULL;
+    switch (option) {
+        case DQ_OPT_SEED: p->seed = v; return DQ_OK;
+        case DQ_OPT_ROUND:
+            if (v > 0xFFFFFFFFull) return DQ_EINVAL;
+            p->round = (uint32_t)v;
+            return DQ_OK;
+        case DQ_OPT_ROUNDING:
+            if (v != DQ_ROUND_CORRELATED && v != DQ_ROUND_INDEPENDENT) return DQ_EINVAL;
+            p->rounding = (int32_t)v;
+            return DQ_OK;
+        case DQ_OPT_TIMING:
+            if (v > 1) return DQ_EINVAL;
+            p->timing = v == 1;
+            return DQ_OK;
+        default: return DQ_EINVAL;
+    }
+}
+
+size_t dq_workspace_bytes(const dq_plan *p) { return p ? p->lay.total : 0; }
+
+dq_status dq_plan_bind(dq_plan *p, void *ws, size_t bytes) {
+    if (!p || !ws) return DQ_ENULL;
+    if (bytes < p->lay.total || !aligned(ws, kAlign)) return DQ_EWORKSPACE;
+    p->ws = static_cast<uint8_t *>(ws);
+    p->ws_bytes = bytes;
+    p->stats_done = 0;
+    p->allocated = p->reordered = false;
+    return DQ_OK;
+}
+
+dq_status dq_workspace_layout(const dq_plan *p, dq_layout *out) {
+    if (!p || !out) return DQ_ENULL;
+    *out = p->lay;
+    return DQ_OK;
+}
+
+size_t dq_region_bytes_max(const dq_plan *p, int64_t m) {
+    if (!p || m < 1 || m > p->n || (p->n % m) != 0) return 0;
+    const int64_t N = max_part_sg(p, m);
+    return align_up((size_t)N * (256 + 4 + 16) + 16, kAlign);
+}
+
+int64_t dq_final_part(const dq_plan *p, int32_t w) {
+    if (!p || w < 0 || w >= p->n) return -1;
+    if (p->n == 1) return 0;
+    if (p->topo == DQ_RING) return (w + 1) % p->n;
+    return w;
+}
+
+dq_status dq_stats(dq_plan *p, int32_t w, const void *grad, int32_t kind, void *stream) {
+    if (!p || !grad) return DQ_ENULL;
+    if (!p->ws) return DQ_EWORKSPACE;
+    if (w < 0 || w >= p->n || (kind != DQ_BF16 && kind != DQ_F32) || !aligned(grad, 16))
+        return DQ_EINVAL;
+    if (w == 0) {
+        p->stats_done = 0;
+        p->allocated = p->reordered = false;
+    }
+    if (w != p->stats_done) return DQ_ESTATE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (w == 0) {
+        hipError_t e = launch_zero(reinterpret_cast<uint32_t *>(&ctrl_of(p)->nonfinite), 1, s);
+        if (e != hipSuccess) return DQ_EHIP;
+    }
+    StatsArgs a;
+    a.grad = grad;
+    a.J = p->J;
+    a.sum = f32_at(p, p->lay.sum);
+    a.sumsq = f32_at(p, p->lay.sumsq);
+    a.first = w == 0;
+    a.nonfinite = &ctrl_of(p)->nonfinite;
+    Launch L;
+    hipError_t e = timed_begin(p, DQ_K_STATS, 0, 0, s, L);
+    if (e == hipSuccess) e = launch_stats(a, kind == DQ_F32, s);
+    if (e == hipSuccess) e = timed_end(p, L, s);
+    if (e != hipSuccess) return DQ_EHIP;
+    p->stats_done++;
+    return DQ_OK;
+}
+
+dq_status dq_allocate(dq_plan *p, void *stream) {
+    if (!p) return DQ_ENULL;
+    if (!p->ws) return DQ_EWORKSPACE;
+    if (p->stats_done != p->n) return DQ_ESTATE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    AllocArgs a;
+    a.sumsq = f32_at(p, p->lay.sumsq);
+    a.J = p->J;
+    a.budget = p->budget_bits;
+    a.ctrl = ctrl_of(p);
+    a.widths = p->ws + p->lay.widths;
+    a.blkcnt = blkcnt_of(p);
+    a.nblk = p->nblk;
+    Launch L;
+    hipError_t e = timed_begin(p, DQ_K_ALLOCATE, 0, 0, s, L);
+    // counts[] and class_counts[] start at zero (a fill kernel, graph-safe)
+    const int64_t nzero = (int64_t)(offsetof(Ctrl, rho_bits) / 4);
+    if (e == hipSuccess) e = launch_zero(reinterpret_cast<uint32_t *>(a.ctrl), nzero, s);
+    for (int step = 0; step < kBisectSteps && e == hipSuccess; step++)
+        e = launch_alloc_step(a, step, s);
+    if (e == hipSuccess) e = launch_alloc_final(a, s);
+    if (e == hipSuccess) e = timed_end(p, L, s);
+    if (e != hipSuccess) return DQ_EHIP;
+    p->allocated = true;
+    p->reordered = false;
+    return DQ_OK;
+}
+
+dq_status dq_reorder(dq_plan *p, void *stream) {
+    if (!p) return DQ_ENULL;
+    if (!p->ws) return DQ_EWORKSPACE;
+    if (!p->allocated) return DQ_ESTATE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    ReorderArgs a;
+    a.widths = p->ws + p->lay.widths;
+    a.sum = f32_at(p, p->lay.sum);
+    a.denom = (float)(256 * p->n);
+    a.J = p->J;
+    a.ctrl = ctrl_of(p);
+    a.blkcnt = blkcnt_of(p);
+    a.nblk = p->nblk;
+    a.perm = i32_at(p, p->lay.perm);
+    a.inv = i32_at(p, p->lay.inv);
+    a.mu_stream = f32_at(p, p->lay.mu_stream);
+    Launch L;
+    hipError_t e = timed_begin(p, DQ_K_REORDER, 0, 0, s, L);
+    if (e == hipSuccess) e = launch_reorder(a, s);
+    if (e == hipSuccess) e = timed_end(p, L, s);
+    if (e != hipSuccess) return DQ_EHIP;
+    p->reordered = true;
+    return DQ_OK;
+}
+
+dq_status dq_compress(dq_plan *p, int32_t w, int32_t step, const void *grad, int32_t kind,
+                      void *out, void *stream) {
+    if (!p || !grad || !out) return DQ_ENULL;
+    if (!p->ws) return DQ_EWORKSPACE;
+    if (!p->reordered) return DQ_ESTATE;
+    SchedPart sp;
+    if (w < 0 || w >= p->n || (kind != DQ_BF16 && kind != DQ_F32) || !compress_part(p, w, step, sp))
+        return DQ_EINVAL;
+    if (!aligned(grad, 16) || !aligned(out, 16)) return DQ_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    CodecArgs a;
+    fill_common(p, a);
+    fill_rng(p, w, step, a);
+    a.m = sp.m;
+    a.part = sp.part;
+    a.grad = grad;
+    a.out0 = static_cast<uint8_t *>(out);
+    Launch L;
+    hipError_t e = timed_begin(p, DQ_K_COMPRESS, sp.m, sp.part, s, L);
+    if (e == hipSuccess) e = launch_codec(a, kCompress, local_of_kind(kind), max_part_sg(p, sp.m), s);
+    if (e == hipSuccess) e = timed_end(p, L, s);
+    return hip_status(e);
+}
+
+dq_status dq_hop(dq_plan *p, int32_t w, int32_t step, const void *in, const void *local,
+                 int32_t local_kind, void *out0, void *out1, void *stream) {
+    if (!p || !in || !local || !out0) return DQ_ENULL;
+    if (!p->ws) return DQ_EWORKSPACE;
+    if (!p->reordered) return DQ_ESTATE;
+    SchedPart sp;
+    if (w < 0 || w >= p->n || !hop_part(p, w, step, sp)) return DQ_EINVAL;
+    const bool want_packed = p->topo == DQ_BUTTERFLY && step >= 2;
+    if (want_packed != (local_kind == DQ_PACKED)) return DQ_EINVAL;
+    if (local_kind != DQ_BF16 && local_kind != DQ_F32 && local_kind != DQ_PACKED) return DQ_EINVAL;
+    if (sp.two_children && !out1) return DQ_ENULL;
+    if (!aligned(in, 16) || !aligned(local, 16) || !aligned(out0, 16) ||
+        (sp.two_children && !aligned(out1, 16)))
+        return DQ_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    CodecArgs a;
+    fill_common(p, a);
+    fill_rng(p, w, step, a);
+    a.m = sp.m;
+    a.part = sp.part;
+    a.two_children = sp.two_children ? 1 : 0;
+    a.region_in = static_cast<const uint8_t *>(in);
+    if (local_kind == DQ_PACKED) a.region_own = static_cast<const uint8_t *>(local);
+    else a.grad = local;
+    a.out0 = static_cast<uint8_t *>(out0);
+    a.out1 = static_cast<uint8_t *>(sp.two_children ? out1 : out0);
+    Launch L;
+    const int kindk = local_kind == DQ_PACKED ? DQ_K_HOP_PACKED : DQ_K_HOP_GRAD;
+    hipError_t e = timed_begin(p, kindk, sp.m, sp.part, s, L);
+    if (e == hipSuccess) e = launch_codec(a, kHop, local_of_kind(local_kind), max_part_sg(p, sp.m), s);
+    if (e == hipSuccess) e = timed_end(p, L, s);
+    return hip_status(e);
+}
+
+dq_status dq_finalize(dq_plan *p, int64_t part, const void *region, float *out, void *stream) {
+    if (!p || !region || !out) return DQ_ENULL;
+    if (!p->ws) return DQ_EWORKSPACE;
+    if (!p->reordered) return DQ_ESTATE;
+    if (part < 0 || part >= p->n) return DQ_EINVAL;
+    if (!aligned(region, 16) || !aligned(out, 16)) return DQ_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    CodecArgs a;
+    fill_common(p, a);
+    a.m = p->n;
+    a.part = part;
+    a.region_in = static_cast<const uint8_t *>(region);
+    a.out_f32 = out;
+    Launch L;
+    hipError_t e = timed_begin(p, DQ_K_FINALIZE, p->n, part, s, L);
+    if (e == hipSuccess) e = launch_codec(a, kFinalize, kLocalNone, max_part_sg(p, p->n), s);
+    if (e == hipSuccess) e = timed_end(p, L, s);
+    return hip_status(e);
+}
+
+// ---- whole round -----------------------------------------------------------
+
+
+size_t dq_arena_bytes(const dq_plan *p) { return p ? arena_plan(p).total : 0; }
+
+dq_status dq_allreduce(dq_plan *p, const void *const *grads, int32_t kind, void *arena,
+                       size_t arena_bytes, float *out, void *stream) {
+    if (!p || !grads || !arena || !out) return DQ_ENULL;
+    if (!p->ws) return DQ_EWORKSPACE;
+    const ArenaPlan ap = arena_plan(p);
+    if (arena_bytes < ap.total || !aligned(arena, kAlign)) return DQ_EWORKSPACE;
+    uint8_t *A = static_cast<uint8_t *>(arena);
+    dq_status st;
+    for (int w = 0; w < p->n; w++)
+        if ((st = dq_stats(p, w, grads[w], kind, stream)) != DQ_OK) return st;
+    if ((st = dq_allocate(p, stream)) != DQ_OK) return st;
+    if ((st = dq_reorder(p, stream)) != DQ_OK) return st;
+    const int n = p->n;
+    if (n == 1) {
+        if ((st = dq_compress(p, 0, 0, grads[0], kind, A + ap.off[0], stream)) != DQ_OK) return st;
+        return dq_finalize(p, 0, A + ap.off[0], out, stream);
+    }
+    if (p->topo == DQ_RING) {
+        auto slot = [&](int w, int t) { return A + ap.off[(size_t)(t & 1) * n + w]; };
+        for (int w = 0; w < n; w++)
+            if ((st = dq_compress(p, w, 0, grads[w], kind, slot(w, 0), stream)) != DQ_OK) return st;
+        for (int t = 1; t < n; t++)
+            for (int w = 0; w < n; w++)
+                if ((st = dq_hop(p, w, t, slot((w - 1 + n) % n, t - 1), grads[w], kind, slot(w, t),
+                                 nullptr, stream)) != DQ_OK)
+                    return st;
+        for (int w = 0; w < n; w++)
+            if ((st = dq_finalize(p, dq_final_part(p, w), slot(w, n - 1), out, stream)) != DQ_OK)
+                return st;
+        return DQ_OK;
+    }
+    const int L = p->L;
+    const size_t per_w = 1 + (size_t)(2 * (L - 1) + 1);
+    auto cmp = [&](int w) { return A + ap.off[w * per_w]; };
+    auto lvl = [&](int w, int s, int h) { return A + ap.off[w * per_w + 1 + 2 * (s - 1) + h]; };
+    for (int w = 0; w < n; w++)
+        if ((st = dq_compress(p, w, 1, grads[w], kind, cmp(w), stream)) != DQ_OK) return st;
+    for (int s = 1; s <= L; s++) {
+        for (int w = 0; w < n; w++) {
+            const int partner = w ^ (n >> s);
+            const int keep = (w >> (L - s)) & 1;
+            const void *in = s == 1 ? (const void *)cmp(partner) : (const void *)lvl(partner, s - 1, keep);
+            const void *local = s == 1 ? grads[w] : (const void *)lvl(w, s - 1, keep);
+            const int32_t lk = s == 1 ? kind : DQ_PACKED;
+            if ((st = dq_hop(p, w, s, in, local, lk, lvl(w, s, 0), s < L ? lvl(w, s, 1) : nullptr,
+                             stream)) != DQ_OK)
+                return st;
+        }
+    }
+    for (int w = 0; w < n; w++)
+        if ((st = dq_finalize(p, dq_final_part(p, w), lvl(w, L, 0), out, stream)) != DQ_OK) return st;
+    return DQ_OK;
+}
+
+// ---- inspection --------------------------------------------------------------
+
+dq_status dq_get_info(dq_plan *p, dq_info *out, void *stream) {
+    if (!p || !out) return DQ_ENULL;
+    if (!p->ws) return DQ_EWORKSPACE;
+    if (!p->allocated) return DQ_ESTATE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Ctrl c;
+    if (hipMemcpyAsync(&c, ctrl_of(p), sizeof(Ctrl), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return DQ_EHIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return DQ_EHIP;
+    std::memset(out, 0, sizeof(*out));
+    out->rho_bits = c.rho_bits;
+    std::memcpy(&out->rho, &c.rho_bits, 4);
+    out->t12 = 85.0f * out->rho;
+    out->t24 = 544.0f * out->rho;
+    out->t48 = 16384.0f * out->rho;
+    out->budget_bits = p->budget_bits;
+    int64_t used = 0;
+    for (int k = 0; k < 3; k++) {
+        out->class_counts[k] = (int64_t)c.class_counts[k];
+        p->host_counts[k] = out->class_counts[k];
+        used += out->class_counts[k] * (2 << k);
+    }
+    out->used_bits = used;
+    out->achieved_bits = (double)used / (double)p->J;
+    out->nonfinite = c.nonfinite ? 1 : 0;
+    return out->nonfinite ? DQ_ENONFINITE : DQ_OK;
+}
+
+dq_status dq_timing_read(dq_plan *p, dq_timing *out) {
+    if (!p || !out) return DQ_ENULL;
+    // exact per-part super-group counts need the class counts of this round
+    Ctrl c;
+    std::memset(&c, 0, sizeof(c));
+    if (p->ws && p->allocated && !p->launches.empty()) {
+        if (hipEventSynchronize(p->launches.back().e1) != hipSuccess) return DQ_EHIP;
+        if (hipMemcpy(&c, ctrl_of(p), sizeof(Ctrl), hipMemcpyDeviceToHost) != hipSuccess)
+            return DQ_EHIP;
+    }
+    for (auto &L : p->launches) {
+        float ms = 0.0f;
+        if (hipEventSynchronize(L.e1) != hipSuccess) return DQ_EHIP;
+        if (hipEventElapsedTime(&ms, L.e0, L.e1) != hipSuccess) return DQ_EHIP;
+        p->acc.ms[L.kind] += ms;
+        p->acc.launches[L.kind] += 1;
+        int64_t sg = 0;
+        if (L.m == 0) {
+            sg = p->J;
+        } else {
+            for (int k = 0; k < 3; k++) {
+                const int64_t Ck = (int64_t)c.class_counts[k];
+                sg += (L.part + 1) * Ck / L.m - L.part * Ck / L.m;
+            }
+        }
+        p->acc.coords[L.kind] += sg * kSG;
+        p->pool.push_back(L.e0);
+        p->pool.push_back(L.e1);
+    }
+    p->launches.clear();
+    *out = p->acc;
+    std::memset(&p->acc, 0, sizeof(p->acc));
+    return DQ_OK;
+}
+
+size_t dq_mxfp8_arena_bytes(const dq_plan *p) { (void)p; return 0; }
+
+dq_status dq_mxfp8_allreduce(dq_plan *p, const void *const *grads, int32_t kind, void *arena,
+                             size_t arena_bytes, float *out, void *stream) {
+    (void)p; (void)grads; (void)kind; (void)arena; (void)arena_bytes; (void)out; (void)stream;
+    return DQ_EINVAL;
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// dq_internal.h -- declarations shared by the C ABI (dq_api.cpp) and the HIP
+// kernels (dq_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dq {
+
+constexpr int kSG = 256;          // coordinates per super-group
+constexpr int kGroup = 16;        // coordinates per group (one lane owns one group)
+constexpr int kGroupsPerSG = 16;
+constexpr int kSGPerBlock = 16;   // codec kernels: 4 waves x 4 super-groups
+constexpr int kReorderSGPerBlock = 1024;  // allocation/reorder: 256 threads x 4
+constexpr int kBisectSteps = 32;  // step 0 tests rho = 0, steps 1..31 bisect
+
+// control block at the head of the workspace's control area
+struct Ctrl {
+    unsigned long long counts[kBisectSteps];  // sum of widths at each bisection probe
+    unsigned long long class_counts[3];       // super-groups at 2, 4, 8 bits
+    uint32_t rho_bits;
+    int32_t nonfinite;
+    int32_t pad[2];
+};
+
+enum Mode { kCompress = 0, kHop = 1, kFinalize = 2 };
+enum Local { kLocalNone = 0, kLocalBF16 = 1, kLocalF32 = 2, kLocalPacked = 3 };
+
+// arguments of one codec launch (compress / hop / finalize) on one part
+struct CodecArgs {
+    const unsigned long long *class_counts;  // device, C_2, C_4, C_8
+    int64_t m, part;                         // part `part` of m
+    int32_t two_children;                    // hop output split into parts 2c, 2c+1 of 2m
+    const int32_t *perm;
+    const float *mu_stream;
+    const void *grad;                        // local gradient (bf16 / f32)
+    const uint8_t *region_in;                // incoming region (hop, finalize)
+    const uint8_t *region_own;               // own packed region (butterfly level >= 2)
+    uint8_t *out0, *out1;                    // output region(s)
+    float *out_f32;                          // finalize output, original order
+    float n_workers_f;                       // finalize: fl(n * mu)
+    uint32_t key0, key1, round, tag, stagger;
+};
+
+struct StatsArgs {
+    const void *grad;
+    int64_t J;
+    float *sum, *sumsq;
+    int32_t first;
+    int32_t *nonfinite;
+};
+
+struct AllocArgs {
+    const float *sumsq;
+    int64_t J;
+    long long budget;   // floor(B * J)
+    Ctrl *ctrl;
+    uint8_t *widths;
+    int32_t *blkcnt;    // [3][nblk]
+    int64_t nblk;
+};
+
+struct ReorderArgs {
+    const uint8_t *widths;
+    const float *sum;
+    float denom;        // fl(256 n)
+    int64_t J;
+    const Ctrl *ctrl;
+    int32_t *blkcnt;    // [3][nblk] counts in, offsets out (scan)
+    int64_t nblk;
+    int32_t *perm, *inv;
+    float *mu_stream;
+};
+
+struct Mxfp8Args {
+    const void *grad;        // local gradient (hop / compress), original order
+    int32_t grad_f32;
+    const uint8_t *in;       // incoming region: codes[nblk32] then scales
+    uint8_t *out;
+    float *out_f32;          // finalize
+    int64_t coord_lo, ncoord; // coordinates of the part (multiple of 256)
+    int32_t mode;            // kCompress / kHop / kFinalize
+};
+
+// launchers (dq_kernels.hip); each returns the hipError_t of its launch
+hipError_t launch_zero(uint32_t *p, int64_t n, hipStream_t s);
+hipError_t launch_stats(const StatsArgs &a, int f32, hipStream_t s);
+hipError_t launch_alloc_step(const AllocArgs &a, int step, hipStream_t s);
+hipError_t launch_alloc_final(const AllocArgs &a, hipStream_t s);
+hipError_t launch_reorder(const ReorderArgs &a, hipStream_t s);
+hipError_t launch_codec(const CodecArgs &a, int mode, int local, int64_t max_sg, hipStream_t s);
+hipError_t launch_mxfp8(const Mxfp8Args &a, hipStream_t s);
+
+}  // namespace dq

@@ -1,0 +1,651 @@
+// dq_kernels.hip -- HIP kernels of the DynamiQ hot path for gfx950 (CDNA4).
+//
+// Everything here is HBM-streaming integer/fp32 work: no stage is a dense
+// contraction, so nothing uses MFMA.  Kernels are written for 64-lane
+// wavefronts:
+//   * stats: 32 lanes per super-group (SG), each lane one 128-bit load of 8
+//     bf16; the sum order is 8 sequential adds then an xor tree over 32 lanes;
+//   * codec (compress / hop / finalize): one 16-lane DPP row per SG, one lane
+//     per group of 16 coordinates, so group scales are per-lane scalars and the
+//     SG maximum is a 4-step DPP row reduction; 128-bit loads of codes and of
+//     the local bf16 gradient; level tables staged in LDS once per block;
+//   * allocation: integer counts only (order-free), bisection on the fp32 bit
+//     pattern of the scalar with no host round trip;
+//   * reorder: per-block counts, one scan block, stable per-block scatter.
+//
+// Numerics follow the readings shared with the CPU oracle: fp32, round to
+// nearest even, no contraction (built with -ffp-contract=off), correctly
+// rounded division.
+#include "dq_internal.h"
+#include "dq_tables.h"
+
+namespace dq {
+
+__device__ const LevelTables g_tables = kLevelTables;
+
+// ---------------------------------------------------------------------------
+// small device helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL,
+                                                      0xF, 0xF, false));
+}
+
+// maximum over the 16 lanes of a DPP row (all lanes get the result)
+__device__ __forceinline__ float row_max16(float x) {
+    x = fmaxf(x, dpp_mov<0xB1>(x));   // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp_mov<0x4E>(x));   // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp_mov<0x141>(x));  // row_half_mirror
+    x = fmaxf(x, dpp_mov<0x140>(x));  // row_mirror
+    return x;
+}
+
+// Philox4x32 with 10 rounds (Salmon et al., SC'11): per round two 32x32->64
+// products of the even words; high halves xored with the odd words and the key;
+// words permuted; key advanced by the Weyl constants between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t &x0, uint32_t &x1, uint32_t &x2,
+                                              uint32_t &x3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; r++) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint32_t la = 0xD2511F53u * x0, ha = __umulhi(0xD2511F53u, x0);
+        const uint32_t lb = 0xCD9E8D57u * x2, hb = __umulhi(0xCD9E8D57u, x2);
+        const uint32_t y0 = hb ^ x1 ^ k0, y2 = ha ^ x3 ^ k1;
+        x0 = y0;
+        x1 = lb;
+        x2 = y2;
+        x3 = la;
+    }
+}
+
+// Scale unit of a super-group: fl(A/255), raised until 255 units cover A.
+__device__ __forceinline__ float scale_unit(float A) {
+    float s = A / 255.0f;
+    while (255.0f * s < A) s = __uint_as_float(__float_as_uint(s) + 1u);
+    return s;
+}
+
+// Smallest c in [0, 255] with fl(c * s) >= a (exists because fl(255 s) >= A >= a).
+__device__ __forceinline__ int group_code(float a, float s) {
+    if (s == 0.0f) return 0;
+    float est = a * __builtin_amdgcn_rcpf(s);
+    int c = (int)ceilf(fminf(est, 255.0f));
+    c = min(max(c, 0), 255);
+    while (c > 0 && (float)(c - 1) * s >= a) c--;
+    while (c < 255 && (float)c * s < a) c++;
+    return c;
+}
+
+// Interval search over NL = 16 or 256 levels: r = largest r <= NL-2 with L[r] <= v.  The
+// closed-form inverse of the level map gives an estimate that is r or r-1
+// (its error is far below half an index); one compare against the next level
+// settles it.  Returns r and the level / weight of interval r.
+template <int NL>
+__device__ __forceinline__ int search_levels(float v, const Row4 *rows, float &Lr, float &Wr) {
+    constexpr float hq = 0.5f * float(NL - 1);
+    const float av = fabsf(v);
+    const float sq = __builtin_amdgcn_sqrtf(fmaf(8.0f, av, 1.0f));
+    const float t = (sq - 1.0f) * 0.5f;
+    const float u = copysignf(t, v);
+    const float rc = fmaf(hq, u, hq - 0.5f);
+    int est = (int)floorf(rc);
+    est = min(max(est, 0), NL - 2);
+    const Row4 row = rows[est];
+    const bool up = v >= row.l1;
+    Lr = up ? row.l1 : row.l0;
+    Wr = up ? row.w1 : row.w0;
+    return est + (up ? 1 : 0);
+}
+
+__device__ __forceinline__ int search_levels2(float v, float &Lr, float &Wr) {
+    constexpr float l0 = kLevelTables.L2[0], l1 = kLevelTables.L2[1], l2 = kLevelTables.L2[2];
+    constexpr float w0 = kLevelTables.W2[0], w1 = kLevelTables.W2[1], w2 = kLevelTables.W2[2];
+    const int r = (v >= l1 ? 1 : 0) + (v >= l2 ? 1 : 0);
+    Lr = r == 0 ? l0 : (r == 1 ? l1 : l2);
+    Wr = r == 0 ? w0 : (r == 1 ? w1 : w2);
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// parts and regions
+// ---------------------------------------------------------------------------
+
+struct PartInfo {
+    int64_t lo[3], cnt[3], N;
+    int64_t offc[3], offs, offg;
+};
+
+__device__ __forceinline__ void part_info(const unsigned long long *C, int64_t m, int64_t c,
+                                          PartInfo &p) {
+    int64_t base = 0, off = 0;
+    p.N = 0;
+#pragma unroll
+    for (int k = 0; k < 3; k++) {
+        const int64_t Ck = (int64_t)C[k];
+        const int64_t a = c * Ck / m, b = (c + 1) * Ck / m;
+        p.lo[k] = base + a;
+        p.cnt[k] = b - a;
+        p.N += b - a;
+        base += Ck;
+    }
+#pragma unroll
+    for (int k = 0; k < 3; k++) {
+        p.offc[k] = off;
+        off += p.cnt[k] * 32 * (2 << k);
+    }
+    p.offs = off;
+    off += 4 * p.N;
+    off = (off + 15) & ~int64_t(15);
+    p.offg = off;
+}
+
+struct SharedTables {
+    float dec2[4];
+    float dec4[16];
+    float dec8[256];
+    Row4 r4[15];
+    Row4 r8[255];
+};
+
+template <int B>
+__device__ __forceinline__ float level_of(const SharedTables &T, uint32_t code) {
+    if constexpr (B == 2) return T.dec2[code];
+    else if constexpr (B == 4) return T.dec4[code];
+    else return T.dec8[code];
+}
+
+// load / store the 2B bytes of one group's codes (B = bits per code)
+template <int B>
+__device__ __forceinline__ void load_codes(const uint8_t *p, uint32_t (&w)[B / 2]) {
+    if constexpr (B == 8) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(p);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else if constexpr (B == 4) {
+        const uint2 v = *reinterpret_cast<const uint2 *>(p);
+        w[0] = v.x; w[1] = v.y;
+    } else {
+        w[0] = *reinterpret_cast<const uint32_t *>(p);
+    }
+}
+
+template <int B>
+__device__ __forceinline__ void store_codes(uint8_t *p, const uint32_t (&w)[B / 2]) {
+    if constexpr (B == 8) {
+        *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else if constexpr (B == 4) {
+        *reinterpret_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
+    } else {
+        *reinterpret_cast<uint32_t *>(p) = w[0];
+    }
+}
+
+// decode the group (lane g) of super-group t (part-local), class-local index idx
+template <int Q>
+__device__ __forceinline__ void decode_group(const uint8_t *region, int64_t offc, int64_t offs,
+                                             int64_t offg, int64_t t, int64_t idx, int g,
+                                             const SharedTables &T, float (&x)[16]) {
+    uint32_t w[Q / 2];
+    load_codes<Q>(region + offc + idx * (32 * Q) + g * (2 * Q), w);
+    const float s = *reinterpret_cast<const float *>(region + offs + 4 * t);
+    const uint32_t c = region[offg + 16 * t + g];
+    const float sigma = (float)c * s;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const uint32_t code = (w[(i * Q) / 32] >> ((i * Q) % 32)) & ((1u << Q) - 1u);
+        x[i] = sigma * level_of<Q>(T, code);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// codec kernel: compress / hop / finalize on one part
+// ---------------------------------------------------------------------------
+
+// Q = bits per code of this super-group's class; K = its class index
+template <int Q, int MODE, int LOCAL>
+__device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo *P, int64_t t,
+                                         int64_t idx, int g, const SharedTables &T) {
+    constexpr int K = Q == 2 ? 0 : (Q == 4 ? 1 : 2);
+    const PartInfo &pin = P[0];
+    const int64_t pos = pin.lo[K] + idx;          // stream position
+    const int64_t j = a.perm[pos];                // original super-group
+    float y[16];
+
+    if constexpr (MODE != kCompress) decode_group<Q>(a.region_in, pin.offc[K], pin.offs, pin.offg,
+                                                     t, idx, g, T, y);
+
+    if constexpr (MODE == kFinalize) {
+        const float add = a.n_workers_f * a.mu_stream[pos];
+        float4 *o = reinterpret_cast<float4 *>(a.out_f32 + j * kSG + g * kGroup);
+#pragma unroll
+        for (int v = 0; v < 4; v++)
+            o[v] = make_float4(y[4 * v] + add, y[4 * v + 1] + add, y[4 * v + 2] + add, y[4 * v + 3] + add);
+    } else {
+    const float mu = a.mu_stream[pos];
+    if constexpr (LOCAL == kLocalBF16) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(
+            static_cast<const uint16_t *>(a.grad) + j * kSG + g * kGroup);
+        const uint4 h0 = src[0], h1 = src[1];
+        const uint32_t hw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const float e0 = bf16_lo(hw[i]) - mu, e1 = bf16_hi(hw[i]) - mu;
+            if constexpr (MODE == kHop) {
+                y[2 * i] = y[2 * i] + e0;
+                y[2 * i + 1] = y[2 * i + 1] + e1;
+            } else {
+                y[2 * i] = e0;
+                y[2 * i + 1] = e1;
+            }
+        }
+    } else if constexpr (LOCAL == kLocalF32) {
+        const float4 *src = reinterpret_cast<const float4 *>(
+            static_cast<const float *>(a.grad) + j * kSG + g * kGroup);
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const float4 f = src[v];
+            const float e[4] = {f.x - mu, f.y - mu, f.z - mu, f.w - mu};
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                if constexpr (MODE == kHop) y[4 * v + i] = y[4 * v + i] + e[i];
+                else y[4 * v + i] = e[i];
+            }
+        }
+    } else if constexpr (LOCAL == kLocalPacked) {
+        float own[16];
+        decode_group<Q>(a.region_own, pin.offc[K], pin.offs, pin.offg, t, idx, g, T, own);
+#pragma unroll
+        for (int i = 0; i < 16; i++) y[i] = y[i] + own[i];
+    }
+
+    // ---- encode ----
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(y[i]));
+    const float A = row_max16(amax);
+    const float s = scale_unit(A);
+    const int c = group_code(amax, s);
+    const float sigma = (float)c * s;
+    const float inv = sigma == 0.0f ? 0.0f : 1.0f / sigma;
+
+    uint32_t w[Q / 2];
+#pragma unroll
+    for (int i = 0; i < Q / 2; i++) w[i] = 0u;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        // 8 dithers of coordinates 8h..8h+7 of this group from one Philox call
+        uint32_t x0 = 2u * g + h, x1 = (uint32_t)j, x2 = a.round, x3 = a.tag;
+        philox4x32_10(x0, x1, x2, x3, a.key0, a.key1);
+        const uint32_t d[4] = {x0, x1, x2, x3};
+#pragma unroll
+        for (int ii = 0; ii < 8; ii++) {
+            const int i = 8 * h + ii;
+            const float v = fminf(fmaxf(y[i] * inv, -1.0f), 1.0f);
+            float Lr, Wr;
+            int r;
+            if constexpr (Q == 2) r = search_levels2(v, Lr, Wr);
+            else if constexpr (Q == 4) r = search_levels<16>(v, T.r4, Lr, Wr);
+            else r = search_levels<256>(v, T.r8, Lr, Wr);
+            const float P = (v - Lr) * Wr;
+            const uint32_t d0 = (ii & 1) ? (d[ii >> 1] >> 16) : (d[ii >> 1] & 0xFFFFu);
+            const uint32_t dd = (d0 + a.stagger) & 0xFFFFu;
+            const uint32_t code = (uint32_t)r + (((float)dd + 0.5f) < P ? 1u : 0u);
+            w[(i * Q) / 32] |= code << ((i * Q) % 32);
+        }
+    }
+
+    // ---- output slot (one region, or the child the super-group falls in) ----
+    // The part layouts live in LDS (P[0] = this part, P[1], P[2] = its
+    // children); the child is picked by index so only its fields are read.
+    int sel = 0;
+    int64_t idx_o = idx;
+    uint8_t *region = a.out0;
+    if (MODE == kHop && a.two_children) {
+        const int64_t split = P[1].cnt[K];
+        const bool second = idx >= split;
+        sel = second ? 2 : 1;
+        idx_o = second ? idx - split : idx;
+        const uintptr_t r0 = reinterpret_cast<uintptr_t>(a.out0);
+        const uintptr_t r1 = reinterpret_cast<uintptr_t>(a.out1);
+        region = reinterpret_cast<uint8_t *>(second ? r1 : r0);
+    }
+    const PartInfo &po = P[sel];
+    int64_t t_o = idx_o;
+    if constexpr (K > 0) t_o += po.cnt[0];
+    if constexpr (K > 1) t_o += po.cnt[1];
+    if (sel == 0) t_o = t;
+    const int64_t offc = po.offc[K], offs = po.offs, offg = po.offg;
+    store_codes<Q>(region + offc + idx_o * (32 * Q) + g * (2 * Q), w);
+    region[offg + 16 * t_o + g] = (uint8_t)c;
+    if (g == 0) *reinterpret_cast<float *>(region + offs + 4 * t_o) = s;
+    }
+}
+
+template <int MODE, int LOCAL>
+__global__ __launch_bounds__(256) void k_codec(CodecArgs a) {
+    __shared__ __align__(16) SharedTables T;
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) T.dec8[i] = g_tables.L8[i];
+    for (int i = threadIdx.x; i < 255; i += blockDim.x) T.r8[i] = g_tables.R8[i];
+    if (threadIdx.x < 16) T.dec4[threadIdx.x] = g_tables.L4[threadIdx.x];
+    if (threadIdx.x < 15) T.r4[threadIdx.x] = g_tables.R4[threadIdx.x];
+    if (threadIdx.x < 4) T.dec2[threadIdx.x] = g_tables.L2[threadIdx.x];
+    __syncthreads();
+
+    // part layouts: computed once per block, read back as LDS broadcasts
+    __shared__ PartInfo P[3];
+    if (threadIdx.x == 0) {
+        part_info(a.class_counts, a.m, a.part, P[0]);
+        if (MODE == kHop && a.two_children) {
+            part_info(a.class_counts, 2 * a.m, 2 * a.part, P[1]);
+            part_info(a.class_counts, 2 * a.m, 2 * a.part + 1, P[2]);
+        }
+    }
+    __syncthreads();
+    const PartInfo &pin = P[0];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane & 15, row = lane >> 4;
+    for (int64_t base = (int64_t)blockIdx.x * kSGPerBlock; base < pin.N;
+         base += (int64_t)gridDim.x * kSGPerBlock) {
+        const int64_t t = base + wave * 4 + row;
+        if (t >= pin.N) continue;
+        const int64_t n0 = pin.cnt[0], n01 = pin.cnt[0] + pin.cnt[1];
+        if (t < n0) codec_sg<2, MODE, LOCAL>(a, P, t, t, g, T);
+        else if (t < n01) codec_sg<4, MODE, LOCAL>(a, P, t, t - n0, g, T);
+        else codec_sg<8, MODE, LOCAL>(a, P, t, t - n01, g, T);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// statistics
+// ---------------------------------------------------------------------------
+
+template <int F32>
+__global__ __launch_bounds__(256) void k_stats(StatsArgs a) {
+    const int half = (threadIdx.x >> 5) & 1, wave = threadIdx.x >> 6, l = threadIdx.x & 31;
+    for (int64_t base = (int64_t)blockIdx.x * 8; base < a.J; base += (int64_t)gridDim.x * 8) {
+        const int64_t j = base + wave * 2 + half;
+        const bool live = j < a.J;
+        float e[8];
+        if (live) {
+            if (F32) {
+                const float4 *src = reinterpret_cast<const float4 *>(
+                    static_cast<const float *>(a.grad) + j * kSG + l * 8);
+                const float4 f0 = src[0], f1 = src[1];
+                e[0] = f0.x; e[1] = f0.y; e[2] = f0.z; e[3] = f0.w;
+                e[4] = f1.x; e[5] = f1.y; e[6] = f1.z; e[7] = f1.w;
+            } else {
+                const uint4 h = *reinterpret_cast<const uint4 *>(
+                    static_cast<const uint16_t *>(a.grad) + j * kSG + l * 8);
+                e[0] = bf16_lo(h.x); e[1] = bf16_hi(h.x); e[2] = bf16_lo(h.y); e[3] = bf16_hi(h.y);
+                e[4] = bf16_lo(h.z); e[5] = bf16_hi(h.z); e[6] = bf16_lo(h.w); e[7] = bf16_hi(h.w);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; i++) e[i] = 0.0f;
+        }
+        float s = e[0], q = e[0] * e[0];
+#pragma unroll
+        for (int i = 1; i < 8; i++) {
+            s = s + e[i];
+            const float sq = e[i] * e[i];
+            q = q + sq;
+        }
+#pragma unroll
+        for (int delta = 16; delta >= 1; delta >>= 1) {
+            s = s + __shfl_xor(s, delta, 32);
+            q = q + __shfl_xor(q, delta, 32);
+        }
+        if (live && l == 0) {
+            float S = s, F = q;
+            if (!a.first) {
+                S = a.sum[j] + s;
+                F = a.sumsq[j] + q;
+            }
+            a.sum[j] = S;
+            a.sumsq[j] = F;
+            if (!(__builtin_isfinite(S) && __builtin_isfinite(F))) atomicOr(a.nonfinite, 1);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// allocation: bisection on the fp32 bit pattern of rho, integer counts
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v) {
+    __shared__ unsigned long long part[4];
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+    __syncthreads();
+    unsigned long long t = 0;
+    if (threadIdx.x == 0) t = part[0] + part[1] + part[2] + part[3];
+    return t;
+}
+
+// Replays the probes done so far; returns false once the search has converged.
+__device__ __forceinline__ bool bisect_state(const Ctrl *c, long long budget, int upto,
+                                             uint32_t &lo, uint32_t &hi) {
+    lo = 0u;
+    hi = 0x7F800000u;
+    for (int k = 1; k < upto; k++) {
+        if (hi - lo <= 1u) return false;
+        const uint32_t mid = lo + (hi - lo) / 2u;
+        if ((long long)c->counts[k] <= budget) hi = mid;
+        else lo = mid;
+    }
+    return hi - lo > 1u;
+}
+
+__global__ __launch_bounds__(256) void k_alloc_step(AllocArgs a, int step) {
+    Ctrl *c = a.ctrl;
+    uint32_t probe = 0u;
+    if (step > 0) {
+        if ((long long)c->counts[0] <= a.budget) return;
+        uint32_t lo, hi;
+        if (!bisect_state(c, a.budget, step, lo, hi)) return;
+        probe = lo + (hi - lo) / 2u;
+    }
+    const float rho = __uint_as_float(probe);
+    const float t4 = 544.0f * rho, t8 = 16384.0f * rho;
+    unsigned long long local = 0;
+    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < a.J;
+         j += (int64_t)gridDim.x * blockDim.x) {
+        const float F = a.sumsq[j];
+        local += F >= t8 ? 8u : (F >= t4 ? 4u : 2u);
+    }
+    const unsigned long long tot = block_sum_u64(local);
+    if (threadIdx.x == 0) atomicAdd(&c->counts[step], tot);
+}
+
+__device__ __forceinline__ uint32_t final_rho_bits(const Ctrl *c, long long budget) {
+    if ((long long)c->counts[0] <= budget) return 0u;
+    uint32_t lo, hi;
+    bisect_state(c, budget, kBisectSteps, lo, hi);
+    return hi;
+}
+
+// widths, per-block class counts for the reorder, global class counts
+__global__ __launch_bounds__(256) void k_alloc_final(AllocArgs a) {
+    Ctrl *c = a.ctrl;
+    const uint32_t rb = final_rho_bits(c, a.budget);
+    if (blockIdx.x == 0 && threadIdx.x == 0) c->rho_bits = rb;
+    const float rho = __uint_as_float(rb);
+    const float t4 = 544.0f * rho, t8 = 16384.0f * rho;
+    uint32_t cnt[3] = {0u, 0u, 0u};
+    const int64_t j0 = (int64_t)blockIdx.x * kReorderSGPerBlock + threadIdx.x * 4;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int64_t j = j0 + i;
+        if (j < a.J) {
+            const float F = a.sumsq[j];
+            const int k = F >= t8 ? 2 : (F >= t4 ? 1 : 0);
+            a.widths[j] = (uint8_t)(2 << k);
+            cnt[k]++;
+        }
+    }
+    // pack three counts (each <= 1024) into 16-bit fields and reduce
+    unsigned long long v = (unsigned long long)cnt[0] | ((unsigned long long)cnt[1] << 16) |
+                           ((unsigned long long)cnt[2] << 32);
+    const unsigned long long tot = block_sum_u64(v);
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int k = 0; k < 3; k++) {
+            const uint32_t ck = (uint32_t)((tot >> (16 * k)) & 0xFFFFu);
+            a.blkcnt[k * a.nblk + blockIdx.x] = (int32_t)ck;
+            if (ck) atomicAdd(&c->class_counts[k], (unsigned long long)ck);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// reorder: exclusive scan of per-block class counts, stable scatter
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(1024) void k_reorder_scan(ReorderArgs a) {
+    __shared__ int64_t sh[1024];
+    const int64_t nb = a.nblk;
+    const int64_t per = (nb + 1023) / 1024;
+    const int64_t b0 = threadIdx.x * per, b1 = min(nb, b0 + per);
+    int64_t base = 0;
+    for (int k = 0; k < 3; k++) {
+        int64_t mine = 0;
+        for (int64_t b = b0; b < b1; b++) mine += a.blkcnt[k * nb + b];
+        sh[threadIdx.x] = mine;
+        __syncthreads();
+        // Hillis-Steele inclusive scan over 1024 threads
+        for (int d = 1; d < 1024; d <<= 1) {
+            const int64_t add = threadIdx.x >= d ? sh[threadIdx.x - d] : 0;
+            __syncthreads();
+            sh[threadIdx.x] += add;
+            __syncthreads();
+        }
+        int64_t run = base + sh[threadIdx.x] - mine;
+        for (int64_t b = b0; b < b1; b++) {
+            const int32_t cb = a.blkcnt[k * nb + b];
+            a.blkcnt[k * nb + b] = (int32_t)run;
+            run += cb;
+        }
+        base += (int64_t)a.ctrl->class_counts[k];
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(256) void k_reorder_scatter(ReorderArgs a) {
+    __shared__ unsigned long long wtot[4];
+    const int64_t j0 = (int64_t)blockIdx.x * kReorderSGPerBlock + threadIdx.x * 4;
+    int k_of[4];
+    uint32_t cnt[3] = {0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int64_t j = j0 + i;
+        k_of[i] = -1;
+        if (j < a.J) {
+            const uint8_t q = a.widths[j];
+            k_of[i] = q == 2 ? 0 : (q == 4 ? 1 : 2);
+            cnt[k_of[i]]++;
+        }
+    }
+    const unsigned long long mine = (unsigned long long)cnt[0] | ((unsigned long long)cnt[1] << 16) |
+                                    ((unsigned long long)cnt[2] << 32);
+    // inclusive scan inside the wave
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    unsigned long long inc = mine;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const unsigned long long o = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += o;
+    }
+    if (lane == 63) wtot[wave] = inc;
+    __syncthreads();
+    unsigned long long before = 0;
+    for (int w = 0; w < wave; w++) before += wtot[w];
+    unsigned long long excl = before + inc - mine;
+    int32_t pos[3];
+#pragma unroll
+    for (int k = 0; k < 3; k++)
+        pos[k] = a.blkcnt[k * a.nblk + blockIdx.x] + (int32_t)((excl >> (16 * k)) & 0xFFFFu);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        if (k_of[i] < 0) continue;
+        const int64_t j = j0 + i;
+        const int32_t p = pos[k_of[i]]++;
+        a.perm[p] = (int32_t)j;
+        a.inv[j] = p;
+        a.mu_stream[p] = a.sum[j] / a.denom;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// utility
+// ---------------------------------------------------------------------------
+
+__global__ void k_zero_u32(uint32_t *p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+static int grid_for(int64_t items, int64_t per_block, int64_t cap) {
+    int64_t b = (items + per_block - 1) / per_block;
+    if (b < 1) b = 1;
+    if (b > cap) b = cap;
+    return (int)b;
+}
+
+constexpr int64_t kStreamGrid = 2048;  // 256 CUs x 8 resident blocks
+
+hipError_t launch_zero(uint32_t *p, int64_t n, hipStream_t s) {
+    hipLaunchKernelGGL(k_zero_u32, dim3(grid_for(n, 256, 1024)), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_stats(const StatsArgs &a, int f32, hipStream_t s) {
+    const dim3 grid(grid_for(a.J, 8, kStreamGrid));
+    if (f32) hipLaunchKernelGGL(k_stats<1>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_stats<0>, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_alloc_step(const AllocArgs &a, int step, hipStream_t s) {
+    hipLaunchKernelGGL(k_alloc_step, dim3(grid_for(a.J, 256, kStreamGrid)), dim3(256), 0, s, a, step);
+    return hipGetLastError();
+}
+
+hipError_t launch_alloc_final(const AllocArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(k_alloc_final, dim3((unsigned)a.nblk), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_reorder(const ReorderArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(k_reorder_scan, dim3(1), dim3(1024), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_reorder_scatter, dim3((unsigned)a.nblk), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_codec(const CodecArgs &a, int mode, int local, int64_t max_sg, hipStream_t s) {
+    const dim3 grid(grid_for(max_sg, kSGPerBlock, kStreamGrid)), block(256);
+    if (mode == kCompress && local == kLocalBF16) hipLaunchKernelGGL((k_codec<kCompress, kLocalBF16>), grid, block, 0, s, a);
+    else if (mode == kCompress && local == kLocalF32) hipLaunchKernelGGL((k_codec<kCompress, kLocalF32>), grid, block, 0, s, a);
+    else if (mode == kHop && local == kLocalBF16) hipLaunchKernelGGL((k_codec<kHop, kLocalBF16>), grid, block, 0, s, a);
+    else if (mode == kHop && local == kLocalF32) hipLaunchKernelGGL((k_codec<kHop, kLocalF32>), grid, block, 0, s, a);
+    else if (mode == kHop && local == kLocalPacked) hipLaunchKernelGGL((k_codec<kHop, kLocalPacked>), grid, block, 0, s, a);
+    else if (mode == kFinalize) hipLaunchKernelGGL((k_codec<kFinalize, kLocalNone>), grid, block, 0, s, a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace dq

@@ -1,0 +1,259 @@
+"""Python binding of the C ABI in ``include/dq.h``.
+
+Argument marshalling only: every stage runs in the HIP kernels of
+``libdq.so``.  PyTorch supplies device memory (tensors) and the stream
+(``torch.cuda.current_stream()``).  If the shared library is missing the
+import of this module's functions raises; there is no CPU fallback.
+"""
+import ctypes as C
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdq.so")
+
+DQ_OK, DQ_EINVAL, DQ_EBUDGET, DQ_ESTATE, DQ_EWORKSPACE, DQ_ENULL, DQ_EHIP, DQ_ENONFINITE = \
+    0, -1, -2, -3, -4, -5, -6, -7
+RING, BUTTERFLY = 0, 1
+BF16, F32, PACKED = 0, 1, 2
+CORRELATED, INDEPENDENT = 0, 1
+OPT_SEED, OPT_ROUND, OPT_ROUNDING, OPT_TIMING = 0, 1, 2, 3
+KERNEL_KINDS = ("stats", "allocate", "reorder", "compress", "hop_grad", "hop_packed",
+                "finalize", "mxfp8")
+
+
+class dq_info(C.Structure):
+    _fields_ = [("rho_bits", C.c_uint32), ("rho", C.c_float), ("t12", C.c_float),
+                ("t24", C.c_float), ("t48", C.c_float), ("class_counts", C.c_int64 * 3),
+                ("budget_bits", C.c_int64), ("used_bits", C.c_int64),
+                ("achieved_bits", C.c_double), ("nonfinite", C.c_int32)]
+
+
+class dq_layout(C.Structure):
+    _fields_ = [(n, C.c_size_t) for n in ("sum", "sumsq", "widths", "perm", "inv", "mu_stream",
+                                          "ctrl", "total")]
+
+
+class dq_timing(C.Structure):
+    _fields_ = [("ms", C.c_double * 8), ("launches", C.c_int64 * 8), ("coords", C.c_int64 * 8)]
+
+
+class DQError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+_lib = None
+
+# exported symbols and their signatures (every declaration of include/dq.h)
+_SIGS = {
+    "dq_plan_create": (C.c_int, [C.c_int64, C.c_int32, C.c_int32, C.c_float, C.POINTER(C.c_void_p)]),
+    "dq_plan_destroy": (None, [C.c_void_p]),
+    "dq_plan_set_u64": (C.c_int, [C.c_void_p, C.c_int32, C.c_uint64]),
+    "dq_workspace_bytes": (C.c_size_t, [C.c_void_p]),
+    "dq_plan_bind": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t]),
+    "dq_workspace_layout": (C.c_int, [C.c_void_p, C.POINTER(dq_layout)]),
+    "dq_region_bytes_max": (C.c_size_t, [C.c_void_p, C.c_int64]),
+    "dq_stats": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p]),
+    "dq_allocate": (C.c_int, [C.c_void_p, C.c_void_p]),
+    "dq_reorder": (C.c_int, [C.c_void_p, C.c_void_p]),
+    "dq_compress": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p,
+                              C.c_void_p]),
+    "dq_hop": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_int32,
+                         C.c_void_p, C.c_void_p, C.c_void_p]),
+    "dq_finalize": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "dq_final_part": (C.c_int64, [C.c_void_p, C.c_int32]),
+    "dq_arena_bytes": (C.c_size_t, [C.c_void_p]),
+    "dq_allreduce": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
+                               C.c_void_p, C.c_void_p]),
+    "dq_mxfp8_arena_bytes": (C.c_size_t, [C.c_void_p]),
+    "dq_mxfp8_allreduce": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
+                                     C.c_void_p, C.c_void_p]),
+    "dq_get_info": (C.c_int, [C.c_void_p, C.POINTER(dq_info), C.c_void_p]),
+    "dq_timing_read": (C.c_int, [C.c_void_p, C.POINTER(dq_timing)]),
+    "dq_status_string": (C.c_char_p, [C.c_int32]),
+    "dq_version": (C.c_int32, []),
+}
+
+
+def lib():
+    """Load ``libdq.so`` (built by ``__graft_entry__.build()``); raise if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                               "(run __graft_entry__.build())")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(s):
+    return lib().dq_status_string(int(s)).decode()
+
+
+def _check(rc, what):
+    if rc != DQ_OK:
+        raise DQError(rc, what)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr())
+
+
+def _kind(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.uint8:
+        return PACKED
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+class Plan:
+    """One gradient-synchronisation round over ``n_workers`` virtual workers.
+
+    Mirrors ``include/dq.h``: create -> options -> bind workspace -> stats (rank
+    order) -> allocate -> reorder -> compress / hop -> finalize.
+    """
+
+    def __init__(self, n_coords, n_workers, topology=RING, avg_bits=5.0, seed=1, rnd=0,
+                 rounding=CORRELATED, device="cuda", timing=False):
+        self.d = int(n_coords)
+        self.n = int(n_workers)
+        self.J = self.d // 256
+        self.topology = int(topology)
+        self.log2n = max(0, (self.n - 1).bit_length())
+        h = C.c_void_p()
+        _check(lib().dq_plan_create(self.d, self.n, self.topology, float(avg_bits), C.byref(h)),
+               "dq_plan_create")
+        self.h = h
+        self.set(OPT_SEED, seed)
+        self.set(OPT_ROUND, rnd)
+        self.set(OPT_ROUNDING, rounding)
+        self.set(OPT_TIMING, 1 if timing else 0)
+        nbytes = lib().dq_workspace_bytes(self.h)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _check(lib().dq_plan_bind(self.h, _ptr(self.workspace), nbytes), "dq_plan_bind")
+        lay = dq_layout()
+        _check(lib().dq_workspace_layout(self.h, C.byref(lay)), "dq_workspace_layout")
+        self.layout = {n: getattr(lay, n) for n, _ in dq_layout._fields_}
+
+    def __del__(self):
+        h = getattr(self, "h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.dq_plan_destroy(h)
+            self.h = None
+
+    def set(self, option, value):
+        _check(lib().dq_plan_set_u64(self.h, int(option), int(value)), "dq_plan_set_u64")
+
+    # ---- stages --------------------------------------------------------
+    def stats(self, worker, grad, stream=None):
+        _check(lib().dq_stats(self.h, int(worker), _ptr(grad), _kind(grad), _stream(stream)),
+               "dq_stats")
+
+    def allocate(self, stream=None):
+        _check(lib().dq_allocate(self.h, _stream(stream)), "dq_allocate")
+
+    def reorder(self, stream=None):
+        _check(lib().dq_reorder(self.h, _stream(stream)), "dq_reorder")
+
+    def compress(self, worker, step, grad, region_out, stream=None):
+        _check(lib().dq_compress(self.h, int(worker), int(step), _ptr(grad), _kind(grad),
+                                 _ptr(region_out), _stream(stream)), "dq_compress")
+
+    def hop(self, worker, step, region_in, local, out0, out1=None, stream=None):
+        _check(lib().dq_hop(self.h, int(worker), int(step), _ptr(region_in), _ptr(local),
+                            _kind(local), _ptr(out0), None if out1 is None else _ptr(out1),
+                            _stream(stream)), "dq_hop")
+
+    def finalize(self, part, region, out, stream=None):
+        _check(lib().dq_finalize(self.h, int(part), _ptr(region), _ptr(out), _stream(stream)),
+               "dq_finalize")
+
+    def final_part(self, worker):
+        return int(lib().dq_final_part(self.h, int(worker)))
+
+    # ---- whole round -----------------------------------------------------
+    def region_bytes_max(self, m):
+        return int(lib().dq_region_bytes_max(self.h, int(m)))
+
+    def new_region(self, m, device="cuda"):
+        return torch.zeros(self.region_bytes_max(m), dtype=torch.uint8, device=device)
+
+    def arena_bytes(self):
+        return int(lib().dq_arena_bytes(self.h))
+
+    def allreduce(self, grads, out=None, arena=None, stream=None):
+        assert len(grads) == self.n
+        kind = _kind(grads[0])
+        dev = grads[0].device
+        if arena is None:
+            arena = torch.empty(self.arena_bytes(), dtype=torch.uint8, device=dev)
+        if out is None:
+            out = torch.empty(self.d, dtype=torch.float32, device=dev)
+        ptrs = (C.c_void_p * self.n)(*[g.data_ptr() for g in grads])
+        _check(lib().dq_allreduce(self.h, ptrs, kind, _ptr(arena), arena.numel(), _ptr(out),
+                                  _stream(stream)), "dq_allreduce")
+        return out
+
+    def mxfp8_allreduce(self, grads, out=None, arena=None, stream=None):
+        kind = _kind(grads[0])
+        dev = grads[0].device
+        if arena is None:
+            arena = torch.empty(max(1, int(lib().dq_mxfp8_arena_bytes(self.h))), dtype=torch.uint8,
+                                device=dev)
+        if out is None:
+            out = torch.empty(self.d, dtype=torch.float32, device=dev)
+        ptrs = (C.c_void_p * self.n)(*[g.data_ptr() for g in grads])
+        _check(lib().dq_mxfp8_allreduce(self.h, ptrs, kind, _ptr(arena), arena.numel(), _ptr(out),
+                                        _stream(stream)), "dq_mxfp8_allreduce")
+        return out
+
+    # ---- inspection ------------------------------------------------------
+    def info(self, stream=None):
+        i = dq_info()
+        rc = lib().dq_get_info(self.h, C.byref(i), _stream(stream))
+        if rc not in (DQ_OK, DQ_ENONFINITE):
+            _check(rc, "dq_get_info")
+        return {"rho_bits": i.rho_bits, "rho": i.rho, "t12": i.t12, "t24": i.t24, "t48": i.t48,
+                "class_counts": list(i.class_counts), "budget_bits": i.budget_bits,
+                "used_bits": i.used_bits, "achieved_bits": i.achieved_bits,
+                "nonfinite": bool(i.nonfinite), "status": rc}
+
+    def timing(self):
+        t = dq_timing()
+        _check(lib().dq_timing_read(self.h, C.byref(t)), "dq_timing_read")
+        return {k: {"ms": t.ms[i], "launches": t.launches[i], "coords": t.coords[i]}
+                for i, k in enumerate(KERNEL_KINDS)}
+
+    def _view(self, name, dtype, count):
+        off = self.layout[name]
+        nbytes = count * torch.empty(0, dtype=dtype).element_size()
+        return self.workspace[off:off + nbytes].view(dtype)
+
+    def stats_arrays(self):
+        return self._view("sum", torch.float32, self.J), self._view("sumsq", torch.float32, self.J)
+
+    def widths(self):
+        return self._view("widths", torch.uint8, self.J)
+
+    def perm(self):
+        return self._view("perm", torch.int32, self.J), self._view("inv", torch.int32, self.J)
+
+    def mu_stream(self):
+        return self._view("mu_stream", torch.float32, self.J)

@@ -72,8 +72,10 @@ def _log_uniform(lo, hi, n, g, device):
 
 
 def _laplace(n, g, device):
-    u = torch.rand(n, generator=g, device=device, dtype=torch.float32) - 0.5
-    return -torch.sign(u) * torch.log1p(-2.0 * u.abs())
+    # a random sign times Exp(1) = -log(1 - U), U in [0, 1) so always finite
+    e = -torch.log1p(-torch.rand(n, generator=g, device=device, dtype=torch.float32))
+    sign = torch.where(torch.rand(n, generator=g, device=device) < 0.5, -1.0, 1.0)
+    return sign * e
 
 
 def _blocks(d, nblocks):

@@ -1,0 +1,233 @@
+/*
+ * dq.h -- C ABI of the DynamiQ hot path on MI355X (gfx950).
+ *
+ * One gradient-synchronisation round of DynamiQ, run over n virtual workers
+ * whose buffers all sit in one GPU's HBM; the hops of the ring or butterfly
+ * all-reduce are simulated by handing region buffers from one worker to the
+ * next.  The stages and where the pages define them:
+ *
+ *   dq_stats     per super-group sum and squared l2 norm, folded over workers
+ *                (DynamiQ scribe notes, "Key idea and contribution": statistics
+ *                collection phase; pith.science review, Fig. 2 caption)
+ *   dq_allocate  widths {2,4,8} from one scalar under the bit budget, with the
+ *                locked threshold ratios T12 = 5/32 T24, T24 = 17/512 T48
+ *                (pith.science review, "What carries the argument", Fig. 3)
+ *   dq_reorder   width-contiguous streams (scribe notes, same section)
+ *   dq_compress  first quantisation of (g - mean) with hierarchical UINT8 group
+ *                scales, non-uniform levels and correlated stochastic rounding
+ *                (scribe notes, same section; review, referee summary)
+ *   dq_hop       fused decompress-accumulate-recompress of one hop (scribe
+ *                notes, "Key idea and contribution": the fused kernel)
+ *   dq_finalize  decode, add back the mean, restore the original order
+ *                (scribe notes, main all-reduce phase)
+ *
+ * Numerics and layouts not fixed by the pages follow the readings recorded in
+ * the repository's design document; the CPU oracle implements the same ones.
+ *
+ * Conventions
+ *   - Every call returns a dq_status; errors are negative.  Nothing aborts or
+ *     throws across the ABI.  Argument checks are synchronous; a device fault
+ *     surfaces at the caller's next synchronisation of the stream.
+ *   - The caller owns every device buffer: gradients, regions, outputs and the
+ *     plan workspace.  The plan owns only host state and borrows the bound
+ *     workspace.  No stage allocates device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     device work of a call is enqueued on it; no call synchronises except
+ *     dq_get_info and dq_timing_read.
+ *   - A plan is not thread-safe.
+ *   - Device pointers to gradients must be 16-byte aligned; region buffers and
+ *     the workspace 256-byte aligned.
+ */
+#ifndef DQ_H
+#define DQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dq_status {
+    DQ_OK = 0,
+    DQ_EINVAL = -1,       /* argument out of range (sizes, worker, step, kind) */
+    DQ_EBUDGET = -2,      /* avg_bits < 2 or NaN */
+    DQ_ESTATE = -3,       /* call out of stage order */
+    DQ_EWORKSPACE = -4,   /* no workspace bound, or too small / misaligned */
+    DQ_ENULL = -5,        /* a required pointer is NULL */
+    DQ_EHIP = -6,         /* the HIP runtime reported an error */
+    DQ_ENONFINITE = -7    /* a gradient had a non-finite value or square */
+} dq_status;
+
+typedef enum dq_topology { DQ_RING = 0, DQ_BUTTERFLY = 1 } dq_topology;
+
+/* element kinds: gradients are DQ_BF16 or DQ_F32; the local operand of a
+ * butterfly hop at level >= 2 is DQ_PACKED (the worker's own region) */
+typedef enum dq_kind { DQ_BF16 = 0, DQ_F32 = 1, DQ_PACKED = 2 } dq_kind;
+
+typedef enum dq_rounding {
+    DQ_ROUND_CORRELATED = 0,   /* one shared dither per coordinate, staggered by worker rank */
+    DQ_ROUND_INDEPENDENT = 1   /* an independent dither per quantisation event */
+} dq_rounding;
+
+typedef enum dq_option {
+    DQ_OPT_SEED = 0,       /* 64-bit Philox key (default 1) */
+    DQ_OPT_ROUND = 1,      /* round index, 32-bit, part of every Philox counter (default 0) */
+    DQ_OPT_ROUNDING = 2,   /* dq_rounding (default DQ_ROUND_CORRELATED) */
+    DQ_OPT_TIMING = 3      /* 1: time every launch with HIP events on its stream */
+} dq_option;
+
+typedef struct dq_plan dq_plan;
+
+/* Result of one allocation, read back by dq_get_info. */
+typedef struct dq_info {
+    uint32_t rho_bits;         /* fp32 bit pattern of the scalar rho */
+    float rho;
+    float t12, t24, t48;       /* fl(85 rho), fl(544 rho), fl(16384 rho) */
+    int64_t class_counts[3];   /* super-groups at 2, 4, 8 bits */
+    int64_t budget_bits;       /* floor(avg_bits * J) */
+    int64_t used_bits;         /* sum of widths over super-groups */
+    double achieved_bits;      /* used_bits / J (payload bits per coordinate) */
+    int32_t nonfinite;         /* 1 if a gradient value or square was not finite */
+} dq_info;
+
+/* Byte offsets of the plan state inside the bound workspace (for inspection). */
+typedef struct dq_layout {
+    size_t sum;        /* float[J]  per-SG sum, folded over workers (original order) */
+    size_t sumsq;      /* float[J]  F_j, per-SG squared norm summed over workers */
+    size_t widths;     /* uint8[J]  q_j */
+    size_t perm;       /* int32[J]  stream position -> SG */
+    size_t inv;        /* int32[J]  SG -> stream position */
+    size_t mu_stream;  /* float[J]  global mean mu in stream order */
+    size_t ctrl;       /* control block (counts, rho, flags) */
+    size_t total;
+} dq_layout;
+
+/* Accumulated kernel time per launch kind while DQ_OPT_TIMING is on. */
+typedef enum dq_kernel_kind {
+    DQ_K_STATS = 0, DQ_K_ALLOCATE = 1, DQ_K_REORDER = 2, DQ_K_COMPRESS = 3,
+    DQ_K_HOP_GRAD = 4, DQ_K_HOP_PACKED = 5, DQ_K_FINALIZE = 6, DQ_K_MXFP8 = 7,
+    DQ_K_COUNT = 8
+} dq_kernel_kind;
+
+typedef struct dq_timing {
+    double ms[DQ_K_COUNT];       /* summed launch durations (HIP events) */
+    int64_t launches[DQ_K_COUNT];
+    int64_t coords[DQ_K_COUNT];  /* coordinates processed (hop/compress/finalize/stats) */
+} dq_timing;
+
+/* ---- plan ---------------------------------------------------------------- */
+
+/* Host-only; allocates no device memory.  n_coords > 0 and a multiple of 256;
+ * n_workers >= 1 (a power of two for DQ_BUTTERFLY).  avg_bits is the payload
+ * budget in bits per coordinate (>= 2; > 8 means every width is 8).
+ * Errors: DQ_ENULL, DQ_EINVAL, DQ_EBUDGET. */
+dq_status dq_plan_create(int64_t n_coords, int32_t n_workers, int32_t topology,
+                         float avg_bits, dq_plan **out);
+void dq_plan_destroy(dq_plan *plan);
+
+/* Set a dq_option.  Errors: DQ_ENULL, DQ_EINVAL (unknown option or value). */
+dq_status dq_plan_set_u64(dq_plan *plan, int32_t option, uint64_t value);
+
+/* Device bytes the caller must provide for the plan state. */
+size_t dq_workspace_bytes(const dq_plan *plan);
+
+/* Bind caller-owned device memory (>= dq_workspace_bytes, 256-byte aligned).
+ * Errors: DQ_ENULL, DQ_EWORKSPACE. */
+dq_status dq_plan_bind(dq_plan *plan, void *d_workspace, size_t bytes);
+
+dq_status dq_workspace_layout(const dq_plan *plan, dq_layout *out);
+
+/* Worst-case bytes of the region of any part of m (m = n for the ring,
+ * m = 2^s for butterfly level s, m = 1 for n = 1).  0 if m is not valid. */
+size_t dq_region_bytes_max(const dq_plan *plan, int64_t m);
+
+/* ---- stages (enqueue on `stream`) ----------------------------------------- */
+
+/* Statistics of worker `worker`'s gradient (n_coords values of `kind`,
+ * DQ_BF16 or DQ_F32).  Workers are called in rank order 0..n-1; calling worker
+ * 0 starts a new round.  Errors: DQ_ENULL, DQ_EINVAL, DQ_ESTATE (out of rank
+ * order), DQ_EWORKSPACE, DQ_EHIP. */
+dq_status dq_stats(dq_plan *plan, int32_t worker, const void *d_grad, int32_t kind,
+                   void *stream);
+
+/* Minimal rho meeting the budget, widths and class counts (device-resident).
+ * Requires all n dq_stats calls.  Errors: DQ_ESTATE, DQ_EHIP. */
+dq_status dq_allocate(dq_plan *plan, void *stream);
+
+/* Stable partition by width: perm, inv, mean in stream order.
+ * Requires dq_allocate.  Errors: DQ_ESTATE, DQ_EHIP. */
+dq_status dq_reorder(dq_plan *plan, void *stream);
+
+/* First quantisation of worker `worker`'s gradient on the part implied by the
+ * schedule: ring step 0 (part w of n); butterfly level 1 (the sibling half,
+ * part (w >> (L-1)) ^ 1 of 2); n == 1: step 0, the whole vector.  Writes the
+ * region of that part into d_region_out (>= dq_region_bytes_max of its m).
+ * Errors: DQ_ENULL, DQ_EINVAL, DQ_ESTATE, DQ_EHIP. */
+dq_status dq_compress(dq_plan *plan, int32_t worker, int32_t step, const void *d_grad,
+                      int32_t kind, void *d_region_out, void *stream);
+
+/* Fused hop: decode d_region_in, add the local operand, re-encode.
+ *   ring step t in 1..n-1: part (w - t) mod n; local = worker w's gradient
+ *     (kind DQ_BF16/DQ_F32); output one region (d_region_out1 unused).
+ *   butterfly level s in 1..L: part w >> (L-s) of 2^s; local = the gradient at
+ *     s = 1, the worker's own packed region of the same part (DQ_PACKED) at
+ *     s >= 2; for s < L the output is the two child regions (parts 2c and
+ *     2c+1 of 2^(s+1)) in d_region_out0 and d_region_out1, for s = L one region.
+ * d_region_in is the region of the same part produced by the previous hop (or
+ * compress) of the sending worker.  Errors: DQ_ENULL, DQ_EINVAL, DQ_ESTATE,
+ * DQ_EHIP. */
+dq_status dq_hop(dq_plan *plan, int32_t worker, int32_t step, const void *d_region_in,
+                 const void *d_local, int32_t local_kind, void *d_region_out0,
+                 void *d_region_out1, void *stream);
+
+/* Decode the final region of part `part` (of m = n), add fl(n * mu), and write
+ * its super-groups at their original positions of d_out (float[n_coords]).
+ * The result is the sum over workers.  Errors: DQ_ENULL, DQ_EINVAL, DQ_ESTATE,
+ * DQ_EHIP. */
+dq_status dq_finalize(dq_plan *plan, int64_t part, const void *d_region, float *d_out,
+                      void *stream);
+
+/* Part that worker `worker` holds after the reduce phase ((w+1) mod n for the
+ * ring, w for the butterfly, 0 for n == 1); -1 on bad arguments. */
+int64_t dq_final_part(const dq_plan *plan, int32_t worker);
+
+/* ---- whole round ---------------------------------------------------------- */
+
+/* Device bytes of the region arena dq_allreduce uses. */
+size_t dq_arena_bytes(const dq_plan *plan);
+
+/* One full simulated round: dq_stats for every worker, dq_allocate,
+ * dq_reorder, the schedule's compress and hop calls with region hand-offs,
+ * and dq_finalize of every part into d_out (float[n_coords]).
+ * h_grads is a HOST array of n device pointers of the same kind.
+ * Errors: as the stages, DQ_EWORKSPACE if the arena is too small. */
+dq_status dq_allreduce(dq_plan *plan, const void *const *h_grads, int32_t kind,
+                       void *d_arena, size_t arena_bytes, float *d_out, void *stream);
+
+/* The same schedule with the MXFP8 reference codec (OCP MX v1.0: 32-element
+ * blocks, E8M0 scale, E4M3 elements) on parts of the ORIGINAL order
+ * (part c of m = super-groups [floor(cJ/m), floor((c+1)J/m))), re-encoded
+ * at every hop, fp32 output.  For the quality report only.  Needs a bound
+ * workspace and d_arena >= dq_mxfp8_arena_bytes. */
+size_t dq_mxfp8_arena_bytes(const dq_plan *plan);
+dq_status dq_mxfp8_allreduce(dq_plan *plan, const void *const *h_grads, int32_t kind,
+                             void *d_arena, size_t arena_bytes, float *d_out, void *stream);
+
+/* ---- inspection ----------------------------------------------------------- */
+
+/* Copy the allocation result to the host.  SYNCHRONISES `stream`.
+ * Returns DQ_ENONFINITE (after filling *out) if a gradient was not finite. */
+dq_status dq_get_info(dq_plan *plan, dq_info *out, void *stream);
+
+/* Read (and reset) the accumulated launch timings.  SYNCHRONISES the streams
+ * the timed launches ran on.  Errors: DQ_ENULL, DQ_EHIP. */
+dq_status dq_timing_read(dq_plan *plan, dq_timing *out);
+
+const char *dq_status_string(int32_t status);
+int32_t dq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DQ_H */

@@ -168,8 +168,12 @@ class Oracle:
         self.log2n = max(0, (self.n - 1).bit_length())
 
     def __del__(self):
-        if getattr(self, "h", None):
-            lib().or_destroy(self.h)
+        h = getattr(self, "h", None)
+        if h and _lib is not None:
+            try:
+                _lib.or_destroy(h)
+            except Exception:
+                pass
             self.h = None
 
     # stages

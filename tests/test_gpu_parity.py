@@ -1,0 +1,323 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs, stage by stage, bit for bit.
+
+Compared in order: per-SG sums and squared norms, rho, widths, perm / inv,
+mean in stream order, every region every hop writes (codes, scale units,
+group codes), and the final fp32 sum.  The first mismatch names its stage.
+"""
+import numpy as np
+import pytest
+import torch
+
+from compressed_hop_gradient_amd import dq, synth
+from oracle import pyoracle as po
+from tests import regions as R
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _np(t):
+    return synth.as_numpy(t)
+
+
+def _bits(a):
+    a = np.ascontiguousarray(a)
+    return a.view(np.uint32) if a.dtype == np.float32 else a
+
+
+def _grads_np(grads):
+    return [_np(g) for g in grads]
+
+
+def _schedule(n, topo):
+    """Yield the steps of one round: ('compress', w, step) / ('hop', w, step)."""
+    if n == 1:
+        yield ("compress", 0, 0)
+        return
+    if topo == dq.RING:
+        for w in range(n):
+            yield ("compress", w, 0)
+        for t in range(1, n):
+            for w in range(n):
+                yield ("hop", w, t)
+        return
+    L = n.bit_length() - 1
+    for w in range(n):
+        yield ("compress", w, 1)
+    for s in range(1, L + 1):
+        for w in range(n):
+            yield ("hop", w, s)
+
+
+def _out_parts(n, topo, kind, w, step):
+    """(m, part) of each output region of a step."""
+    if n == 1:
+        return [(1, 0)]
+    if topo == dq.RING:
+        return [(n, w if kind == "compress" else (w - step) % n)]
+    L = n.bit_length() - 1
+    if kind == "compress":
+        return [(2, (w >> (L - 1)) ^ 1)]
+    c = w >> (L - step)
+    if step < L:
+        return [(2 ** (step + 1), 2 * c), (2 ** (step + 1), 2 * c + 1)]
+    return [(n, c)]
+
+
+class Round:
+    """Drives the same schedule on the GPU and on the oracle, keeping every
+    region both produce (fresh zeroed buffers per step)."""
+
+    def __init__(self, grads, topo, budget=5.0, seed=1, rnd=0, rounding=dq.CORRELATED):
+        self.grads = grads
+        self.gnp = _grads_np(grads)
+        self.n = len(grads)
+        self.d = grads[0].numel()
+        self.topo = topo
+        self.plan = dq.Plan(self.d, self.n, topo, budget, seed=seed, rnd=rnd, rounding=rounding)
+        self.orc = po.Oracle(self.d, self.n, topo, budget, seed=seed, rnd=rnd, rounding=rounding)
+
+    def stages(self):
+        for w in range(self.n):
+            self.plan.stats(w, self.grads[w])
+            self.orc.stats(w, self.gnp[w])
+        self.plan.allocate()
+        self.orc.allocate()
+        self.plan.reorder()
+        self.orc.reorder()
+        torch.cuda.synchronize()
+
+    def check_stages(self):
+        s_g, F_g = [x.cpu().numpy() for x in self.plan.stats_arrays()]
+        s_o, F_o, mu_o = self.orc.stats_arrays()
+        assert np.array_equal(_bits(s_g), _bits(s_o)), "stats: sum"
+        assert np.array_equal(_bits(F_g), _bits(F_o)), "stats: squared norm"
+        info = self.plan.info()
+        assert not info["nonfinite"], "inputs must be finite"
+        assert info["rho_bits"] == self.orc.rho_bits(), "allocate: rho"
+        assert np.array_equal(self.plan.widths().cpu().numpy(), self.orc.widths()), "allocate: widths"
+        C = self.orc.class_counts()
+        assert list(info["class_counts"]) == C.tolist(), "allocate: class counts"
+        assert info["used_bits"] <= info["budget_bits"]
+        perm_g, inv_g = [x.cpu().numpy() for x in self.plan.perm()]
+        perm_o, inv_o = self.orc.perm()
+        assert np.array_equal(perm_g, perm_o), "reorder: perm"
+        assert np.array_equal(inv_g, inv_o), "reorder: inv"
+        mus = self.plan.mu_stream().cpu().numpy()
+        assert np.array_equal(_bits(mus), _bits(mu_o[perm_o])), "reorder: mean in stream order"
+        self.C = C
+        return info
+
+    def run_hops(self, check_every=True):
+        n, topo = self.n, self.topo
+        g_reg, o_reg = {}, {}
+        L = max(0, n.bit_length() - 1)
+        for kind, w, step in _schedule(n, topo):
+            parts = _out_parts(n, topo, kind, w, step)
+            gout = [self.plan.new_region(m) for m, _ in parts]
+            oout = [np.zeros(self.orc.worst_region_bytes(), np.uint8) for _ in parts]
+            if kind == "compress":
+                self.plan.compress(w, step, self.grads[w], gout[0])
+                self.orc.compress(w, step, self.gnp[w], oout[0])
+            else:
+                if topo == dq.RING:
+                    key_in = ((w - 1) % n, step - 1)
+                    g_in, o_in = g_reg[key_in][0], o_reg[key_in][0]
+                    g_loc, o_loc = self.grads[w], self.gnp[w]
+                else:
+                    partner = w ^ (n >> step)
+                    keep = (w >> (L - step)) & 1
+                    if step == 1:
+                        g_in, o_in = g_reg[(partner, "c")][0], o_reg[(partner, "c")][0]
+                        g_loc, o_loc = self.grads[w], self.gnp[w]
+                    else:
+                        g_in, o_in = g_reg[(partner, step - 1)][keep], o_reg[(partner, step - 1)][keep]
+                        g_loc, o_loc = g_reg[(w, step - 1)][keep], o_reg[(w, step - 1)][keep]
+                self.plan.hop(w, step, g_in, g_loc, gout[0], gout[1] if len(gout) > 1 else None)
+                self.orc.hop(w, step, o_in, o_loc, oout[0], oout[1] if len(oout) > 1 else None)
+            key = (w, "c") if (kind == "compress" and topo == dq.BUTTERFLY and n > 1) else (w, step)
+            g_reg[key] = gout
+            o_reg[key] = oout
+            if check_every:
+                torch.cuda.synchronize()
+                for (m, c), gb, ob in zip(parts, gout, oout):
+                    size = R.region_bytes(self.C, m, c)
+                    gbytes = gb[:size].cpu().numpy()
+                    if not np.array_equal(gbytes, ob[:size]):
+                        bad = np.nonzero(gbytes != ob[:size])[0]
+                        raise AssertionError(f"{kind} worker {w} step {step} part {c}/{m}: "
+                                             f"{bad.size} of {size} bytes differ, first at {bad[0]}")
+        self.g_reg, self.o_reg = g_reg, o_reg
+
+    def finalize(self):
+        n = self.n
+        out_g = torch.full((self.d,), float("nan"), dtype=torch.float32, device=DEV)
+        out_o = np.full(self.d, np.nan, np.float32)
+        L = max(0, n.bit_length() - 1)
+        for w in range(n):
+            part = self.plan.final_part(w)
+            assert part == self.orc.final_part(w)
+            if n == 1:
+                key = (0, 0)
+            elif self.topo == dq.RING:
+                key = (w, n - 1)
+            else:
+                key = (w, L)
+            self.plan.finalize(part, self.g_reg[key][0], out_g)
+            self.orc.finalize(part, self.o_reg[key][0], out_o)
+        torch.cuda.synchronize()
+        out_g = out_g.cpu().numpy()
+        assert np.array_equal(_bits(out_g), _bits(out_o)), "finalize: output"
+        return out_g
+
+
+def full_round(grads, topo, **kw):
+    r = Round(grads, topo, **kw)
+    r.stages()
+    info = r.check_stages()
+    r.run_hops()
+    out = r.finalize()
+    return r, info, out
+
+
+def _scaled(name, J, workers=None, seed=0):
+    return synth.generate(name, d=256 * J, device=DEV, seed=seed, workers=workers)
+
+
+# ---------------------------------------------------------------------------
+
+def test_tiny_workload_bit_exact():
+    """The tiny workload exactly as specified: 65,536 fp32 coordinates, 4
+    workers, ring, 5 bits, data seed 0, rounding seed 1."""
+    _need_gpu()
+    grads = synth.generate("tiny", device=DEV)
+    r, info, out = full_round(grads, dq.RING, budget=5.0, seed=1)
+    assert info["achieved_bits"] <= 5.0
+    # the native whole-round entry point gives the same bytes
+    p = dq.Plan(65536, 4, dq.RING, 5.0, seed=1)
+    out2 = p.allreduce(grads)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(out2.cpu().numpy()), _bits(out))
+
+
+@pytest.mark.parametrize("name,J,topo", [
+    ("bert", 3001, dq.RING),          # 8 workers, ragged parts
+    ("gemma", 4099, dq.BUTTERFLY),    # 8 workers, 3 levels, two-child outputs
+    ("large", 2053, dq.RING),         # zero super-groups
+])
+def test_scaled_workloads_bit_exact(name, J, topo):
+    _need_gpu()
+    full_round(_scaled(name, J), topo)
+
+
+@pytest.mark.parametrize("budget", [3.0, 4.0, 5.0, 6.0])
+def test_llama_shape_budget_sweep(budget):
+    _need_gpu()
+    grads = _scaled("llama", 1537)
+    r, info, out = full_round(grads, dq.RING, budget=budget)
+    assert info["used_bits"] <= budget * r.plan.J
+
+
+@pytest.mark.parametrize("n,topo", [(1, dq.RING), (1, dq.BUTTERFLY), (2, dq.RING), (2, dq.BUTTERFLY),
+                                    (4, dq.BUTTERFLY), (16, dq.BUTTERFLY), (3, dq.RING), (5, dq.RING)])
+def test_worker_counts(n, topo):
+    _need_gpu()
+    grads = _scaled("bert", 733, workers=range(n))
+    full_round(grads, topo)
+
+
+@pytest.mark.parametrize("topo", [dq.RING, dq.BUTTERFLY])
+def test_independent_rounding_bit_exact(topo):
+    _need_gpu()
+    full_round(_scaled("gemma", 1031), topo, rounding=dq.INDEPENDENT, seed=2 ** 40 + 17, rnd=9)
+
+
+@pytest.mark.parametrize("J,n,topo", [(1, 8, dq.RING), (3, 8, dq.BUTTERFLY), (7, 4, dq.RING),
+                                      (17, 16, dq.RING)])
+def test_tiny_and_empty_parts(J, n, topo):
+    """Fewer super-groups than parts: some parts are empty."""
+    _need_gpu()
+    full_round(_scaled("bert", J, workers=range(n)), topo)
+
+
+@pytest.mark.parametrize("budget", [2.0, 8.0, 100.0, 2.0001, 7.999])
+def test_budget_extremes(budget):
+    _need_gpu()
+    r, info, out = full_round(_scaled("llama", 517, workers=range(4)), dq.RING, budget=budget)
+    if budget >= 8:
+        assert info["class_counts"] == [0, 0, 517] and info["rho_bits"] == 0
+    if budget == 2.0:
+        assert info["class_counts"] == [517, 0, 0]
+
+
+def test_zero_and_constant_super_groups_f32():
+    _need_gpu()
+    n, J = 4, 40
+    g = [torch.randn(256 * J, device=DEV) * 1e-3 for _ in range(n)]
+    for t in g:
+        t[:256] = 0.0
+        t[256 * 5:256 * 6] = 0.375
+        t[256 * 9:256 * 10] = -2.0 ** -130   # subnormal constant
+    r, info, out = full_round(g, dq.RING)
+    assert np.all(out[:256] == 0.0)
+    assert np.all(out[256 * 5:256 * 6] == np.float32(1.5))
+
+
+def test_all_zero_gradients():
+    _need_gpu()
+    g = [torch.zeros(256 * 33, dtype=torch.bfloat16, device=DEV) for _ in range(8)]
+    r, info, out = full_round(g, dq.BUTTERFLY)
+    assert np.all(out == 0.0)
+
+
+def test_nonfinite_flag():
+    _need_gpu()
+    g = [torch.randn(256 * 8, device=DEV) for _ in range(2)]
+    g[1][300] = float("inf")
+    p = dq.Plan(256 * 8, 2, dq.RING, 5.0)
+    p.stats(0, g[0])
+    p.stats(1, g[1])
+    p.allocate()
+    info = p.info()
+    assert info["nonfinite"] and info["status"] == dq.DQ_ENONFINITE
+    # a new round with finite data clears it
+    g[1][300] = 0.0
+    p.stats(0, g[0])
+    p.stats(1, g[1])
+    p.allocate()
+    assert not p.info()["nonfinite"]
+
+
+def test_deterministic_and_native_schedule_matches():
+    _need_gpu()
+    grads = _scaled("gemma", 2050)
+    outs = []
+    for _ in range(2):
+        p = dq.Plan(grads[0].numel(), 8, dq.BUTTERFLY, 5.0, seed=5)
+        outs.append(p.allreduce(grads).cpu().numpy())
+    assert np.array_equal(_bits(outs[0]), _bits(outs[1]))
+    o = po.Oracle(grads[0].numel(), 8, po.BUTTERFLY, 5.0, seed=5)
+    ref = o.allreduce(_grads_np(grads))
+    assert np.array_equal(_bits(outs[0]), _bits(ref))
+
+
+def test_timing_counts_coordinates():
+    _need_gpu()
+    grads = _scaled("bert", 999)
+    p = dq.Plan(grads[0].numel(), 8, dq.RING, 5.0, timing=True)
+    p.allreduce(grads)
+    t = p.timing()
+    J = p.J
+    assert t["hop_grad"]["launches"] == 8 * 7
+    assert t["hop_grad"]["coords"] == 7 * J * 256       # each ring step covers every SG once
+    assert t["compress"]["coords"] == J * 256
+    assert t["finalize"]["coords"] == J * 256
+    assert t["stats"]["coords"] == 8 * J * 256
+    assert all(v["ms"] >= 0 for v in t.values())
