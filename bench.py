@@ -1,0 +1,213 @@
+"""Benchmark of the DynamiQ hot path on one MI355X.
+
+A step is one whole simulated gradient-synchronisation round (stats for every
+worker, allocate, reorder, compress, every hop of the schedule, finalize) over
+the Gemma-1B-shaped workload: 1.0e9 bf16 coordinates per worker, 8 virtual
+workers in HBM, butterfly (recursive halving, 3 levels), 5 bits/coordinate.
+Inputs are generated on the GPU before the timed region.
+
+Printed as one JSON line:
+  value        fused-hop (DAR) coordinates processed per second of step time
+  roofline     the DAR kernel with the bf16 local operand (level 1 of the
+               butterfly): algorithmic bytes per launch / its HIP-event duration
+  cpu_baseline the CPU oracle's whole round on a bounded sample of the same
+               workload, same unit
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
+METRIC = "fused DAR hop coords/s + HBM GB/s (% of peak), 1B-coord bf16 grad at 5 bits"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="gemma")
+    ap.add_argument("--budget", type=float, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-sgs", type=int, default=1 << 20)
+    ap.add_argument("--no-quality", action="store_true")
+    return ap.parse_args()
+
+
+def dar_bytes_per_coord(achieved_bits):
+    """Algorithmic HBM bytes per coordinate of the DAR hop with a bf16 local:
+    read the incoming region ((b + 0.625)/8 B: codes + fp32 scale unit + 16
+    UINT8 group codes per 256), read the local bf16 (2 B), read perm and mean
+    (8 B per 256), write the outgoing region ((b + 0.625)/8 B)."""
+    region = (achieved_bits + 0.625) / 8.0
+    return 2.0 * region + 2.0 + 8.0 / 256.0
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("dq_kernels.hip", "dq_tables.h", "dq_internal.h"):
+        with open(os.path.join(ROOT, "compressed_hop_gradient_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, src_hash):
+    """HBM bytes per launch from rocprofv3 PMC runs, if taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    e = rec.get(kernel)
+    if not e or e.get("kernel_source") != src_hash:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(args, wl_name, budget, device):
+    """The oracle as it stands, on host cores, on a bounded sample (inputs are
+    drawn by the shared generator on the GPU and copied to the host)."""
+    from compressed_hop_gradient_amd import synth
+    from oracle import build as obuild
+    from oracle import pyoracle as po
+
+    if not os.path.exists(obuild.LIB):
+        obuild.build()
+    wl = synth.WORKLOADS[wl_name]
+    J = min(args.cpu_sample_sgs, wl.d // 256)
+    grads = [synth.as_numpy(g) for g in synth.generate(wl_name, d=256 * J, device=device)]
+    topo = po.BUTTERFLY if wl.topology == "butterfly" else po.RING
+    o = po.Oracle(256 * J, wl.n, topo, budget, seed=wl.rounding_seed)
+    t0 = time.perf_counter()
+    o.allreduce(grads)
+    dt = time.perf_counter() - t0
+    dar = dar_coords_per_round(wl.n, wl.topology, 256 * J)
+    return {"value": dar / dt, "unit": "coords/s", "cores": po.get_threads(), "kind": "oracle",
+            "sample": f"whole round of the {wl_name} workload scaled to {J} super-groups "
+                      f"({256 * J} coords x {wl.n} workers), same recipe and schedule; "
+                      f"{dt:.2f} s", "seconds": dt}
+
+
+def dar_coords_per_round(n, topology, d):
+    if n == 1:
+        return 0
+    if topology == "ring":
+        return (n - 1) * d
+    L = n.bit_length() - 1
+    return sum(n * d // (2 ** s) for s in range(1, L + 1))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the virtual workers of the simulated all-reduce "
+              f"share one MI355X, so --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from compressed_hop_gradient_amd import dq, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS[args.workload]
+    budget = wl.budget if args.budget is None else args.budget
+    topo = dq.BUTTERFLY if wl.topology == "butterfly" else dq.RING
+    print(f"[bench] generating {args.workload}: {wl.n} x {wl.d} {wl.dtype}", file=sys.stderr, flush=True)
+    grads = synth.generate(args.workload, device=dev)
+    torch.cuda.synchronize()
+
+    plan = dq.Plan(wl.d, wl.n, topo, budget, seed=wl.rounding_seed, device=dev, timing=True)
+    arena = torch.empty(plan.arena_bytes(), dtype=torch.uint8, device=dev)
+    out = torch.empty(wl.d, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        plan.allreduce(grads, out=out, arena=arena, stream=stream)
+        print(f"[bench] warmup {i + 1}/{args.warmup}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    plan.timing()  # discard warm-up launch timings
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        plan.allreduce(grads, out=out, arena=arena, stream=stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
+    tim = plan.timing()
+    info = plan.info()
+    secs = t1 - t0
+    ms_per_step = 1e3 * secs / args.steps
+    dar_coords = tim["hop_grad"]["coords"] + tim["hop_packed"]["coords"]
+    value = dar_coords / secs
+
+    b = info["achieved_bits"]
+    bpc = dar_bytes_per_coord(b)
+    hg = tim["hop_grad"]
+    launches = max(1, hg["launches"])
+    bytes_per_launch = hg["coords"] / launches * bpc
+    avg_ms = hg["ms"] / launches
+    achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
+    src_hash = kernel_source_hash()
+    traffic = measured_traffic("hop_grad", src_hash)
+
+    kernels = {}
+    for k, v in tim.items():
+        if v["launches"]:
+            kernels[k] = {"ms_per_step": v["ms"] / args.steps, "launches_per_step": v["launches"] / args.steps,
+                          "coords_per_s": (v["coords"] / (v["ms"] * 1e-3)) if v["ms"] > 0 else None}
+
+    quality = None
+    if not args.no_quality:
+        exact = torch.zeros(wl.d, dtype=torch.float64, device=dev)
+        for g in grads:
+            exact += g.double()
+        err = ((out.double() - exact) ** 2).sum().item() / (exact ** 2).sum().item()
+        quality = {"vnmse_correlated": err, "achieved_bits": b,
+                   "wire_bits_per_coord": b + 0.625, "stats_traffic_ratio": 8.0 / (256 * 2),
+                   "class_counts": info["class_counts"]}
+        del exact
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "coords/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {wl.d} bf16 coords x {wl.n} virtual workers, "
+                               f"{wl.topology}, {budget:g} bits/coord",
+                   "n_coords": wl.d, "n_workers": wl.n, "topology": wl.topology, "avg_bits": budget},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "DAR hop, bf16 local (k_codec<hop,bf16>)",
+                     "algorithmic_bytes_per_launch": bytes_per_launch,
+                     "bytes_per_coord": bpc, "avg_launch_ms": avg_ms, "launches": hg["launches"],
+                     "kernel_source": src_hash},
+        "dar_kernel_coords_per_s": (hg["coords"] / (hg["ms"] * 1e-3)) if hg["ms"] > 0 else None,
+        "kernels": kernels,
+        "quality": quality,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        del grads, arena, out, plan
+        torch.cuda.empty_cache()
+        res["cpu_baseline"] = cpu_baseline(args, args.workload, budget, dev)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
