@@ -15,6 +15,8 @@ FLAGS = [
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",
     # packed FP32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the compile-time check of the level buckets walks every bucket
+    "-fconstexpr-steps=100000000",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 SOURCES = ["dq_kernels.hip", "dq_api.cpp"]

@@ -424,10 +424,10 @@ dq_status dq_compress(dq_plan *p, int32_t w, int32_t step, const void *grad, int
     CodecArgs a;
     fill_common(p, a);
     fill_rng(p, w, step, a);
-    a.m = sp.m;
-    a.part = sp.part;
+    a.m_out = a.m_in = sp.m;
+    a.part_out = a.part_in = sp.part;
     a.grad = grad;
-    a.out0 = static_cast<uint8_t *>(out);
+    a.out = static_cast<uint8_t *>(out);
     Launch L;
     hipError_t e = timed_begin(p, DQ_K_COMPRESS, sp.m, sp.part, s, L);
     if (e == hipSuccess) e = launch_codec(a, kCompress, local_of_kind(kind), max_part_sg(p, sp.m), s);
@@ -453,19 +453,25 @@ dq_status dq_hop(dq_plan *p, int32_t w, int32_t step, const void *in, const void
     CodecArgs a;
     fill_common(p, a);
     fill_rng(p, w, step, a);
-    a.m = sp.m;
-    a.part = sp.part;
-    a.two_children = sp.two_children ? 1 : 0;
+    a.m_in = sp.m;
+    a.part_in = sp.part;
     a.region_in = static_cast<const uint8_t *>(in);
     if (local_kind == DQ_PACKED) a.region_own = static_cast<const uint8_t *>(local);
     else a.grad = local;
-    a.out0 = static_cast<uint8_t *>(out0);
-    a.out1 = static_cast<uint8_t *>(sp.two_children ? out1 : out0);
-    Launch L;
     const int kindk = local_kind == DQ_PACKED ? DQ_K_HOP_PACKED : DQ_K_HOP_GRAD;
-    hipError_t e = timed_begin(p, kindk, sp.m, sp.part, s, L);
-    if (e == hipSuccess) e = launch_codec(a, kHop, local_of_kind(local_kind), max_part_sg(p, sp.m), s);
-    if (e == hipSuccess) e = timed_end(p, L, s);
+    // one launch per output region: the part itself, or each of its two children
+    const int nout = sp.two_children ? 2 : 1;
+    hipError_t e = hipSuccess;
+    for (int h = 0; h < nout && e == hipSuccess; h++) {
+        a.m_out = sp.two_children ? 2 * sp.m : sp.m;
+        a.part_out = sp.two_children ? 2 * sp.part + h : sp.part;
+        a.out = static_cast<uint8_t *>(h == 0 ? out0 : out1);
+        Launch L;
+        e = timed_begin(p, kindk, a.m_out, a.part_out, s, L);
+        if (e == hipSuccess)
+            e = launch_codec(a, kHop, local_of_kind(local_kind), max_part_sg(p, a.m_out), s);
+        if (e == hipSuccess) e = timed_end(p, L, s);
+    }
     return hip_status(e);
 }
 
@@ -478,8 +484,8 @@ dq_status dq_finalize(dq_plan *p, int64_t part, const void *region, float *out, 
     hipStream_t s = static_cast<hipStream_t>(stream);
     CodecArgs a;
     fill_common(p, a);
-    a.m = p->n;
-    a.part = part;
+    a.m_out = a.m_in = p->n;
+    a.part_out = a.part_in = part;
     a.region_in = static_cast<const uint8_t *>(region);
     a.out_f32 = out;
     Launch L;

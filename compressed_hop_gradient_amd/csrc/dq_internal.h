@@ -26,17 +26,19 @@ struct Ctrl {
 enum Mode { kCompress = 0, kHop = 1, kFinalize = 2 };
 enum Local { kLocalNone = 0, kLocalBF16 = 1, kLocalF32 = 2, kLocalPacked = 3 };
 
-// arguments of one codec launch (compress / hop / finalize) on one part
+// arguments of one codec launch (compress / hop / finalize).  A launch covers
+// the super-groups of one output part (m_out, part_out); the input regions
+// (incoming and own packed) hold the part (m_in, part_in) that contains it
+// (the same part, or its parent when a hop writes the two children).
 struct CodecArgs {
     const unsigned long long *class_counts;  // device, C_2, C_4, C_8
-    int64_t m, part;                         // part `part` of m
-    int32_t two_children;                    // hop output split into parts 2c, 2c+1 of 2m
+    int64_t m_out, part_out, m_in, part_in;
     const int32_t *perm;
     const float *mu_stream;
     const void *grad;                        // local gradient (bf16 / f32)
     const uint8_t *region_in;                // incoming region (hop, finalize)
     const uint8_t *region_own;               // own packed region (butterfly level >= 2)
-    uint8_t *out0, *out1;                    // output region(s)
+    uint8_t *out;                            // output region of (m_out, part_out)
     float *out_f32;                          // finalize output, original order
     float n_workers_f;                       // finalize: fl(n * mu)
     uint32_t key0, key1, round, tag, stagger;

@@ -22,6 +22,8 @@
 namespace dq {
 
 __device__ const LevelTables g_tables = kLevelTables;
+__device__ const BucketTable<256> g_buckets8 = kBuckets8;
+__device__ const BucketTable<16> g_buckets4 = kBuckets4;
 
 // ---------------------------------------------------------------------------
 // small device helpers
@@ -84,20 +86,21 @@ __device__ __forceinline__ int group_code(float a, float s) {
     return c;
 }
 
-// Interval search over NL = 16 or 256 levels: r = largest r <= NL-2 with L[r] <= v.  The
-// closed-form inverse of the level map gives an estimate that is r or r-1
-// (its error is far below half an index); one compare against the next level
-// settles it.  Returns r and the level / weight of interval r.
-template <int NL>
-__device__ __forceinline__ int search_levels(float v, const Row4 *rows, float &Lr, float &Wr) {
-    constexpr float hq = 0.5f * float(NL - 1);
-    const float av = fabsf(v);
-    const float sq = __builtin_amdgcn_sqrtf(fmaf(8.0f, av, 1.0f));
-    const float t = (sq - 1.0f) * 0.5f;
-    const float u = copysignf(t, v);
-    const float rc = fmaf(hq, u, hq - 0.5f);
-    int est = (int)floorf(rc);
-    est = min(max(est, 0), NL - 2);
+// Interval search over NL = 16 or 256 levels: r = largest r <= NL-2 with
+// L[r] <= v.  The bucket of v (exponent and 7 mantissa bits of |v|, and the
+// sign) holds at most one level boundary, so its table entry is r or r - 1;
+// one compare with the next level settles it.  Returns r and the level /
+// weight of interval r.
+__device__ __forceinline__ int bucket_index(float v) {
+    const uint32_t b = __float_as_uint(v);
+    int k = (int)((b >> 16) & 0x7FFFu) - kKeyBase;
+    k = min(max(k, 0), kKeyMax);
+    return k + ((b >> 31) ? kKeys : 0);
+}
+
+__device__ __forceinline__ int search_levels(float v, const uint8_t *est_tab, const Row4 *rows,
+                                             float &Lr, float &Wr) {
+    const int est = est_tab[bucket_index(v)];
     const Row4 row = rows[est];
     const bool up = v >= row.l1;
     Lr = up ? row.l1 : row.l0;
@@ -119,8 +122,8 @@ __device__ __forceinline__ int search_levels2(float v, float &Lr, float &Wr) {
 // ---------------------------------------------------------------------------
 
 struct PartInfo {
-    int64_t lo[3], cnt[3], N;
-    int64_t offc[3], offs, offg;
+    int64_t lo[3], cnt[3], pre[3], N;   // stream start, count, part-local start per class
+    int64_t offc[3], offs, offg;        // region byte offsets: codes per class, scales, group codes
 };
 
 __device__ __forceinline__ void part_info(const unsigned long long *C, int64_t m, int64_t c,
@@ -133,6 +136,7 @@ __device__ __forceinline__ void part_info(const unsigned long long *C, int64_t m
         const int64_t a = c * Ck / m, b = (c + 1) * Ck / m;
         p.lo[k] = base + a;
         p.cnt[k] = b - a;
+        p.pre[k] = p.N;
         p.N += b - a;
         base += Ck;
     }
@@ -153,6 +157,8 @@ struct SharedTables {
     float dec8[256];
     Row4 r4[15];
     Row4 r8[255];
+    uint8_t b4[2 * kKeys];
+    uint8_t b8[2 * kKeys];
 };
 
 template <int B>
@@ -208,18 +214,23 @@ __device__ __forceinline__ void decode_group(const uint8_t *region, int64_t offc
 // codec kernel: compress / hop / finalize on one part
 // ---------------------------------------------------------------------------
 
-// Q = bits per code of this super-group's class; K = its class index
+// One super-group per 16-lane row, one group of 16 coordinates per lane.
+// Q = bits per code of the super-group's class, K = the class index.
+// Po = output part, Pi = input part (the same part or its parent).
 template <int Q, int MODE, int LOCAL>
-__device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo *P, int64_t t,
-                                         int64_t idx, int g, const SharedTables &T) {
+__device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po,
+                                         const PartInfo &Pi, int64_t t, int g,
+                                         const SharedTables &T) {
     constexpr int K = Q == 2 ? 0 : (Q == 4 ? 1 : 2);
-    const PartInfo &pin = P[0];
-    const int64_t pos = pin.lo[K] + idx;          // stream position
+    const int64_t idx = t - Po.pre[K];            // index in the class, output part
+    const int64_t pos = Po.lo[K] + idx;           // stream position
     const int64_t j = a.perm[pos];                // original super-group
+    const int64_t idx_in = pos - Pi.lo[K];        // index in the class, input part
+    const int64_t t_in = Pi.pre[K] + idx_in;
     float y[16];
 
-    if constexpr (MODE != kCompress) decode_group<Q>(a.region_in, pin.offc[K], pin.offs, pin.offg,
-                                                     t, idx, g, T, y);
+    if constexpr (MODE != kCompress)
+        decode_group<Q>(a.region_in, Pi.offc[K], Pi.offs, Pi.offg, t_in, idx_in, g, T, y);
 
     if constexpr (MODE == kFinalize) {
         const float add = a.n_workers_f * a.mu_stream[pos];
@@ -228,103 +239,90 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo *P, 
         for (int v = 0; v < 4; v++)
             o[v] = make_float4(y[4 * v] + add, y[4 * v + 1] + add, y[4 * v + 2] + add, y[4 * v + 3] + add);
     } else {
-    const float mu = a.mu_stream[pos];
-    if constexpr (LOCAL == kLocalBF16) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(
-            static_cast<const uint16_t *>(a.grad) + j * kSG + g * kGroup);
-        const uint4 h0 = src[0], h1 = src[1];
-        const uint32_t hw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+        const float mu = a.mu_stream[pos];
+        if constexpr (LOCAL == kLocalBF16) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(
+                static_cast<const uint16_t *>(a.grad) + j * kSG + g * kGroup);
+            const uint4 h0 = src[0], h1 = src[1];
+            const uint32_t hw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const float e0 = bf16_lo(hw[i]) - mu, e1 = bf16_hi(hw[i]) - mu;
-            if constexpr (MODE == kHop) {
-                y[2 * i] = y[2 * i] + e0;
-                y[2 * i + 1] = y[2 * i + 1] + e1;
-            } else {
-                y[2 * i] = e0;
-                y[2 * i + 1] = e1;
+            for (int i = 0; i < 8; i++) {
+                const float e0 = bf16_lo(hw[i]) - mu, e1 = bf16_hi(hw[i]) - mu;
+                if constexpr (MODE == kHop) {
+                    y[2 * i] = y[2 * i] + e0;
+                    y[2 * i + 1] = y[2 * i + 1] + e1;
+                } else {
+                    y[2 * i] = e0;
+                    y[2 * i + 1] = e1;
+                }
+            }
+        } else if constexpr (LOCAL == kLocalF32) {
+            const float4 *src = reinterpret_cast<const float4 *>(
+                static_cast<const float *>(a.grad) + j * kSG + g * kGroup);
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                const float4 f = src[v];
+                const float e[4] = {f.x - mu, f.y - mu, f.z - mu, f.w - mu};
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    if constexpr (MODE == kHop) y[4 * v + i] = y[4 * v + i] + e[i];
+                    else y[4 * v + i] = e[i];
+                }
+            }
+        } else if constexpr (LOCAL == kLocalPacked) {
+            float own[16];
+            decode_group<Q>(a.region_own, Pi.offc[K], Pi.offs, Pi.offg, t_in, idx_in, g, T, own);
+#pragma unroll
+            for (int i = 0; i < 16; i++) y[i] = y[i] + own[i];
+        }
+
+        // ---- encode ----
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(y[i]));
+        const float A = row_max16(amax);
+        const float s = scale_unit(A);
+        const int c = group_code(amax, s);
+        const float sigma = (float)c * s;
+        const float inv = sigma == 0.0f ? 0.0f : 1.0f / sigma;
+
+        typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+        const ushort2_t stag = {(unsigned short)a.stagger, (unsigned short)a.stagger};
+        uint32_t w[Q / 2];
+#pragma unroll
+        for (int i = 0; i < Q / 2; i++) w[i] = 0u;
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            // 8 dithers of coordinates 8h..8h+7 of this group from one Philox call
+            uint32_t x0 = 2u * g + h, x1 = (uint32_t)j, x2 = a.round, x3 = a.tag;
+            philox4x32_10(x0, x1, x2, x3, a.key0, a.key1);
+            // add the worker's stagger to both 16-bit halves (mod 65536)
+            uint32_t d[4] = {x0, x1, x2, x3};
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                ushort2_t hv = __builtin_bit_cast(ushort2_t, d[q]);
+                hv = hv + stag;
+                d[q] = __builtin_bit_cast(uint32_t, hv);
+            }
+#pragma unroll
+            for (int ii = 0; ii < 8; ii++) {
+                const int i = 8 * h + ii;
+                const float v = fminf(fmaxf(y[i] * inv, -1.0f), 1.0f);
+                float Lr, Wr;
+                int r;
+                if constexpr (Q == 2) r = search_levels2(v, Lr, Wr);
+                else if constexpr (Q == 4) r = search_levels(v, T.b4, T.r4, Lr, Wr);
+                else r = search_levels(v, T.b8, T.r8, Lr, Wr);
+                const float P = (v - Lr) * Wr;
+                const uint32_t dd = (ii & 1) ? (d[ii >> 1] >> 16) : (d[ii >> 1] & 0xFFFFu);
+                const uint32_t code = (uint32_t)r + (((float)dd + 0.5f) < P ? 1u : 0u);
+                w[(i * Q) / 32] |= code << ((i * Q) % 32);
             }
         }
-    } else if constexpr (LOCAL == kLocalF32) {
-        const float4 *src = reinterpret_cast<const float4 *>(
-            static_cast<const float *>(a.grad) + j * kSG + g * kGroup);
-#pragma unroll
-        for (int v = 0; v < 4; v++) {
-            const float4 f = src[v];
-            const float e[4] = {f.x - mu, f.y - mu, f.z - mu, f.w - mu};
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                if constexpr (MODE == kHop) y[4 * v + i] = y[4 * v + i] + e[i];
-                else y[4 * v + i] = e[i];
-            }
-        }
-    } else if constexpr (LOCAL == kLocalPacked) {
-        float own[16];
-        decode_group<Q>(a.region_own, pin.offc[K], pin.offs, pin.offg, t, idx, g, T, own);
-#pragma unroll
-        for (int i = 0; i < 16; i++) y[i] = y[i] + own[i];
-    }
 
-    // ---- encode ----
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(y[i]));
-    const float A = row_max16(amax);
-    const float s = scale_unit(A);
-    const int c = group_code(amax, s);
-    const float sigma = (float)c * s;
-    const float inv = sigma == 0.0f ? 0.0f : 1.0f / sigma;
-
-    uint32_t w[Q / 2];
-#pragma unroll
-    for (int i = 0; i < Q / 2; i++) w[i] = 0u;
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-        // 8 dithers of coordinates 8h..8h+7 of this group from one Philox call
-        uint32_t x0 = 2u * g + h, x1 = (uint32_t)j, x2 = a.round, x3 = a.tag;
-        philox4x32_10(x0, x1, x2, x3, a.key0, a.key1);
-        const uint32_t d[4] = {x0, x1, x2, x3};
-#pragma unroll
-        for (int ii = 0; ii < 8; ii++) {
-            const int i = 8 * h + ii;
-            const float v = fminf(fmaxf(y[i] * inv, -1.0f), 1.0f);
-            float Lr, Wr;
-            int r;
-            if constexpr (Q == 2) r = search_levels2(v, Lr, Wr);
-            else if constexpr (Q == 4) r = search_levels<16>(v, T.r4, Lr, Wr);
-            else r = search_levels<256>(v, T.r8, Lr, Wr);
-            const float P = (v - Lr) * Wr;
-            const uint32_t d0 = (ii & 1) ? (d[ii >> 1] >> 16) : (d[ii >> 1] & 0xFFFFu);
-            const uint32_t dd = (d0 + a.stagger) & 0xFFFFu;
-            const uint32_t code = (uint32_t)r + (((float)dd + 0.5f) < P ? 1u : 0u);
-            w[(i * Q) / 32] |= code << ((i * Q) % 32);
-        }
-    }
-
-    // ---- output slot (one region, or the child the super-group falls in) ----
-    // The part layouts live in LDS (P[0] = this part, P[1], P[2] = its
-    // children); the child is picked by index so only its fields are read.
-    int sel = 0;
-    int64_t idx_o = idx;
-    uint8_t *region = a.out0;
-    if (MODE == kHop && a.two_children) {
-        const int64_t split = P[1].cnt[K];
-        const bool second = idx >= split;
-        sel = second ? 2 : 1;
-        idx_o = second ? idx - split : idx;
-        const uintptr_t r0 = reinterpret_cast<uintptr_t>(a.out0);
-        const uintptr_t r1 = reinterpret_cast<uintptr_t>(a.out1);
-        region = reinterpret_cast<uint8_t *>(second ? r1 : r0);
-    }
-    const PartInfo &po = P[sel];
-    int64_t t_o = idx_o;
-    if constexpr (K > 0) t_o += po.cnt[0];
-    if constexpr (K > 1) t_o += po.cnt[1];
-    if (sel == 0) t_o = t;
-    const int64_t offc = po.offc[K], offs = po.offs, offg = po.offg;
-    store_codes<Q>(region + offc + idx_o * (32 * Q) + g * (2 * Q), w);
-    region[offg + 16 * t_o + g] = (uint8_t)c;
-    if (g == 0) *reinterpret_cast<float *>(region + offs + 4 * t_o) = s;
+        store_codes<Q>(a.out + Po.offc[K] + idx * (32 * Q) + g * (2 * Q), w);
+        a.out[Po.offg + 16 * t + g] = (uint8_t)c;
+        if (g == 0) *reinterpret_cast<float *>(a.out + Po.offs + 4 * t) = s;
     }
 }
 
@@ -332,33 +330,34 @@ template <int MODE, int LOCAL>
 __global__ __launch_bounds__(256) void k_codec(CodecArgs a) {
     __shared__ __align__(16) SharedTables T;
     for (int i = threadIdx.x; i < 256; i += blockDim.x) T.dec8[i] = g_tables.L8[i];
-    for (int i = threadIdx.x; i < 255; i += blockDim.x) T.r8[i] = g_tables.R8[i];
+    if constexpr (MODE != kFinalize) {
+        for (int i = threadIdx.x; i < 255; i += blockDim.x) T.r8[i] = g_tables.R8[i];
+        for (int i = threadIdx.x; i < 2 * kKeys; i += blockDim.x) {
+            T.b8[i] = g_buckets8.est[i];
+            T.b4[i] = g_buckets4.est[i];
+        }
+        if (threadIdx.x < 15) T.r4[threadIdx.x] = g_tables.R4[threadIdx.x];
+    }
     if (threadIdx.x < 16) T.dec4[threadIdx.x] = g_tables.L4[threadIdx.x];
-    if (threadIdx.x < 15) T.r4[threadIdx.x] = g_tables.R4[threadIdx.x];
     if (threadIdx.x < 4) T.dec2[threadIdx.x] = g_tables.L2[threadIdx.x];
-    __syncthreads();
 
     // part layouts: computed once per block, read back as LDS broadcasts
-    __shared__ PartInfo P[3];
-    if (threadIdx.x == 0) {
-        part_info(a.class_counts, a.m, a.part, P[0]);
-        if (MODE == kHop && a.two_children) {
-            part_info(a.class_counts, 2 * a.m, 2 * a.part, P[1]);
-            part_info(a.class_counts, 2 * a.m, 2 * a.part + 1, P[2]);
-        }
-    }
+    __shared__ PartInfo P[2];
+    if (threadIdx.x == 0) part_info(a.class_counts, a.m_out, a.part_out, P[0]);
+    if (threadIdx.x == 64) part_info(a.class_counts, a.m_in, a.part_in, P[1]);
     __syncthreads();
-    const PartInfo &pin = P[0];
+    const PartInfo &Po = P[0], &Pi = P[1];
+
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane & 15, row = lane >> 4;
-    for (int64_t base = (int64_t)blockIdx.x * kSGPerBlock; base < pin.N;
+    const int64_t N = Po.N;
+    for (int64_t base = (int64_t)blockIdx.x * kSGPerBlock; base < N;
          base += (int64_t)gridDim.x * kSGPerBlock) {
         const int64_t t = base + wave * 4 + row;
-        if (t >= pin.N) continue;
-        const int64_t n0 = pin.cnt[0], n01 = pin.cnt[0] + pin.cnt[1];
-        if (t < n0) codec_sg<2, MODE, LOCAL>(a, P, t, t, g, T);
-        else if (t < n01) codec_sg<4, MODE, LOCAL>(a, P, t, t - n0, g, T);
-        else codec_sg<8, MODE, LOCAL>(a, P, t, t - n01, g, T);
+        if (t >= N) continue;
+        if (t < Po.pre[1]) codec_sg<2, MODE, LOCAL>(a, Po, Pi, t, g, T);
+        else if (t < Po.pre[2]) codec_sg<4, MODE, LOCAL>(a, Po, Pi, t, g, T);
+        else codec_sg<8, MODE, LOCAL>(a, Po, Pi, t, g, T);
     }
 }
 

@@ -56,6 +56,82 @@ constexpr LevelTables make_tables() {
 
 constexpr LevelTables kLevelTables = make_tables();
 
+// ---------------------------------------------------------------------------
+// Bucket index for the interval search.  The key of v is 7 mantissa bits and
+// the exponent of |v| (fp32 bits >> 16), offset so that key 0 holds every
+// |v| < 2^-9 (below the smallest positive 8-bit level) and key kKeyMax holds
+// |v| = 1.  Each bucket is at most 2^-7 wide relative to its start, narrower
+// than the closest pair of levels, so it contains at most one level boundary:
+// the table gives r or r - 1 and one compare with the next level decides.
+// Entries [0, kKeys) serve v >= 0, entries [kKeys, 2 kKeys) serve v < 0.
+// ---------------------------------------------------------------------------
+
+constexpr int kKeyBase = 0x3B00;              // fp32 bits of 2^-9, >> 16
+constexpr int kKeyMax = 0x3F80 - kKeyBase;    // key of 1.0
+constexpr int kKeys = kKeyMax + 1;
+
+constexpr float key_lo(int k) {
+    return k == 0 ? 0.0f : __builtin_bit_cast(float, (unsigned)(k + kKeyBase) << 16);
+}
+constexpr float key_hi(int k) {
+    return k == kKeyMax ? 1.0f : __builtin_bit_cast(float, (unsigned)(k + 1 + kKeyBase) << 16);
+}
+
+template <int NL>
+struct BucketTable {
+    unsigned char est[2 * kKeys];
+};
+
+// est for v >= 0 in bucket k: largest r <= NL-2 with L[r] <= key_lo(k);
+// est for v < 0: largest r <= NL-2 with L[r] <= -key_hi(k).  Both by sweeps.
+template <int NL>
+constexpr BucketTable<NL> make_buckets() {
+    BucketTable<NL> t{};
+    int r = 0;
+    for (int k = 0; k < kKeys; k++) {
+        const float lo = key_lo(k);
+        while (r + 1 <= NL - 2 && level_f(r + 1, NL) <= lo) r++;
+        t.est[k] = (unsigned char)r;
+    }
+    r = 0;
+    for (int k = kKeys - 1; k >= 0; k--) {
+        const float nh = -key_hi(k);
+        while (r + 1 <= NL - 2 && level_f(r + 1, NL) <= nh) r++;
+        t.est[kKeys + k] = (unsigned char)r;
+    }
+    return t;
+}
+
+// at most one level boundary inside every bucket (sweeps over the levels)
+template <int NL>
+constexpr bool buckets_hold_one_boundary() {
+    // positive side: levels in (key_lo(k), key_hi(k))
+    int r = 0;
+    for (int k = 0; k < kKeys; k++) {
+        const float lo = key_lo(k), hi = key_hi(k);
+        while (r < NL && level_f(r, NL) <= lo) r++;
+        int c = 0;
+        for (int q = r; q < NL && level_f(q, NL) < hi; q++) c++;
+        if (c > 1) return false;
+    }
+    // negative side: levels in (-key_hi(k), -key_lo(k)]
+    for (int k = 0; k < kKeys; k++) {
+        const float a = -key_hi(k), b = -key_lo(k);
+        int c = 0;
+        for (int q = 0; q < NL / 2 + 1; q++) {
+            const float L = level_f(q, NL);
+            if (L > a && L <= b) c++;
+        }
+        if (c > 1) return false;
+    }
+    return true;
+}
+
+constexpr BucketTable<256> kBuckets8 = make_buckets<256>();
+constexpr BucketTable<16> kBuckets4 = make_buckets<16>();
+static_assert(buckets_hold_one_boundary<16>(), "4-bit buckets");
+static_assert(buckets_hold_one_boundary<256>(), "8-bit buckets");  // needs -fconstexpr-steps
+
 // spot checks of the closed form at compile time
 static_assert(kLevelTables.L2[0] == -1.0f && kLevelTables.L2[3] == 1.0f, "endpoints");
 static_assert(kLevelTables.L2[2] == float(2.0 / 9.0), "phi(1/3) = 2/9");
