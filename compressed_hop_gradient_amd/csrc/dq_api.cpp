@@ -59,6 +59,13 @@ int32_t *i32_at(dq_plan *p, size_t off) { return reinterpret_cast<int32_t *>(p->
 int32_t *blkcnt_of(dq_plan *p) {
     return reinterpret_cast<int32_t *>(p->ws + p->lay.ctrl + align_up(sizeof(Ctrl), kAlign));
 }
+PartInfo *parts_of(dq_plan *p) {
+    return reinterpret_cast<PartInfo *>(p->ws + p->lay.ctrl + align_up(sizeof(Ctrl), kAlign) +
+                                        align_up(4 * 3 * (size_t)p->nblk, kAlign));
+}
+const PartInfo *part_entry(dq_plan *p, int64_t m, int64_t c) {
+    return parts_of(p) + part_table_index(p->n, p->topo, m, c);
+}
 
 void compute_layout(dq_plan *p) {
     const size_t J = (size_t)p->J;
@@ -72,6 +79,7 @@ void compute_layout(dq_plan *p) {
     p->lay.ctrl = off;
     off = align_up(off + sizeof(Ctrl), kAlign);
     off = align_up(off + 4 * 3 * (size_t)p->nblk, kAlign);
+    off = align_up(off + sizeof(PartInfo) * (size_t)part_table_entries(p->n, p->topo), kAlign);
     p->lay.total = off;
 }
 
@@ -164,7 +172,6 @@ void fill_rng(const dq_plan *p, int32_t w, int32_t step, CodecArgs &a) {
 
 void fill_common(dq_plan *p, CodecArgs &a) {
     std::memset(&a, 0, sizeof(a));
-    a.class_counts = ctrl_of(p)->class_counts;
     a.perm = i32_at(p, p->lay.perm);
     a.mu_stream = f32_at(p, p->lay.mu_stream);
     a.n_workers_f = (float)p->n;
@@ -405,6 +412,7 @@ dq_status dq_reorder(dq_plan *p, void *stream) {
     Launch L;
     hipError_t e = timed_begin(p, DQ_K_REORDER, 0, 0, s, L);
     if (e == hipSuccess) e = launch_reorder(a, s);
+    if (e == hipSuccess) e = launch_part_table(ctrl_of(p)->class_counts, p->n, p->topo, parts_of(p), s);
     if (e == hipSuccess) e = timed_end(p, L, s);
     if (e != hipSuccess) return DQ_EHIP;
     p->reordered = true;
@@ -424,8 +432,7 @@ dq_status dq_compress(dq_plan *p, int32_t w, int32_t step, const void *grad, int
     CodecArgs a;
     fill_common(p, a);
     fill_rng(p, w, step, a);
-    a.m_out = a.m_in = sp.m;
-    a.part_out = a.part_in = sp.part;
+    a.part_out = a.part_in = part_entry(p, sp.m, sp.part);
     a.grad = grad;
     a.out = static_cast<uint8_t *>(out);
     Launch L;
@@ -453,8 +460,7 @@ dq_status dq_hop(dq_plan *p, int32_t w, int32_t step, const void *in, const void
     CodecArgs a;
     fill_common(p, a);
     fill_rng(p, w, step, a);
-    a.m_in = sp.m;
-    a.part_in = sp.part;
+    a.part_in = part_entry(p, sp.m, sp.part);
     a.region_in = static_cast<const uint8_t *>(in);
     if (local_kind == DQ_PACKED) a.region_own = static_cast<const uint8_t *>(local);
     else a.grad = local;
@@ -463,13 +469,14 @@ dq_status dq_hop(dq_plan *p, int32_t w, int32_t step, const void *in, const void
     const int nout = sp.two_children ? 2 : 1;
     hipError_t e = hipSuccess;
     for (int h = 0; h < nout && e == hipSuccess; h++) {
-        a.m_out = sp.two_children ? 2 * sp.m : sp.m;
-        a.part_out = sp.two_children ? 2 * sp.part + h : sp.part;
+        const int64_t m_out = sp.two_children ? 2 * sp.m : sp.m;
+        const int64_t c_out = sp.two_children ? 2 * sp.part + h : sp.part;
+        a.part_out = part_entry(p, m_out, c_out);
         a.out = static_cast<uint8_t *>(h == 0 ? out0 : out1);
         Launch L;
-        e = timed_begin(p, kindk, a.m_out, a.part_out, s, L);
+        e = timed_begin(p, kindk, m_out, c_out, s, L);
         if (e == hipSuccess)
-            e = launch_codec(a, kHop, local_of_kind(local_kind), max_part_sg(p, a.m_out), s);
+            e = launch_codec(a, kHop, local_of_kind(local_kind), max_part_sg(p, m_out), s);
         if (e == hipSuccess) e = timed_end(p, L, s);
     }
     return hip_status(e);
@@ -484,8 +491,7 @@ dq_status dq_finalize(dq_plan *p, int64_t part, const void *region, float *out, 
     hipStream_t s = static_cast<hipStream_t>(stream);
     CodecArgs a;
     fill_common(p, a);
-    a.m_out = a.m_in = p->n;
-    a.part_out = a.part_in = part;
+    a.part_out = a.part_in = part_entry(p, p->n, part);
     a.region_in = static_cast<const uint8_t *>(region);
     a.out_f32 = out;
     Launch L;

@@ -24,6 +24,20 @@ struct Ctrl {
 };
 
 enum Mode { kCompress = 0, kHop = 1, kFinalize = 2 };
+
+// Layout of one part (m, c) of the bitwidth-sorted stream and of its region;
+// computed once per round on the device (k_part_table) for every part the
+// schedule uses.
+struct PartInfo {
+    int64_t lo[3];     // first stream position of each class in the part
+    int64_t cnt[3];    // super-groups of each class
+    int64_t pre[3];    // part-local index of each class's first super-group
+    int64_t N;         // super-groups in the part
+    int64_t offc[3];   // region byte offset of each class's codes
+    int64_t offs;      // region byte offset of the fp32 scale units
+    int64_t offg;      // region byte offset of the UINT8 group codes
+    int64_t bytes;     // region size
+};
 enum Local { kLocalNone = 0, kLocalBF16 = 1, kLocalF32 = 2, kLocalPacked = 3 };
 
 // arguments of one codec launch (compress / hop / finalize).  A launch covers
@@ -31,8 +45,8 @@ enum Local { kLocalNone = 0, kLocalBF16 = 1, kLocalF32 = 2, kLocalPacked = 3 };
 // (incoming and own packed) hold the part (m_in, part_in) that contains it
 // (the same part, or its parent when a hop writes the two children).
 struct CodecArgs {
-    const unsigned long long *class_counts;  // device, C_2, C_4, C_8
-    int64_t m_out, part_out, m_in, part_in;
+    const PartInfo *part_out;                // device part table entries
+    const PartInfo *part_in;
     const int32_t *perm;
     const float *mu_stream;
     const void *grad;                        // local gradient (bf16 / f32)
@@ -91,6 +105,12 @@ hipError_t launch_alloc_step(const AllocArgs &a, int step, hipStream_t s);
 hipError_t launch_alloc_final(const AllocArgs &a, hipStream_t s);
 hipError_t launch_reorder(const ReorderArgs &a, hipStream_t s);
 hipError_t launch_codec(const CodecArgs &a, int mode, int local, int64_t max_sg, hipStream_t s);
+// part table for the schedule of n workers: ring entry c = part c of n;
+// butterfly entry (m - 2) + c = part c of m for m = 2, 4, .., n; n = 1: one entry
+int32_t part_table_entries(int32_t n, int32_t topology);
+int32_t part_table_index(int32_t n, int32_t topology, int64_t m, int64_t c);
+hipError_t launch_part_table(const unsigned long long *class_counts, int32_t n, int32_t topology,
+                             PartInfo *table, hipStream_t s);
 hipError_t launch_mxfp8(const Mxfp8Args &a, hipStream_t s);
 
 }  // namespace dq
