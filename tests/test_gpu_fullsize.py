@@ -1,0 +1,224 @@
+"""Parity at the workloads' full sizes, in the launch configuration the
+benchmark uses (the same library calls on the same buffer sizes).
+
+The oracle computes every statistic, the allocation and the reorder itself from
+a host copy of the inputs, and these are compared over every super-group.  It
+then follows a sample of super-groups (class and part boundaries plus random
+ones) through every compress and hop of the schedule: after each step the
+sampled super-groups' region bytes are compared, and at the end their decoded
+output.  Inputs come from the shared seeded generator (drawn on the GPU).
+"""
+import numpy as np
+import pytest
+import torch
+
+from compressed_hop_gradient_amd import dq, synth
+from oracle import pyoracle as po
+from tests import regions as R
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+DEV = "cuda"
+
+
+def _bits(a):
+    return np.ascontiguousarray(a).view(np.uint32)
+
+
+def _host(t):
+    return synth.as_numpy(t)
+
+
+def _sample_positions(C, n, topo, rng, extra=96):
+    """Stream positions at class and part boundaries, plus random ones."""
+    J = int(sum(C))
+    pos = set()
+    ms = [n] if topo == dq.RING else [2 ** s for s in range(1, n.bit_length())]
+    for m in ms:
+        for c in range(m):
+            for lo, cnt in R.part_ranges(C, m, c):
+                if cnt:
+                    pos.update((lo, lo + cnt - 1))
+    pos.update(int(x) for x in rng.integers(0, J, extra))
+    return np.array(sorted(pos), dtype=np.int64)
+
+
+def _gather(region_gpu, C, m, c, positions):
+    """GPU region bytes (codes, scale, group codes) of the sampled positions in part c of m."""
+    rng_ = R.part_ranges(C, m, c)
+    lay = R.layout([cnt for _, cnt in rng_])
+    idx = []
+    keep = []
+    for p in positions:
+        for k, (lo, cnt) in enumerate(rng_):
+            if lo <= p < lo + cnt:
+                i = p - lo
+                local = sum(x for _, x in rng_[:k]) + i
+                q = R.QS[k]
+                a = lay["codes"][k] + i * 32 * q
+                idx.append(np.concatenate([np.arange(a, a + 32 * q), lay["s"] + 4 * local + np.arange(4),
+                                           lay["c"] + 16 * local + np.arange(16)]))
+                keep.append(p)
+    if not keep:
+        return [], []
+    flat = torch.from_numpy(np.concatenate(idx)).to(region_gpu.device)
+    got = region_gpu[flat].cpu().numpy()
+    out, o = [], 0
+    for ii in idx:
+        out.append(got[o:o + ii.size])
+        o += ii.size
+    return keep, out
+
+
+def _oracle_bytes(region_np, C, m, c, p):
+    codes, s, cg = R.sg_raw(region_np, C, m, c, p)
+    return np.frombuffer(codes + s + cg, np.uint8)
+
+
+def _steps(n, topo):
+    if topo == dq.RING:
+        yield ("compress", None, 0)
+        for t in range(1, n):
+            yield ("hop", None, t)
+    else:
+        L = n.bit_length() - 1
+        yield ("compress", None, 1)
+        for s in range(1, L + 1):
+            yield ("hop", None, s)
+
+
+def _run(name, budget, capsys, budgets_stage_only=()):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    wl = synth.WORKLOADS[name]
+    topo = dq.BUTTERFLY if wl.topology == "butterfly" else dq.RING
+    n, d = wl.n, wl.d
+
+    def say(msg):
+        with capsys.disabled():
+            print(f"[fullsize {name}] {msg}", flush=True)
+
+    say("generating")
+    grads = synth.generate(name, device=DEV)
+    torch.cuda.synchronize()
+    say("host copy")
+    gnp = [_host(g) for g in grads]
+
+    plan = dq.Plan(d, n, topo, budget, seed=wl.rounding_seed)
+    orc = po.Oracle(d, n, topo, budget, seed=wl.rounding_seed)
+    say("stats / allocate / reorder")
+    for w in range(n):
+        plan.stats(w, grads[w])
+        orc.stats(w, gnp[w])
+    plan.allocate()
+    plan.reorder()
+    orc.allocate()
+    orc.reorder()
+    torch.cuda.synchronize()
+    s_g, F_g = [x.cpu().numpy() for x in plan.stats_arrays()]
+    s_o, F_o, mu_o = orc.stats_arrays()
+    assert np.array_equal(_bits(s_g), _bits(s_o)), "stats: sum"
+    assert np.array_equal(_bits(F_g), _bits(F_o)), "stats: squared norm"
+    info = plan.info()
+    assert not info["nonfinite"]
+    assert info["rho_bits"] == orc.rho_bits(), "allocate: rho"
+    assert np.array_equal(plan.widths().cpu().numpy(), orc.widths()), "allocate: widths"
+    C = orc.class_counts()
+    assert info["class_counts"] == C.tolist()
+    perm_o, inv_o = orc.perm()
+    perm_g, inv_g = [x.cpu().numpy() for x in plan.perm()]
+    assert np.array_equal(perm_g, perm_o) and np.array_equal(inv_g, inv_o), "reorder"
+    assert np.array_equal(_bits(plan.mu_stream().cpu().numpy()), _bits(mu_o[perm_o])), "reorder: mean"
+
+    positions = _sample_positions(C, n, topo, np.random.default_rng(7))
+    say(f"{positions.size} sampled super-groups through the schedule")
+    L = max(0, n.bit_length() - 1)
+    g_prev, o_prev = {}, {}
+    checked = 0
+    for kind, _, step in _steps(n, topo):
+        g_cur, o_cur = {}, {}
+        for w in range(n):
+            if topo == dq.RING:
+                parts = [(n, w if kind == "compress" else (w - step) % n)]
+            elif kind == "compress":
+                parts = [(2, (w >> (L - 1)) ^ 1)]
+            else:
+                c = w >> (L - step)
+                parts = [(2 ** (step + 1), 2 * c), (2 ** (step + 1), 2 * c + 1)] if step < L else [(n, c)]
+            gout = [plan.new_region(m) for m, _ in parts]
+            oout = [np.zeros(R.region_bytes(C, m, c) + 64, np.uint8) for m, c in parts]
+            if kind == "compress":
+                plan.compress(w, step, grads[w], gout[0])
+                orc.compress(w, step, gnp[w], oout[0], filt=positions)
+            elif topo == dq.RING:
+                src = (w - 1) % n
+                plan.hop(w, step, g_prev[src][0], grads[w], gout[0])
+                orc.hop(w, step, o_prev[src][0], gnp[w], oout[0], filt=positions)
+            else:
+                partner, keep = w ^ (n >> step), (w >> (L - step)) & 1
+                if step == 1:
+                    gi, oi = g_prev[partner][0], o_prev[partner][0]
+                    gl, ol = grads[w], gnp[w]
+                else:
+                    gi, oi = g_prev[partner][keep], o_prev[partner][keep]
+                    gl, ol = g_prev[w][keep], o_prev[w][keep]
+                plan.hop(w, step, gi, gl, gout[0], gout[1] if len(gout) > 1 else None)
+                orc.hop(w, step, oi, ol, oout[0], oout[1] if len(oout) > 1 else None, filt=positions)
+            torch.cuda.synchronize()
+            for (m, c), gb, ob in zip(parts, gout, oout):
+                keep_pos, gbytes = _gather(gb, C, m, c, positions)
+                for p, gbb in zip(keep_pos, gbytes):
+                    obb = _oracle_bytes(ob, C, m, c, p)
+                    assert np.array_equal(gbb, obb), f"{kind} worker {w} step {step}: position {p} differs"
+                    checked += 1
+            g_cur[w], o_cur[w] = gout, oout
+        g_prev, o_prev = g_cur, o_cur
+        say(f"{kind} step {step} ok")
+    out_g = torch.full((d,), float("nan"), dtype=torch.float32, device=DEV)
+    out_o = np.zeros(d, np.float32)
+    for w in range(n):
+        part = plan.final_part(w)
+        plan.finalize(part, g_prev[w][0], out_g)
+        orc.finalize(part, o_prev[w][0], out_o, filt=positions)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out_g).any(), "finalize left a coordinate unwritten"
+    cols = (perm_o[positions].astype(np.int64)[:, None] * 256 + np.arange(256)[None, :]).ravel()
+    got = out_g[torch.from_numpy(cols).to(DEV)].cpu().numpy()
+    assert np.array_equal(_bits(got), _bits(out_o[cols])), "finalize: output"
+    say(f"{checked} sampled region records and {positions.size} output super-groups bit-exact")
+
+    for b in budgets_stage_only:
+        p2 = dq.Plan(d, n, topo, b, seed=wl.rounding_seed)
+        o2 = po.Oracle(d, n, topo, b, seed=wl.rounding_seed)
+        for w in range(n):
+            p2.stats(w, grads[w])
+            o2.stats(w, gnp[w])
+        p2.allocate()
+        p2.reorder()
+        o2.allocate()
+        o2.reorder()
+        i2 = p2.info()
+        assert i2["rho_bits"] == o2.rho_bits() and i2["used_bits"] <= i2["budget_bits"]
+        assert np.array_equal(p2.widths().cpu().numpy(), o2.widths())
+        assert np.array_equal(p2.perm()[0].cpu().numpy(), o2.perm()[0])
+        say(f"budget {b}: allocation and reorder bit-exact ({i2['achieved_bits']:.4f} bits)")
+
+
+@pytest.mark.timeout(600)
+def test_bert_full(capsys):
+    _run("bert", 5.0, capsys)
+
+
+@pytest.mark.timeout(600)
+def test_gemma_full(capsys):
+    _run("gemma", 5.0, capsys)
+
+
+@pytest.mark.timeout(900)
+def test_llama_full(capsys):
+    _run("llama", 5.0, capsys, budgets_stage_only=(3.0, 4.0, 6.0))
+
+
+@pytest.mark.timeout(900)
+def test_large_full(capsys):
+    _run("large", 5.0, capsys)
