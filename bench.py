@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-sgs", type=int, default=1 << 20)
     ap.add_argument("--no-quality", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed region, copy this many MiB once with a plain copy kernel "
+                         "(reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -166,14 +169,39 @@ def main():
 
     quality = None
     if not args.no_quality:
+        # same inputs and schedule: DynamiQ (correlated, independent) and MXFP8
         exact = torch.zeros(wl.d, dtype=torch.float64, device=dev)
         for g in grads:
             exact += g.double()
-        err = ((out.double() - exact) ** 2).sum().item() / (exact ** 2).sum().item()
-        quality = {"vnmse_correlated": err, "achieved_bits": b,
-                   "wire_bits_per_coord": b + 0.625, "stats_traffic_ratio": 8.0 / (256 * 2),
-                   "class_counts": info["class_counts"]}
+        norm = (exact ** 2).sum().item()
+
+        def vnmse(o):
+            return ((o.double() - exact) ** 2).sum().item() / norm
+
+        v_corr = vnmse(out)
+        p_ind = dq.Plan(wl.d, wl.n, topo, budget, seed=wl.rounding_seed, rounding=dq.INDEPENDENT,
+                        device=dev)
+        v_ind = vnmse(p_ind.allreduce(grads, out=torch.empty_like(out), arena=arena))
+        del p_ind
+        mx_arena = torch.empty(int(dq.lib().dq_mxfp8_arena_bytes(plan.h)), dtype=torch.uint8, device=dev)
+        v_mx = vnmse(plan.mxfp8_allreduce(grads, out=torch.empty_like(out), arena=mx_arena))
+        del mx_arena
+        quality = {"vnmse_correlated": v_corr, "vnmse_independent": v_ind, "vnmse_mxfp8": v_mx,
+                   "mxfp8_over_dynamiq": v_mx / v_corr, "achieved_bits": b,
+                   "wire_bits_per_coord": b + 0.625, "mxfp8_wire_bits_per_coord": 8.25,
+                   "stats_traffic_ratio": 8.0 / (256 * 2), "class_counts": info["class_counts"]}
         del exact
+
+    copy_cal = None
+    if args.copy_calibration_mib > 0:
+        nb = args.copy_calibration_mib << 20
+        src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        copy_cal = {"bytes_read": nb, "bytes_written": nb}
+        del src, dst
 
     res = {
         "metric": METRIC,
@@ -200,6 +228,7 @@ def main():
         "dar_kernel_coords_per_s": (hg["coords"] / (hg["ms"] * 1e-3)) if hg["ms"] > 0 else None,
         "kernels": kernels,
         "quality": quality,
+        "copy_calibration": copy_cal,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)

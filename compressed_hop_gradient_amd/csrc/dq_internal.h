@@ -88,14 +88,18 @@ struct ReorderArgs {
     float *mu_stream;
 };
 
+// MXFP8 reference codec (quality report only).  Regions hold one E4M3 byte per
+// coordinate of the part, then one E8M0 scale byte per 32 coordinates.
 struct Mxfp8Args {
-    const void *grad;        // local gradient (hop / compress), original order
+    const void *grad;          // local gradient (original order), or nullptr
     int32_t grad_f32;
-    const uint8_t *in;       // incoming region: codes[nblk32] then scales
-    uint8_t *out;
-    float *out_f32;          // finalize
-    int64_t coord_lo, ncoord; // coordinates of the part (multiple of 256)
-    int32_t mode;            // kCompress / kHop / kFinalize
+    const uint8_t *in;         // incoming region (hop / finalize), part [in_lo, in_lo + in_n)
+    const uint8_t *own;        // own region (butterfly level >= 2), same part as `in`
+    int64_t in_lo, in_n;
+    uint8_t *out;              // output region, part [lo, lo + n)
+    float *out_f32;            // finalize output (original order)
+    int64_t lo, n;
+    int32_t mode;              // kCompress / kHop / kFinalize
 };
 
 // launchers (dq_kernels.hip); each returns the hipError_t of its launch
@@ -111,6 +115,6 @@ int32_t part_table_entries(int32_t n, int32_t topology);
 int32_t part_table_index(int32_t n, int32_t topology, int64_t m, int64_t c);
 hipError_t launch_part_table(const unsigned long long *class_counts, int32_t n, int32_t topology,
                              PartInfo *table, hipStream_t s);
-hipError_t launch_mxfp8(const Mxfp8Args &a, hipStream_t s);
+hipError_t launch_mxfp8(const Mxfp8Args &a, int local, hipStream_t s);
 
 }  // namespace dq

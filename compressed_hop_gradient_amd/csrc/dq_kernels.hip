@@ -21,6 +21,8 @@
 
 namespace dq {
 
+static int grid_for(int64_t items, int64_t per_block, int64_t cap);
+
 __device__ const LevelTables g_tables = kLevelTables;
 __device__ const BucketTable<256> g_buckets8 = kBuckets8;
 __device__ const BucketTable<16> g_buckets4 = kBuckets4;
@@ -680,6 +682,107 @@ __global__ __launch_bounds__(256) void k_reorder_scatter(ReorderArgs a) {
         a.inv[j] = p;
         a.mu_stream[p] = a.sum[j] / a.denom;
     }
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8 reference (OCP Microscaling v1.0: 32-element blocks, E8M0 scale
+// 2^(floor(log2 max|x|) - 8) clamped to [2^-127, 2^127], E4M3 elements rounded
+// to nearest even and saturated at 448).  Measurement path for the quality
+// report; one thread per 8 coordinates, a DPP quad per 32-element block.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int floor_log2(float a) {   // a > 0
+    const uint32_t b = __float_as_uint(a);
+    const int e = (int)(b >> 23);
+    if (e != 0) return e - 127;
+    return (31 - __clz(b)) - 149;                      // subnormal
+}
+
+// E4M3 code of v (v already divided by the block scale)
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+    const float a = fabsf(v);
+    if (a == 0.0f) return 0u;
+    const uint32_t sign = (__float_as_uint(v) >> 31) << 7;
+    if (a >= 448.0f) return sign | 0x7Eu;
+    const int ex = max(floor_log2(a), -6);
+    const uint32_t q = (uint32_t)rintf(a * ldexpf(1.0f, 3 - ex));   // exact scaling, nearest even
+    return sign | ((uint32_t)((ex + 6) << 3) + q);
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t code, int se) {
+    const uint32_t mag = code & 0x7Fu, E = mag >> 3, M = mag & 7u;
+    const float m = (float)(E ? 8u + M : M);
+    float v = ldexpf(m, (int)(E ? E : 1u) - 10 + se);
+    return (code & 0x80u) ? -v : v;
+}
+
+template <int MODE, int LOCAL>
+__global__ __launch_bounds__(256) void k_mxfp8(Mxfp8Args a) {
+    const int64_t nthreads = a.n / 8;
+    const int64_t in_codes = a.in_n, out_codes = a.n;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nthreads;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        // a.n is a multiple of 256, so the 4 threads of a quad pass or fail this test together
+        const int64_t i0 = a.lo + 8 * t;                 // first coordinate (original order)
+        float y[8];
+        if constexpr (MODE != kCompress) {
+            const int64_t r = i0 - a.in_lo;
+            const uint2 cw = *reinterpret_cast<const uint2 *>(a.in + r);
+            const int se = (int)a.in[in_codes + r / 32] - 127;
+            for (int i = 0; i < 8; i++) y[i] = e4m3_decode(((i < 4 ? cw.x : cw.y) >> (8 * (i & 3))) & 0xFFu, se);
+        }
+        if constexpr (MODE == kFinalize) {
+            float4 *o = reinterpret_cast<float4 *>(a.out_f32 + i0);
+            o[0] = make_float4(y[0], y[1], y[2], y[3]);
+            o[1] = make_float4(y[4], y[5], y[6], y[7]);
+            continue;
+        } else {
+            float e[8];
+            if constexpr (LOCAL == kLocalBF16) {
+                const uint4 h = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.grad) + i0);
+                const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+                for (int i = 0; i < 4; i++) { e[2 * i] = bf16_lo(hw[i]); e[2 * i + 1] = bf16_hi(hw[i]); }
+            } else if constexpr (LOCAL == kLocalF32) {
+                const float4 *src = reinterpret_cast<const float4 *>(static_cast<const float *>(a.grad) + i0);
+                const float4 f0 = src[0], f1 = src[1];
+                e[0] = f0.x; e[1] = f0.y; e[2] = f0.z; e[3] = f0.w;
+                e[4] = f1.x; e[5] = f1.y; e[6] = f1.z; e[7] = f1.w;
+            } else {
+                const int64_t r = i0 - a.in_lo;
+                const uint2 cw = *reinterpret_cast<const uint2 *>(a.own + r);
+                const int se = (int)a.own[in_codes + r / 32] - 127;
+                for (int i = 0; i < 8; i++) e[i] = e4m3_decode(((i < 4 ? cw.x : cw.y) >> (8 * (i & 3))) & 0xFFu, se);
+            }
+            for (int i = 0; i < 8; i++) y[i] = (MODE == kHop) ? y[i] + e[i] : e[i];
+        }
+        float amax = 0.0f;
+        for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(y[i]));
+        amax = fmaxf(amax, dpp_mov<0xB1>(amax));
+        amax = fmaxf(amax, dpp_mov<0x4E>(amax));
+        int se = -127;
+        if (amax > 0.0f) se = min(max(floor_log2(amax) - 8, -127), 127);
+        uint32_t w0 = 0u, w1 = 0u;
+        for (int i = 0; i < 8; i++) {
+            const uint32_t c = e4m3_encode(ldexpf(y[i], -se));
+            if (i < 4) w0 |= c << (8 * i);
+            else w1 |= c << (8 * (i - 4));
+        }
+        const int64_t r = i0 - a.lo;
+        *reinterpret_cast<uint2 *>(a.out + r) = make_uint2(w0, w1);
+        if ((threadIdx.x & 3) == 0) a.out[out_codes + r / 32] = (uint8_t)(se + 127);
+    }
+}
+
+hipError_t launch_mxfp8(const Mxfp8Args &a, int local, hipStream_t s) {
+    const dim3 grid(grid_for(a.n / 8, 256, 4096)), block(256);
+    if (a.mode == kCompress && local == kLocalBF16) hipLaunchKernelGGL((k_mxfp8<kCompress, kLocalBF16>), grid, block, 0, s, a);
+    else if (a.mode == kCompress && local == kLocalF32) hipLaunchKernelGGL((k_mxfp8<kCompress, kLocalF32>), grid, block, 0, s, a);
+    else if (a.mode == kHop && local == kLocalBF16) hipLaunchKernelGGL((k_mxfp8<kHop, kLocalBF16>), grid, block, 0, s, a);
+    else if (a.mode == kHop && local == kLocalF32) hipLaunchKernelGGL((k_mxfp8<kHop, kLocalF32>), grid, block, 0, s, a);
+    else if (a.mode == kHop && local == kLocalPacked) hipLaunchKernelGGL((k_mxfp8<kHop, kLocalPacked>), grid, block, 0, s, a);
+    else if (a.mode == kFinalize) hipLaunchKernelGGL((k_mxfp8<kFinalize, kLocalNone>), grid, block, 0, s, a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

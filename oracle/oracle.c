@@ -847,3 +847,92 @@ void or_mxfp8_roundtrip(const float *x, int64_t n, float *out) {
         for (int64_t i = lo; i < hi; i++) out[i] = (float)(e4m3_round((double)x[i] / X) * X);
     }
 }
+
+/* ------------------------------------------------------------------ */
+/* MXFP8 in the same schedule (reading: the pages compare DynamiQ with    */
+/* MXFP8 all-reduce, scribe notes "Evaluation").  No mean subtraction and */
+/* no reorder: part c of m is super-groups [floor(cJ/m), floor((c+1)J/m)) */
+/* of the original order.  Every compress and hop re-encodes in MXFP8; a  */
+/* hop adds the decoded incoming values and the local values in fp32.     */
+/* Regions are kept as their decoded fp32 values (decoding is exact).     */
+/* ------------------------------------------------------------------ */
+
+static void mx_part(const or_ctx *c, int64_t m, int64_t part, int64_t *lo, int64_t *hi) {
+    *lo = part * c->J / m * OR_SG;
+    *hi = (part + 1) * c->J / m * OR_SG;
+}
+
+int or_mxfp8_allreduce(or_ctx *c, const void *const *grads, int32_t dtype, float *out) {
+    const int n = c->n;
+    const int64_t d = c->d;
+    float *tmp = (float *)malloc((size_t)d * sizeof(float));
+    if (n == 1) {
+        for (int64_t i = 0; i < d; i++) tmp[i] = load_elem(grads[0], dtype, i);
+        or_mxfp8_roundtrip(tmp, d, out);
+        free(tmp);
+        return 0;
+    }
+    /* cur[w]: worker w's quantised partial on its current part (full-length
+       buffers indexed by original coordinate) */
+    float **cur = (float **)malloc((size_t)n * sizeof(float *));
+    float **nxt = (float **)malloc((size_t)n * sizeof(float *));
+    for (int w = 0; w < n; w++) {
+        cur[w] = (float *)calloc((size_t)d, sizeof(float));
+        nxt[w] = (float *)calloc((size_t)d, sizeof(float));
+    }
+    int64_t lo, hi;
+    if (c->topo == OR_RING) {
+        for (int w = 0; w < n; w++) {
+            mx_part(c, n, w, &lo, &hi);
+            for (int64_t i = lo; i < hi; i++) tmp[i] = load_elem(grads[w], dtype, i);
+            or_mxfp8_roundtrip(tmp + lo, hi - lo, cur[w] + lo);
+        }
+        for (int t = 1; t < n; t++) {
+            for (int w = 0; w < n; w++) {
+                const int src = (w - 1 + n) % n;
+                mx_part(c, n, ((int64_t)w - t % n + n) % n, &lo, &hi);
+                for (int64_t i = lo; i < hi; i++) tmp[i] = cur[src][i] + load_elem(grads[w], dtype, i);
+                or_mxfp8_roundtrip(tmp + lo, hi - lo, nxt[w] + lo);
+            }
+            float **sw = cur; cur = nxt; nxt = sw;
+        }
+        for (int w = 0; w < n; w++) {
+            mx_part(c, n, (w + 1) % n, &lo, &hi);
+            memcpy(out + lo, cur[w] + lo, (size_t)(hi - lo) * sizeof(float));
+        }
+    } else {
+        const int L = c->log2n;
+        /* level 1: each worker quantises the half it sends */
+        for (int w = 0; w < n; w++) {
+            mx_part(c, 2, ((int64_t)w >> (L - 1)) ^ 1, &lo, &hi);
+            for (int64_t i = lo; i < hi; i++) tmp[i] = load_elem(grads[w], dtype, i);
+            or_mxfp8_roundtrip(tmp + lo, hi - lo, nxt[w] + lo);   /* nxt = sent halves */
+        }
+        for (int s = 1; s <= L; s++) {
+            for (int w = 0; w < n; w++) {
+                const int partner = w ^ (n >> s);
+                mx_part(c, (int64_t)1 << s, (int64_t)w >> (L - s), &lo, &hi);
+                for (int64_t i = lo; i < hi; i++) {
+                    const float own = (s == 1) ? load_elem(grads[w], dtype, i) : cur[w][i];
+                    const float in = (s == 1) ? nxt[partner][i] : cur[partner][i];
+                    tmp[i] = in + own;
+                }
+                /* write into a scratch then swap after all workers of the level */
+                or_mxfp8_roundtrip(tmp + lo, hi - lo, (s == 1 ? cur[w] : nxt[w]) + lo);
+            }
+            if (s > 1) {
+                for (int w = 0; w < n; w++) {
+                    mx_part(c, (int64_t)1 << s, (int64_t)w >> (L - s), &lo, &hi);
+                    memcpy(cur[w] + lo, nxt[w] + lo, (size_t)(hi - lo) * sizeof(float));
+                }
+            }
+        }
+        for (int w = 0; w < n; w++) {
+            mx_part(c, n, w, &lo, &hi);
+            memcpy(out + lo, cur[w] + lo, (size_t)(hi - lo) * sizeof(float));
+        }
+    }
+    for (int w = 0; w < n; w++) { free(cur[w]); free(nxt[w]); }
+    free(cur); free(nxt); free(tmp);
+    return 0;
+}

@@ -121,6 +121,9 @@ void or_dithers(uint64_t seed, uint32_t round, int64_t j, int32_t mode,
 
 /* MXFP8 (OCP MX v1.0: block 32, E8M0 shared scale, E4M3 elements). */
 void or_mxfp8_roundtrip(const float *x, int64_t n, float *out);
+/* The schedule of the context with MXFP8 re-encoding at every hop, on parts of
+ * the original order; out = the decoded all-reduced sum. */
+int or_mxfp8_allreduce(or_ctx *c, const void *const *grads, int32_t dtype, float *out);
 
 #ifdef __cplusplus
 }

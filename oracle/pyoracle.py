@@ -59,6 +59,7 @@ def lib():
             "or_roundtrip_batch": (None, [vp, i64, i32, vp, f64, vp]),
             "or_dithers": (None, [u64, u32, i64, i32, i32, i32, i32, vp]),
             "or_mxfp8_roundtrip": (None, [vp, i64, vp]),
+            "or_mxfp8_allreduce": (C.c_int, [vp, vp, i32, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -247,6 +248,13 @@ class Oracle:
 
     def final_part(self, w):
         return int(lib().or_final_part(self.h, int(w)))
+
+    def mxfp8_allreduce(self, grads):
+        grads = [np.ascontiguousarray(g) for g in grads]
+        ptrs = (C.c_void_p * self.n)(*[g.ctypes.data for g in grads])
+        out = np.zeros(self.d, np.float32)
+        _check(lib().or_mxfp8_allreduce(self.h, ptrs, _dtype_code(grads[0]), _p(out)), "mxfp8_allreduce")
+        return out
 
     def allreduce(self, grads):
         grads = [np.ascontiguousarray(g) for g in grads]

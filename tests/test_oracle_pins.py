@@ -723,3 +723,28 @@ def test_mxfp8_reference_quantiser():
     assert np.all(np.abs(y - x)[sub] <= 2.0 ** -10 * X[sub] * (1 + 1e-6))
     # a block's max never moves by more than one E4M3 step
     assert np.all(np.abs(y) <= blk * (1 + 2.0 ** -3))
+
+
+def test_mxfp8_schedule_composition():
+    """The MXFP8 reference round is the plain composition of block
+    quantisations along the schedule: one worker = one quantisation; a 2-worker
+    ring quantises each half once alone and once as a two-worker sum."""
+    rng = np.random.default_rng(17)
+    J = 12
+    g = [(rng.standard_normal(256 * J) * np.repeat(10.0 ** rng.uniform(-4, 0, J), 256)).astype(np.float32)
+         for _ in range(2)]
+    o1 = po.Oracle(256 * J, 1)
+    assert np.array_equal(o1.mxfp8_allreduce(g[:1]), po.mxfp8_roundtrip(g[0]))
+    h = 256 * (J // 2)
+    o2 = po.Oracle(256 * J, 2, po.RING)
+    out = o2.mxfp8_allreduce(g)
+    # ring n = 2: worker 0 sends part 0, worker 1 reduces it; and the reverse for part 1
+    exp0 = po.mxfp8_roundtrip(po.mxfp8_roundtrip(g[0][:h]) + g[1][:h])
+    exp1 = po.mxfp8_roundtrip(po.mxfp8_roundtrip(g[1][h:]) + g[0][h:])
+    assert np.array_equal(out, np.concatenate([exp0, exp1]))
+    ob = po.Oracle(256 * J, 2, po.BUTTERFLY)
+    outb = ob.mxfp8_allreduce(g)
+    # butterfly n = 2: worker 0 keeps half 0 and receives worker 1's quantised half 0
+    exp0 = po.mxfp8_roundtrip(po.mxfp8_roundtrip(g[1][:h]) + g[0][:h])
+    exp1 = po.mxfp8_roundtrip(po.mxfp8_roundtrip(g[0][h:]) + g[1][h:])
+    assert np.array_equal(outb, np.concatenate([exp0, exp1]))
