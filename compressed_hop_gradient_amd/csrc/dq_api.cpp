@@ -258,6 +258,10 @@ dq_status dq_plan_create(int64_t n_coords, int32_t n_workers, int32_t topology, 
     while ((1 << L) < n_workers) L++;
     if (topology == DQ_BUTTERFLY && (1 << L) != n_workers) return DQ_EINVAL;
     if (!(avg_bits >= 2.0f)) return DQ_EBUDGET;
+    // codec kernels address a region with 32-bit offsets: the largest region
+    // (a part of the smallest m the schedule uses) must stay below 4 GB
+    const int64_t m_min = n_workers == 1 ? 1 : (topology == DQ_RING ? n_workers : 2);
+    if ((n_coords / kSG / m_min + 3) * (256 + 4 + 16) + 256 >= ((int64_t)1 << 32)) return DQ_EINVAL;
     dq_plan *p = new (std::nothrow) dq_plan();
     if (!p) return DQ_EINVAL;
     p->d = n_coords;

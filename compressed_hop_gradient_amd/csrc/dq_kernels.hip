@@ -40,13 +40,21 @@ __device__ __forceinline__ float dpp_mov(float x) {
                                                       0xF, 0xF, false));
 }
 
-// maximum over the 16 lanes of a DPP row (all lanes get the result)
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov_u(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+// maximum over the 16 lanes of a DPP row (all lanes get the result).  The
+// inputs are magnitudes (non-negative floats), whose order is their bit
+// patterns' integer order, so an integer max serves and folds into DPP.
 __device__ __forceinline__ float row_max16(float x) {
-    x = fmaxf(x, dpp_mov<0xB1>(x));   // quad_perm [1,0,3,2]
-    x = fmaxf(x, dpp_mov<0x4E>(x));   // quad_perm [2,3,0,1]
-    x = fmaxf(x, dpp_mov<0x141>(x));  // row_half_mirror
-    x = fmaxf(x, dpp_mov<0x140>(x));  // row_mirror
-    return x;
+    uint32_t u = __float_as_uint(x);
+    u = max(u, dpp_mov_u<0xB1>(u));   // quad_perm [1,0,3,2]
+    u = max(u, dpp_mov_u<0x4E>(u));   // quad_perm [2,3,0,1]
+    u = max(u, dpp_mov_u<0x141>(u));  // row_half_mirror
+    u = max(u, dpp_mov_u<0x140>(u));  // row_mirror
+    return __uint_as_float(u);
 }
 
 // Philox4x32 with 10 rounds (Salmon et al., SC'11): per round two 32x32->64
@@ -78,44 +86,50 @@ __device__ __forceinline__ void philox4x32_10(uint32_t &x0, uint32_t &x1, uint32
     }
 }
 
-// Scale unit of a super-group: fl(A/255), raised until 255 units cover A.
+// Scale unit of a super-group: fl(A/255), raised to the next float while
+// fl(255 s) < A.  One raise always suffices (the first product is within one
+// part in 2^24 of A, and one ulp of s adds 255 ulps to it); the second guard
+// keeps the definition's loop semantics without a loop.
 __device__ __forceinline__ float scale_unit(float A) {
     float s = A / 255.0f;
-    while (255.0f * s < A) s = __uint_as_float(__float_as_uint(s) + 1u);
+    if (255.0f * s < A) s = __uint_as_float(__float_as_uint(s) + 1u);
+    if (255.0f * s < A) s = __uint_as_float(__float_as_uint(s) + 1u);
     return s;
 }
 
 // Smallest c in [0, 255] with fl(c * s) >= a (exists because fl(255 s) >= A >= a).
+// For a normal s the estimate ceil(a * rcp(s)) (rcp within 1 ulp) is within one
+// of the answer, so one checked step down or up settles it; subnormal s (scale
+// units below 2^-126) take the general search.
 __device__ __forceinline__ int group_code(float a, float s) {
     if (s == 0.0f) return 0;
-    float est = a * __builtin_amdgcn_rcpf(s);
-    int c = (int)ceilf(fminf(est, 255.0f));
+    if (s < 1.1754943508222875e-38f) {
+        int c = 0;
+        while (c < 255 && (float)c * s < a) c++;
+        return c;
+    }
+    int c = (int)ceilf(fminf(a * __builtin_amdgcn_rcpf(s), 255.0f));
     c = min(max(c, 0), 255);
-    while (c > 0 && (float)(c - 1) * s >= a) c--;
-    while (c < 255 && (float)c * s < a) c++;
-    return c;
+    const bool down = c > 0 && (float)(c - 1) * s >= a;
+    const bool up = c < 255 && (float)c * s < a;
+    return down ? c - 1 : (up ? c + 1 : c);
 }
 
 // Interval search over NL = 16 or 256 levels: r = largest r <= NL-2 with
-// L[r] <= v.  The bucket of v (exponent and 7 mantissa bits of |v|, and the
-// sign) holds at most one level boundary, so its table entry is r or r - 1;
-// one compare with the next level settles it.  Returns r and the level /
-// weight of interval r.
-__device__ __forceinline__ int bucket_index(float v) {
+// L[r] <= v.  The bucket of v (sign, exponent and 7 mantissa bits) holds at
+// most one level boundary, so its table entry est is r or r - 1; one compare
+// with the next level settles it, and the pair (L[r], W[r]) is read at r.
+template <int NL>
+__device__ __forceinline__ uint32_t search_levels(float v, const uint8_t *est_tab, const float *cl,
+                                                  const Pair *lw, float &Lr, float &Wr) {
     const uint32_t b = __float_as_uint(v);
-    int k = (int)((b >> 16) & 0x7FFFu) - kKeyBase;
-    k = min(max(k, 0), kKeyMax);
-    return k + ((b >> 31) ? kKeys : 0);
-}
-
-__device__ __forceinline__ int search_levels(float v, const uint8_t *est_tab, const Row4 *rows,
-                                             float &Lr, float &Wr) {
-    const int est = est_tab[bucket_index(v)];
-    const Row4 row = rows[est];
-    const bool up = v >= row.l1;
-    Lr = up ? row.l1 : row.l0;
-    Wr = up ? row.w1 : row.w0;
-    return est + (up ? 1 : 0);
+    const int k = min(max((int)((b >> 16) & 0x7FFFu) - kKeyBase, 0), kKeyMax);
+    const uint32_t est = est_tab[((uint32_t)k << 1) | (b >> 31)];
+    const uint32_t r = est + (v >= cl[est + 1] ? 1u : 0u);
+    const Pair p = lw[r];
+    Lr = p.l;
+    Wr = p.w;
+    return r;
 }
 
 __device__ __forceinline__ int search_levels2(float v, float &Lr, float &Wr) {
@@ -162,8 +176,10 @@ struct SharedTables {
     float dec2[4];
     float dec4[16];
     float dec8[256];
-    Row4 r4[15];
-    Row4 r8[255];
+    float cl4[16];
+    float cl8[256];
+    Pair lw4[15];
+    Pair lw8[255];
     uint8_t b4[2 * kKeys];
     uint8_t b8[2 * kKeys];
 };
@@ -200,20 +216,36 @@ __device__ __forceinline__ void store_codes(uint8_t *p, const uint32_t (&w)[B / 
     }
 }
 
-// decode the group (lane g) of super-group t (part-local), class-local index idx
-template <int Q>
-__device__ __forceinline__ void decode_group(const uint8_t *region, int64_t offc, int64_t offs,
-                                             int64_t offg, int64_t t, int64_t idx, int g,
+// Region pointers of one part, split by class (uniform over a launch).  Offsets
+// added to them are 32-bit: the host keeps every region below 4 GB.
+struct RegionBase {
+    const uint8_t *codes[3];   // codes of class k
+    const uint8_t *s;          // fp32 scale units
+    const uint8_t *g;          // UINT8 group codes
+};
+
+__device__ __forceinline__ RegionBase region_base(const uint8_t *r, const PartInfo &P) {
+    RegionBase b;
+    for (int k = 0; k < 3; k++) b.codes[k] = r + P.offc[k];
+    b.s = r + P.offs;
+    b.g = r + P.offg;
+    return b;
+}
+
+// decode the group (lane g) of the super-group at part-local index t and
+// class-local index idx of class K (B = bits per code)
+template <int B, int K>
+__device__ __forceinline__ void decode_group(const RegionBase &R, uint32_t t, uint32_t idx, int g,
                                              const SharedTables &T, float (&x)[16]) {
-    uint32_t w[Q / 2];
-    load_codes<Q>(region + offc + idx * (32 * Q) + g * (2 * Q), w);
-    const float s = *reinterpret_cast<const float *>(region + offs + 4 * t);
-    const uint32_t c = region[offg + 16 * t + g];
+    uint32_t w[B / 2];
+    load_codes<B>(R.codes[K] + (idx * (32u * B) + (uint32_t)g * (2u * B)), w);
+    const float s = *reinterpret_cast<const float *>(R.s + 4u * t);
+    const uint32_t c = R.g[16u * t + (uint32_t)g];
     const float sigma = (float)c * s;
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-        const uint32_t code = (w[(i * Q) / 32] >> ((i * Q) % 32)) & ((1u << Q) - 1u);
-        x[i] = sigma * level_of<Q>(T, code);
+        const uint32_t code = (w[(i * B) / 32] >> ((i * B) % 32)) & ((1u << B) - 1u);
+        x[i] = sigma * level_of<B>(T, code);
     }
 }
 
@@ -223,139 +255,143 @@ __device__ __forceinline__ void decode_group(const uint8_t *region, int64_t offc
 
 // One super-group per 16-lane row, one group of 16 coordinates per lane.
 // Q = bits per code of the super-group's class, K = the class index.
-// Po = output part, Pi = input part (the same part or its parent).
+// Po = output part, Pi = input part (the same part or its parent); In / Own /
+// Out are their regions.  t is the part-local index in the output part.
 template <int Q, int MODE, int LOCAL>
-__device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po,
-                                         const PartInfo &Pi, int64_t t, int g,
+__device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po, const PartInfo &Pi,
+                                         const RegionBase &In, const RegionBase &Own,
+                                         const RegionBase &Out, uint32_t t, int g,
                                          const SharedTables &T) {
     constexpr int K = Q == 2 ? 0 : (Q == 4 ? 1 : 2);
-    const int64_t idx = t - Po.pre[K];            // index in the class, output part
-    const int64_t pos = Po.lo[K] + idx;           // stream position
-    const int64_t j = a.perm[pos];                // original super-group
-    const int64_t idx_in = pos - Pi.lo[K];        // index in the class, input part
-    const int64_t t_in = Pi.pre[K] + idx_in;
+    const uint32_t idx = t - (uint32_t)Po.pre[K];        // index in the class, output part
+    const uint32_t pos = (uint32_t)Po.lo[K] + idx;       // stream position
+    const uint32_t j = (uint32_t)a.perm[pos];            // original super-group
+    const uint32_t idx_in = pos - (uint32_t)Pi.lo[K];    // index in the class, input part
+    const uint32_t t_in = (uint32_t)Pi.pre[K] + idx_in;
+    const float mu = a.mu_stream[pos];
     float y[16];
 
-    if constexpr (MODE != kCompress)
-        decode_group<Q>(a.region_in, Pi.offc[K], Pi.offs, Pi.offg, t_in, idx_in, g, T, y);
+    if constexpr (MODE != kCompress) decode_group<Q, K>(In, t_in, idx_in, g, T, y);
 
-    {
-        const float mu = a.mu_stream[pos];
-        if constexpr (LOCAL == kLocalBF16) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(
-                static_cast<const uint16_t *>(a.grad) + j * kSG + g * kGroup);
-            const uint4 h0 = src[0], h1 = src[1];
-            const uint32_t hw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+    if constexpr (LOCAL == kLocalBF16) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(
+            static_cast<const uint16_t *>(a.grad) + ((uint64_t)j * kSG + (uint32_t)g * kGroup));
+        const uint4 h0 = src[0], h1 = src[1];
+        const uint32_t hw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const float e0 = bf16_lo(hw[i]) - mu, e1 = bf16_hi(hw[i]) - mu;
-                if constexpr (MODE == kHop) {
-                    y[2 * i] = y[2 * i] + e0;
-                    y[2 * i + 1] = y[2 * i + 1] + e1;
-                } else {
-                    y[2 * i] = e0;
-                    y[2 * i + 1] = e1;
-                }
-            }
-        } else if constexpr (LOCAL == kLocalF32) {
-            const float4 *src = reinterpret_cast<const float4 *>(
-                static_cast<const float *>(a.grad) + j * kSG + g * kGroup);
-#pragma unroll
-            for (int v = 0; v < 4; v++) {
-                const float4 f = src[v];
-                const float e[4] = {f.x - mu, f.y - mu, f.z - mu, f.w - mu};
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    if constexpr (MODE == kHop) y[4 * v + i] = y[4 * v + i] + e[i];
-                    else y[4 * v + i] = e[i];
-                }
-            }
-        } else if constexpr (LOCAL == kLocalPacked) {
-            float own[16];
-            decode_group<Q>(a.region_own, Pi.offc[K], Pi.offs, Pi.offg, t_in, idx_in, g, T, own);
-#pragma unroll
-            for (int i = 0; i < 16; i++) y[i] = y[i] + own[i];
-        }
-
-        // ---- encode ----
-        float amax = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(y[i]));
-        const float A = row_max16(amax);
-        const float s = scale_unit(A);
-        const int c = group_code(amax, s);
-        const float sigma = (float)c * s;
-        const float inv = sigma == 0.0f ? 0.0f : 1.0f / sigma;
-
-        typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
-        const ushort2_t stag = {(unsigned short)a.stagger, (unsigned short)a.stagger};
-        uint32_t w[Q / 2];
-#pragma unroll
-        for (int i = 0; i < Q / 2; i++) w[i] = 0u;
-#pragma unroll
-        for (int h = 0; h < 2; h++) {
-            // 8 dithers of coordinates 8h..8h+7 of this group from one Philox call
-            uint32_t x0 = 2u * g + h, x1 = (uint32_t)j, x2 = a.round, x3 = a.tag;
-            philox4x32_10(x0, x1, x2, x3, a.key0, a.key1);
-            // add the worker's stagger to both 16-bit halves (mod 65536)
-            uint32_t d[4] = {x0, x1, x2, x3};
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                ushort2_t hv = __builtin_bit_cast(ushort2_t, d[q]);
-                hv = hv + stag;
-                d[q] = __builtin_bit_cast(uint32_t, hv);
-            }
-#pragma unroll
-            for (int ii = 0; ii < 8; ii++) {
-                const int i = 8 * h + ii;
-                const float v = fminf(fmaxf(y[i] * inv, -1.0f), 1.0f);
-                float Lr, Wr;
-                int r;
-                if constexpr (Q == 2) r = search_levels2(v, Lr, Wr);
-                else if constexpr (Q == 4) r = search_levels(v, T.b4, T.r4, Lr, Wr);
-                else r = search_levels(v, T.b8, T.r8, Lr, Wr);
-                const float P = (v - Lr) * Wr;
-                const uint32_t dd = (ii & 1) ? (d[ii >> 1] >> 16) : (d[ii >> 1] & 0xFFFFu);
-                const uint32_t code = (uint32_t)r + (((float)dd + 0.5f) < P ? 1u : 0u);
-                w[(i * Q) / 32] |= code << ((i * Q) % 32);
+        for (int i = 0; i < 8; i++) {
+            const float e0 = bf16_lo(hw[i]) - mu, e1 = bf16_hi(hw[i]) - mu;
+            if constexpr (MODE == kHop) {
+                y[2 * i] = y[2 * i] + e0;
+                y[2 * i + 1] = y[2 * i + 1] + e1;
+            } else {
+                y[2 * i] = e0;
+                y[2 * i + 1] = e1;
             }
         }
-
-        store_codes<Q>(a.out + Po.offc[K] + idx * (32 * Q) + g * (2 * Q), w);
-        a.out[Po.offg + 16 * t + g] = (uint8_t)c;
-        if (g == 0) *reinterpret_cast<float *>(a.out + Po.offs + 4 * t) = s;
+    } else if constexpr (LOCAL == kLocalF32) {
+        const float4 *src = reinterpret_cast<const float4 *>(
+            static_cast<const float *>(a.grad) + ((uint64_t)j * kSG + (uint32_t)g * kGroup));
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const float4 f = src[v];
+            const float e[4] = {f.x - mu, f.y - mu, f.z - mu, f.w - mu};
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                if constexpr (MODE == kHop) y[4 * v + i] = y[4 * v + i] + e[i];
+                else y[4 * v + i] = e[i];
+            }
+        }
+    } else if constexpr (LOCAL == kLocalPacked) {
+        float own[16];
+        decode_group<Q, K>(Own, t_in, idx_in, g, T, own);
+#pragma unroll
+        for (int i = 0; i < 16; i++) y[i] = y[i] + own[i];
     }
+
+    // ---- encode ----
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(y[i]));
+    const float A = row_max16(amax);
+    const float s = scale_unit(A);
+    const int c = group_code(amax, s);
+    const float sigma = (float)c * s;
+    const float inv = sigma == 0.0f ? 0.0f : 1.0f / sigma;
+
+    typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+    const ushort2_t stag = {(unsigned short)a.stagger, (unsigned short)a.stagger};
+    uint32_t w[Q / 2];
+#pragma unroll
+    for (int i = 0; i < Q / 2; i++) w[i] = 0u;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        // 8 dithers of coordinates 8h..8h+7 of this group from one Philox call
+        uint32_t x0 = 2u * g + h, x1 = j, x2 = a.round, x3 = a.tag;
+        philox4x32_10(x0, x1, x2, x3, a.key0, a.key1);
+        // add the worker's stagger to both 16-bit halves (mod 65536)
+        uint32_t d[4] = {x0, x1, x2, x3};
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            ushort2_t hv = __builtin_bit_cast(ushort2_t, d[q]);
+            hv = hv + stag;
+            d[q] = __builtin_bit_cast(uint32_t, hv);
+        }
+#pragma unroll
+        for (int ii = 0; ii < 8; ii++) {
+            const int i = 8 * h + ii;
+            const float v = fminf(fmaxf(y[i] * inv, -1.0f), 1.0f);
+            float Lr, Wr;
+            uint32_t r;
+            if constexpr (Q == 2) r = (uint32_t)search_levels2(v, Lr, Wr);
+            else if constexpr (Q == 4) r = search_levels<16>(v, T.b4, T.cl4, T.lw4, Lr, Wr);
+            else r = search_levels<256>(v, T.b8, T.cl8, T.lw8, Lr, Wr);
+            const float P = (v - Lr) * Wr;
+            const uint32_t dd = (ii & 1) ? (d[ii >> 1] >> 16) : (d[ii >> 1] & 0xFFFFu);
+            const uint32_t code = r + (((float)dd + 0.5f) < P ? 1u : 0u);
+            w[(i * Q) / 32] |= code << ((i * Q) % 32);
+        }
+    }
+
+    uint8_t *out_codes = const_cast<uint8_t *>(Out.codes[K]);
+    store_codes<Q>(out_codes + (idx * (32u * Q) + (uint32_t)g * (2u * Q)), w);
+    const_cast<uint8_t *>(Out.g)[16u * t + (uint32_t)g] = (uint8_t)c;
+    if (g == 0) *reinterpret_cast<float *>(const_cast<uint8_t *>(Out.s) + 4u * t) = s;
 }
 
 template <int MODE, int LOCAL>
 __global__ __launch_bounds__(256) void k_codec(CodecArgs a) {
     __shared__ __align__(16) SharedTables T;
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) T.dec8[i] = g_tables.L8[i];
-    {
-        for (int i = threadIdx.x; i < 255; i += blockDim.x) T.r8[i] = g_tables.R8[i];
-        for (int i = threadIdx.x; i < 2 * kKeys; i += blockDim.x) {
-            T.b8[i] = g_buckets8.est[i];
-            T.b4[i] = g_buckets4.est[i];
-        }
-        if (threadIdx.x < 15) T.r4[threadIdx.x] = g_tables.R4[threadIdx.x];
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) {
+        T.dec8[i] = g_tables.L8[i];
+        T.cl8[i] = g_tables.CL8[i];
     }
-    if (threadIdx.x < 16) T.dec4[threadIdx.x] = g_tables.L4[threadIdx.x];
+    for (int i = threadIdx.x; i < 255; i += blockDim.x) T.lw8[i] = g_tables.LW8[i];
+    for (int i = threadIdx.x; i < 2 * kKeys; i += blockDim.x) {
+        T.b8[i] = g_buckets8.est[i];
+        T.b4[i] = g_buckets4.est[i];
+    }
+    if (threadIdx.x < 16) {
+        T.dec4[threadIdx.x] = g_tables.L4[threadIdx.x];
+        T.cl4[threadIdx.x] = g_tables.CL4[threadIdx.x];
+    }
+    if (threadIdx.x < 15) T.lw4[threadIdx.x] = g_tables.LW4[threadIdx.x];
     if (threadIdx.x < 4) T.dec2[threadIdx.x] = g_tables.L2[threadIdx.x];
-
     __syncthreads();
     // part layouts: uniform loads from the per-round part table
     const PartInfo Po = *a.part_out, Pi = *a.part_in;
+    const RegionBase In = region_base(a.region_in, Pi), Own = region_base(a.region_own, Pi);
+    const RegionBase Out = region_base(a.out, Po);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane & 15, row = lane >> 4;
-    const int64_t N = Po.N;
-    for (int64_t base = (int64_t)blockIdx.x * kSGPerBlock; base < N;
-         base += (int64_t)gridDim.x * kSGPerBlock) {
-        const int64_t t = base + wave * 4 + row;
+    const uint32_t N = (uint32_t)Po.N, pre1 = (uint32_t)Po.pre[1], pre2 = (uint32_t)Po.pre[2];
+    for (uint32_t base = blockIdx.x * kSGPerBlock; base < N; base += gridDim.x * kSGPerBlock) {
+        const uint32_t t = base + wave * 4 + row;
         if (t >= N) continue;
-        if (t < Po.pre[1]) codec_sg<2, MODE, LOCAL>(a, Po, Pi, t, g, T);
-        else if (t < Po.pre[2]) codec_sg<4, MODE, LOCAL>(a, Po, Pi, t, g, T);
-        else codec_sg<8, MODE, LOCAL>(a, Po, Pi, t, g, T);
+        if (t < pre1) codec_sg<2, MODE, LOCAL>(a, Po, Pi, In, Own, Out, t, g, T);
+        else if (t < pre2) codec_sg<4, MODE, LOCAL>(a, Po, Pi, In, Own, Out, t, g, T);
+        else codec_sg<8, MODE, LOCAL>(a, Po, Pi, In, Own, Out, t, g, T);
     }
 }
 

@@ -9,20 +9,20 @@
 // (double, rounded once) turns the position inside an interval into a 16-bit
 // dither threshold with a single multiply.
 //
-// The search rows serve the interval search of the encoder: row r holds
-// (L[r], L[r+1], W[r], W[r+1]); in the last row (r = 2^q - 2) the "next level"
-// is +inf so the search never steps past the last interval.
+// The encoder's interval search uses CL[r] = L[r] for r <= 2^q - 2 and
+// CL[2^q - 1] = +inf (so the search never steps past the last interval), and
+// the pairs LW[r] = (L[r], W[r]) of the interval it lands in.
 #pragma once
 
 namespace dq {
 
-struct Row4 { float l0, l1, w0, w1; };
+struct Pair { float l, w; };
 
 struct LevelTables {
     float L2[4], L4[16], L8[256];
     float W2[3];
-    Row4 R4[15];
-    Row4 R8[255];
+    float CL4[16], CL8[256];
+    Pair LW4[15], LW8[255];
 };
 
 constexpr double level_value(int r, int Q) {
@@ -38,9 +38,8 @@ constexpr float weight_f(int r, int Q) {
     return float(65536.0 / (double(level_f(r + 1, Q)) - double(level_f(r, Q))));
 }
 
-constexpr Row4 search_row(int r, int Q) {
-    return Row4{level_f(r, Q), r + 1 <= Q - 2 ? level_f(r + 1, Q) : __builtin_huge_valf(),
-                weight_f(r, Q), r + 1 <= Q - 2 ? weight_f(r + 1, Q) : 0.0f};
+constexpr float compare_level(int r, int Q) {
+    return r <= Q - 2 ? level_f(r, Q) : __builtin_huge_valf();
 }
 
 constexpr LevelTables make_tables() {
@@ -49,8 +48,10 @@ constexpr LevelTables make_tables() {
     for (int r = 0; r < 16; r++) t.L4[r] = level_f(r, 16);
     for (int r = 0; r < 256; r++) t.L8[r] = level_f(r, 256);
     for (int r = 0; r < 3; r++) t.W2[r] = weight_f(r, 4);
-    for (int r = 0; r < 15; r++) t.R4[r] = search_row(r, 16);
-    for (int r = 0; r < 255; r++) t.R8[r] = search_row(r, 256);
+    for (int r = 0; r < 16; r++) t.CL4[r] = compare_level(r, 16);
+    for (int r = 0; r < 256; r++) t.CL8[r] = compare_level(r, 256);
+    for (int r = 0; r < 15; r++) t.LW4[r] = Pair{level_f(r, 16), weight_f(r, 16)};
+    for (int r = 0; r < 255; r++) t.LW8[r] = Pair{level_f(r, 256), weight_f(r, 256)};
     return t;
 }
 
@@ -63,7 +64,7 @@ constexpr LevelTables kLevelTables = make_tables();
 // |v| = 1.  Each bucket is at most 2^-7 wide relative to its start, narrower
 // than the closest pair of levels, so it contains at most one level boundary:
 // the table gives r or r - 1 and one compare with the next level decides.
-// Entries [0, kKeys) serve v >= 0, entries [kKeys, 2 kKeys) serve v < 0.
+// Entry 2k serves v >= 0 in bucket k, entry 2k + 1 serves v < 0 in bucket k.
 // ---------------------------------------------------------------------------
 
 constexpr int kKeyBase = 0x3B00;              // fp32 bits of 2^-9, >> 16
@@ -91,13 +92,13 @@ constexpr BucketTable<NL> make_buckets() {
     for (int k = 0; k < kKeys; k++) {
         const float lo = key_lo(k);
         while (r + 1 <= NL - 2 && level_f(r + 1, NL) <= lo) r++;
-        t.est[k] = (unsigned char)r;
+        t.est[2 * k] = (unsigned char)r;
     }
     r = 0;
     for (int k = kKeys - 1; k >= 0; k--) {
         const float nh = -key_hi(k);
         while (r + 1 <= NL - 2 && level_f(r + 1, NL) <= nh) r++;
-        t.est[kKeys + k] = (unsigned char)r;
+        t.est[2 * k + 1] = (unsigned char)r;
     }
     return t;
 }
