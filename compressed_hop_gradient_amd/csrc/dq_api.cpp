@@ -5,6 +5,7 @@
 #include "dq.h"
 
 #include <cmath>
+#include <cstddef>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -384,11 +385,11 @@ dq_status dq_allocate(dq_plan *p, void *stream) {
     a.nblk = p->nblk;
     Launch L;
     hipError_t e = timed_begin(p, DQ_K_ALLOCATE, 0, 0, s, L);
-    // counts[] and class_counts[] start at zero (a fill kernel, graph-safe)
+    // histograms, class counts, prefix and flag start at zero (a fill kernel,
+    // graph-safe); nonfinite is kept (it belongs to the stats of this round)
     const int64_t nzero = (int64_t)(offsetof(Ctrl, rho_bits) / 4);
     if (e == hipSuccess) e = launch_zero(reinterpret_cast<uint32_t *>(a.ctrl), nzero, s);
-    for (int step = 0; step < kBisectSteps && e == hipSuccess; step++)
-        e = launch_alloc_step(a, step, s);
+    for (int pass = 0; pass < kRadixPasses && e == hipSuccess; pass++) e = launch_alloc_pass(a, pass, s);
     if (e == hipSuccess) e = launch_alloc_final(a, s);
     if (e == hipSuccess) e = timed_end(p, L, s);
     if (e != hipSuccess) return DQ_EHIP;

@@ -12,15 +12,20 @@ constexpr int kGroup = 16;        // coordinates per group (one lane owns one gr
 constexpr int kGroupsPerSG = 16;
 constexpr int kSGPerBlock = 16;   // codec kernels: 4 waves x 4 super-groups
 constexpr int kReorderSGPerBlock = 1024;  // allocation/reorder: 256 threads x 4
-constexpr int kBisectSteps = 32;  // step 0 tests rho = 0, steps 1..31 bisect
+// The scalar rho is found by an exact radix search on its fp32 bit pattern:
+// pass p fixes the bits above kRadixShift[p] by testing up to 256 candidates.
+constexpr int kRadixPasses = 4;
+constexpr int kRadixCand = 256;
 
 // control block at the head of the workspace's control area
 struct Ctrl {
-    unsigned long long counts[kBisectSteps];  // sum of widths at each bisection probe
+    unsigned int hist4[kRadixCand + 1];       // per-pass histograms (see k_alloc_count)
+    unsigned int hist8[kRadixCand + 1];
     unsigned long long class_counts[3];       // super-groups at 2, 4, 8 bits
+    uint32_t prefix;                          // bits of rho fixed so far
+    uint32_t done;                            // 1 once rho is known
     uint32_t rho_bits;
     int32_t nonfinite;
-    int32_t pad[2];
 };
 
 enum Mode { kCompress = 0, kHop = 1, kFinalize = 2 };
@@ -105,7 +110,7 @@ struct Mxfp8Args {
 // launchers (dq_kernels.hip); each returns the hipError_t of its launch
 hipError_t launch_zero(uint32_t *p, int64_t n, hipStream_t s);
 hipError_t launch_stats(const StatsArgs &a, int f32, hipStream_t s);
-hipError_t launch_alloc_step(const AllocArgs &a, int step, hipStream_t s);
+hipError_t launch_alloc_pass(const AllocArgs &a, int pass, hipStream_t s);
 hipError_t launch_alloc_final(const AllocArgs &a, hipStream_t s);
 hipError_t launch_reorder(const ReorderArgs &a, hipStream_t s);
 hipError_t launch_codec(const CodecArgs &a, int mode, int local, int64_t max_sg, hipStream_t s);

@@ -340,7 +340,14 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po,
 #pragma unroll
         for (int ii = 0; ii < 8; ii++) {
             const int i = 8 * h + ii;
-            const float v = fminf(fmaxf(y[i] * inv, -1.0f), 1.0f);
+            // The definition clamps v to [-1, 1].  Here |y| <= sigma, so v
+            // exceeds 1 in magnitude by at most 2 ulps, and there every step
+            // below gives the clamped value's code: the bucket key and the
+            // capped interval (r = 2^q - 2 above +1, r = 0 below -1) are the
+            // same, P(+1) >= 65535.99 > any d + 0.5 so rounding up stays
+            // certain, and P < 0 below -1 keeps rounding down certain.  The
+            // clamp is therefore left out.
+            const float v = y[i] * inv;
             float Lr, Wr;
             uint32_t r;
             if constexpr (Q == 2) r = (uint32_t)search_levels2(v, Lr, Wr);
@@ -503,51 +510,82 @@ hipError_t launch_part_table(const unsigned long long *class_counts, int32_t n, 
 // statistics
 // ---------------------------------------------------------------------------
 
+// Tree step P_k <- P_k + P_{k+delta} for the lanes k < delta that matter; the
+// other lanes compute values nobody reads.  delta = 16 crosses DPP rows: a
+// ds_swizzle (xor 16 inside each 32-lane half); delta = 8, 4, 2, 1 are DPP row
+// shifts (lane i reads lane i + delta).
+template <int CTRL>
+__device__ __forceinline__ float dpp_shl(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float tree32(float x) {
+    x = x + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));  // xor 16
+    x = x + dpp_shl<0x108>(x);   // row_shl:8
+    x = x + dpp_shl<0x104>(x);   // row_shl:4
+    x = x + dpp_shl<0x102>(x);   // row_shl:2
+    x = x + dpp_shl<0x101>(x);   // row_shl:1
+    return x;                    // valid in lane 0 of each 32-lane half
+}
+
+// Each wave handles kStatsPairs pairs of super-groups per iteration (32 lanes,
+// 8 values each, per super-group) so that several 128-bit loads per lane are
+// in flight before the reductions.
+constexpr int kStatsPairs = 4;
+
 template <int F32>
 __global__ __launch_bounds__(256) void k_stats(StatsArgs a) {
     const int half = (threadIdx.x >> 5) & 1, wave = threadIdx.x >> 6, l = threadIdx.x & 31;
-    for (int64_t base = (int64_t)blockIdx.x * 8; base < a.J; base += (int64_t)gridDim.x * 8) {
-        const int64_t j = base + wave * 2 + half;
-        const bool live = j < a.J;
-        float e[8];
-        if (live) {
-            if (F32) {
-                const float4 *src = reinterpret_cast<const float4 *>(
-                    static_cast<const float *>(a.grad) + j * kSG + l * 8);
-                const float4 f0 = src[0], f1 = src[1];
-                e[0] = f0.x; e[1] = f0.y; e[2] = f0.z; e[3] = f0.w;
-                e[4] = f1.x; e[5] = f1.y; e[6] = f1.z; e[7] = f1.w;
+    constexpr int per_block = 4 * 2 * kStatsPairs;
+    for (int64_t base = (int64_t)blockIdx.x * per_block; base < a.J;
+         base += (int64_t)gridDim.x * per_block) {
+        float e[kStatsPairs][8];
+        bool live[kStatsPairs];
+#pragma unroll
+        for (int u = 0; u < kStatsPairs; u++) {
+            const int64_t j = base + (wave * kStatsPairs + u) * 2 + half;
+            live[u] = j < a.J;
+            if (live[u]) {
+                if (F32) {
+                    const float4 *src = reinterpret_cast<const float4 *>(
+                        static_cast<const float *>(a.grad) + j * kSG + l * 8);
+                    const float4 f0 = src[0], f1 = src[1];
+                    e[u][0] = f0.x; e[u][1] = f0.y; e[u][2] = f0.z; e[u][3] = f0.w;
+                    e[u][4] = f1.x; e[u][5] = f1.y; e[u][6] = f1.z; e[u][7] = f1.w;
+                } else {
+                    const uint4 h = *reinterpret_cast<const uint4 *>(
+                        static_cast<const uint16_t *>(a.grad) + j * kSG + l * 8);
+                    e[u][0] = bf16_lo(h.x); e[u][1] = bf16_hi(h.x); e[u][2] = bf16_lo(h.y); e[u][3] = bf16_hi(h.y);
+                    e[u][4] = bf16_lo(h.z); e[u][5] = bf16_hi(h.z); e[u][6] = bf16_lo(h.w); e[u][7] = bf16_hi(h.w);
+                }
             } else {
-                const uint4 h = *reinterpret_cast<const uint4 *>(
-                    static_cast<const uint16_t *>(a.grad) + j * kSG + l * 8);
-                e[0] = bf16_lo(h.x); e[1] = bf16_hi(h.x); e[2] = bf16_lo(h.y); e[3] = bf16_hi(h.y);
-                e[4] = bf16_lo(h.z); e[5] = bf16_hi(h.z); e[6] = bf16_lo(h.w); e[7] = bf16_hi(h.w);
+#pragma unroll
+                for (int i = 0; i < 8; i++) e[u][i] = 0.0f;
             }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; i++) e[i] = 0.0f;
-        }
-        float s = e[0], q = e[0] * e[0];
-#pragma unroll
-        for (int i = 1; i < 8; i++) {
-            s = s + e[i];
-            const float sq = e[i] * e[i];
-            q = q + sq;
         }
 #pragma unroll
-        for (int delta = 16; delta >= 1; delta >>= 1) {
-            s = s + __shfl_xor(s, delta, 32);
-            q = q + __shfl_xor(q, delta, 32);
-        }
-        if (live && l == 0) {
-            float S = s, F = q;
-            if (!a.first) {
-                S = a.sum[j] + s;
-                F = a.sumsq[j] + q;
+        for (int u = 0; u < kStatsPairs; u++) {
+            // 8 sequential adds per lane, then the tree over the 32 lanes
+            float s = e[u][0], q = e[u][0] * e[u][0];
+#pragma unroll
+            for (int i = 1; i < 8; i++) {
+                s = s + e[u][i];
+                const float sq = e[u][i] * e[u][i];
+                q = q + sq;
             }
-            a.sum[j] = S;
-            a.sumsq[j] = F;
-            if (!(__builtin_isfinite(S) && __builtin_isfinite(F))) atomicOr(a.nonfinite, 1);
+            s = tree32(s);
+            q = tree32(q);
+            const int64_t j = base + (wave * kStatsPairs + u) * 2 + half;
+            if (live[u] && l == 0) {
+                float S = s, F = q;
+                if (!a.first) {
+                    S = a.sum[j] + s;
+                    F = a.sumsq[j] + q;
+                }
+                a.sum[j] = S;
+                a.sumsq[j] = F;
+                if (!(__builtin_isfinite(S) && __builtin_isfinite(F))) atomicOr(a.nonfinite, 1);
+            }
         }
     }
 }
@@ -567,53 +605,114 @@ __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v
     return t;
 }
 
-// Replays the probes done so far; returns false once the search has converged.
-__device__ __forceinline__ bool bisect_state(const Ctrl *c, long long budget, int upto,
-                                             uint32_t &lo, uint32_t &hi) {
-    lo = 0u;
-    hi = 0x7F800000u;
-    for (int k = 1; k < upto; k++) {
-        if (hi - lo <= 1u) return false;
-        const uint32_t mid = lo + (hi - lo) / 2u;
-        if ((long long)c->counts[k] <= budget) hi = mid;
-        else lo = mid;
+// Radix search for rho: the smallest x in [0, 0x7F800000] (fp32 bit patterns
+// of rho >= 0, up to +inf) with  sum_j q_j(x) <= budget,  a non-increasing
+// count.  Pass p tests the candidates x_c = prefix + (c << shift_p); the first
+// passing candidate c* leaves prefix + ((c* - 1) << shift_p) as the largest
+// known failing value, and the last pass (shift 0) returns x_{c*} itself.
+// Same result as any exact search of the monotone predicate.
+__device__ __forceinline__ int radix_shift(int pass) { return pass == 0 ? 23 : (pass == 1 ? 15 : (pass == 2 ? 7 : 0)); }
+__device__ __forceinline__ int radix_ncand(int pass) { return pass == 3 ? 128 : 256; }
+
+// number of entries of the non-decreasing t[0..n) that are <= F
+__device__ __forceinline__ uint32_t count_le(const float *t, int n, float F) {
+    uint32_t lo = 0, len = (uint32_t)n;
+    while (len > 0) {
+        const uint32_t half = len >> 1;
+        if (t[lo + half] <= F) {
+            lo += half + 1;
+            len -= half + 1;
+        } else {
+            len = half;
+        }
     }
-    return hi - lo > 1u;
+    return lo;
 }
 
-__global__ __launch_bounds__(256) void k_alloc_step(AllocArgs a, int step) {
+// For every F_j: i4 = #{c : fl(544 x_c) <= F_j}, i8 = #{c : fl(16384 x_c) <= F_j};
+// histograms of i4 and i8 give, by suffix sums, how many super-groups reach
+// 4 and 8 bits at each candidate.
+__global__ __launch_bounds__(256) void k_alloc_count(AllocArgs a, int pass) {
     Ctrl *c = a.ctrl;
-    uint32_t probe = 0u;
-    if (step > 0) {
-        if ((long long)c->counts[0] <= a.budget) return;
-        uint32_t lo, hi;
-        if (!bisect_state(c, a.budget, step, lo, hi)) return;
-        probe = lo + (hi - lo) / 2u;
+    if (c->done) return;
+    __shared__ float t4[kRadixCand], t8[kRadixCand];
+    __shared__ unsigned int h4[kRadixCand + 1], h8[kRadixCand + 1];
+    const int n = radix_ncand(pass), shift = radix_shift(pass);
+    const uint32_t prefix = c->prefix;
+    for (int i = threadIdx.x; i < kRadixCand + 1; i += blockDim.x) {
+        h4[i] = 0u;
+        h8[i] = 0u;
     }
-    const float rho = __uint_as_float(probe);
-    const float t4 = 544.0f * rho, t8 = 16384.0f * rho;
-    unsigned long long local = 0;
+    if (threadIdx.x < n) {
+        const float rho = __uint_as_float(prefix + ((uint32_t)threadIdx.x << shift));
+        t4[threadIdx.x] = 544.0f * rho;
+        t8[threadIdx.x] = 16384.0f * rho;
+    }
+    __syncthreads();
     for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < a.J;
          j += (int64_t)gridDim.x * blockDim.x) {
         const float F = a.sumsq[j];
-        local += F >= t8 ? 8u : (F >= t4 ? 4u : 2u);
+        atomicAdd(&h4[count_le(t4, n, F)], 1u);
+        atomicAdd(&h8[count_le(t8, n, F)], 1u);
     }
-    const unsigned long long tot = block_sum_u64(local);
-    if (threadIdx.x == 0) atomicAdd(&c->counts[step], tot);
+    __syncthreads();
+    for (int i = threadIdx.x; i < n + 1; i += blockDim.x) {
+        if (h4[i]) atomicAdd(&c->hist4[i], h4[i]);
+        if (h8[i]) atomicAdd(&c->hist8[i], h8[i]);
+    }
 }
 
-__device__ __forceinline__ uint32_t final_rho_bits(const Ctrl *c, long long budget) {
-    if ((long long)c->counts[0] <= budget) return 0u;
-    uint32_t lo, hi;
-    bisect_state(c, budget, kBisectSteps, lo, hi);
-    return hi;
+// One block of 256: total bits at each candidate from suffix sums of the
+// histograms, first passing candidate, next prefix (or rho); then clears the
+// histograms for the next pass.
+__global__ __launch_bounds__(256) void k_alloc_decide(AllocArgs a, int pass) {
+    Ctrl *c = a.ctrl;
+    if (c->done) return;
+    __shared__ unsigned long long s4[kRadixCand], s8[kRadixCand];
+    __shared__ int first;
+    const int n = radix_ncand(pass), shift = radix_shift(pass);
+    const int t = threadIdx.x;
+    // s[t] starts as hist[t + 1]; after the scan s[t] = #{j : i_j > t}
+    s4[t] = t < n ? c->hist4[t + 1] : 0ull;
+    s8[t] = t < n ? c->hist8[t + 1] : 0ull;
+    if (t == 0) first = n;
+    __syncthreads();
+    for (int d = 1; d < kRadixCand; d <<= 1) {
+        const unsigned long long v4 = t + d < kRadixCand ? s4[t + d] : 0ull;
+        const unsigned long long v8 = t + d < kRadixCand ? s8[t + d] : 0ull;
+        __syncthreads();
+        s4[t] += v4;
+        s8[t] += v8;
+        __syncthreads();
+    }
+    if (t < n) {
+        const long long total = 2 * (long long)a.J + 2 * (long long)s4[t] + 4 * (long long)s8[t];
+        if (total <= a.budget) atomicMin(&first, t);
+    }
+    __syncthreads();
+    if (t == 0) {
+        const int cs = first;
+        const uint32_t prefix = c->prefix;
+        if (cs == 0) {              // only at pass 0 (later passes start at a failing value): rho = 0
+            c->rho_bits = prefix;
+            c->done = 1u;
+        } else if (pass == kRadixPasses - 1) {
+            c->rho_bits = prefix + ((uint32_t)cs << shift);
+            c->done = 1u;
+        } else {
+            c->prefix = prefix + ((uint32_t)(cs - 1) << shift);
+        }
+    }
+    for (int i = t; i < kRadixCand + 1; i += blockDim.x) {
+        c->hist4[i] = 0u;
+        c->hist8[i] = 0u;
+    }
 }
 
 // widths, per-block class counts for the reorder, global class counts
 __global__ __launch_bounds__(256) void k_alloc_final(AllocArgs a) {
     Ctrl *c = a.ctrl;
-    const uint32_t rb = final_rho_bits(c, a.budget);
-    if (blockIdx.x == 0 && threadIdx.x == 0) c->rho_bits = rb;
+    const uint32_t rb = c->rho_bits;
     const float rho = __uint_as_float(rb);
     const float t4 = 544.0f * rho, t8 = 16384.0f * rho;
     uint32_t cnt[3] = {0u, 0u, 0u};
@@ -850,14 +949,17 @@ hipError_t launch_zero(uint32_t *p, int64_t n, hipStream_t s) {
 }
 
 hipError_t launch_stats(const StatsArgs &a, int f32, hipStream_t s) {
-    const dim3 grid(grid_for(a.J, 8, kStreamGrid));
+    const dim3 grid(grid_for(a.J, 4 * 2 * kStatsPairs, kStreamGrid));
     if (f32) hipLaunchKernelGGL(k_stats<1>, grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL(k_stats<0>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_alloc_step(const AllocArgs &a, int step, hipStream_t s) {
-    hipLaunchKernelGGL(k_alloc_step, dim3(grid_for(a.J, 256, kStreamGrid)), dim3(256), 0, s, a, step);
+hipError_t launch_alloc_pass(const AllocArgs &a, int pass, hipStream_t s) {
+    hipLaunchKernelGGL(k_alloc_count, dim3(grid_for(a.J, 256, 1024)), dim3(256), 0, s, a, pass);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_alloc_decide, dim3(1), dim3(256), 0, s, a, pass);
     return hipGetLastError();
 }
 
