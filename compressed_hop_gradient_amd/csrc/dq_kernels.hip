@@ -123,8 +123,8 @@ template <int NL>
 __device__ __forceinline__ uint32_t search_levels(float v, const uint8_t *est_tab, const float *cl,
                                                   const Pair *lw, float &Lr, float &Wr) {
     const uint32_t b = __float_as_uint(v);
-    const int k = min(max((int)((b >> 16) & 0x7FFFu) - kKeyBase, 0), kKeyMax);
-    const uint32_t est = est_tab[((uint32_t)k << 1) | (b >> 31)];
+    const uint32_t k = __builtin_elementwise_sub_sat((b >> 16) & 0x3FFFu, (uint32_t)kKeyBase);
+    const uint32_t est = est_tab[(k << 1) | (b >> 31)];
     const uint32_t r = est + (v >= cl[est + 1] ? 1u : 0u);
     const Pair p = lw[r];
     Lr = p.l;
@@ -540,11 +540,20 @@ __global__ __launch_bounds__(256) void k_stats(StatsArgs a) {
     for (int64_t base = (int64_t)blockIdx.x * per_block; base < a.J;
          base += (int64_t)gridDim.x * per_block) {
         float e[kStatsPairs][8];
+        float prior_s[kStatsPairs], prior_q[kStatsPairs];
         bool live[kStatsPairs];
 #pragma unroll
         for (int u = 0; u < kStatsPairs; u++) {
             const int64_t j = base + (wave * kStatsPairs + u) * 2 + half;
             live[u] = j < a.J;
+            // the running sums of earlier workers are fetched with the data,
+            // so the read-modify-write costs no extra round trip
+            prior_s[u] = 0.0f;
+            prior_q[u] = 0.0f;
+            if (live[u] && l == 0 && !a.first) {
+                prior_s[u] = a.sum[j];
+                prior_q[u] = a.sumsq[j];
+            }
             if (live[u]) {
                 if (F32) {
                     const float4 *src = reinterpret_cast<const float4 *>(
@@ -579,8 +588,8 @@ __global__ __launch_bounds__(256) void k_stats(StatsArgs a) {
             if (live[u] && l == 0) {
                 float S = s, F = q;
                 if (!a.first) {
-                    S = a.sum[j] + s;
-                    F = a.sumsq[j] + q;
+                    S = prior_s[u] + s;
+                    F = prior_q[u] + q;
                 }
                 a.sum[j] = S;
                 a.sumsq[j] = F;
@@ -941,7 +950,8 @@ static int grid_for(int64_t items, int64_t per_block, int64_t cap) {
     return (int)b;
 }
 
-constexpr int64_t kStreamGrid = 2048;  // 256 CUs x 8 resident blocks
+constexpr int64_t kStreamGrid = 2048;  // 256 CUs x 8 blocks
+constexpr int64_t kCodecGrid = 3072;   // 256 CUs x 12 blocks
 
 hipError_t launch_zero(uint32_t *p, int64_t n, hipStream_t s) {
     hipLaunchKernelGGL(k_zero_u32, dim3(grid_for(n, 256, 1024)), dim3(256), 0, s, p, n);
@@ -977,7 +987,9 @@ hipError_t launch_reorder(const ReorderArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_codec(const CodecArgs &a, int mode, int local, int64_t max_sg, hipStream_t s) {
-    const dim3 grid(grid_for(max_sg, kSGPerBlock, kStreamGrid)), block(256);
+    // the encoding kernels gain from a deeper queue of blocks (12 per CU);
+    // finalize is a plain stream and runs best at 8
+    const dim3 grid(grid_for(max_sg, kSGPerBlock, mode == kFinalize ? kStreamGrid : kCodecGrid)), block(256);
     if (mode == kCompress && local == kLocalBF16) hipLaunchKernelGGL((k_codec<kCompress, kLocalBF16>), grid, block, 0, s, a);
     else if (mode == kCompress && local == kLocalF32) hipLaunchKernelGGL((k_codec<kCompress, kLocalF32>), grid, block, 0, s, a);
     else if (mode == kHop && local == kLocalBF16) hipLaunchKernelGGL((k_codec<kHop, kLocalBF16>), grid, block, 0, s, a);

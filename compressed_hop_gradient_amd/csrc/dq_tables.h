@@ -69,13 +69,19 @@ constexpr LevelTables kLevelTables = make_tables();
 
 constexpr int kKeyBase = 0x3B00;              // fp32 bits of 2^-9, >> 16
 constexpr int kKeyMax = 0x3F80 - kKeyBase;    // key of 1.0
-constexpr int kKeys = kKeyMax + 1;
+// The kernels take the key from fp32 bits 29..16 (bit 30 is clear for every
+// |v| < 2), so a key never exceeds 0x3FFF - kKeyBase and needs no upper
+// clamp.  Keys above kKeyMax hold |v| > 1 + 2^-7, which finite inputs never
+// produce (|v| exceeds 1 by at most two ulps); they repeat the entries of
+// |v| = 1.  Non-finite inputs (flagged by the stats) land somewhere in the
+// table and give meaningless but in-bounds codes.
+constexpr int kKeys = 0x4000 - kKeyBase;
 
 constexpr float key_lo(int k) {
-    return k == 0 ? 0.0f : __builtin_bit_cast(float, (unsigned)(k + kKeyBase) << 16);
+    return k == 0 ? 0.0f : (k >= kKeyMax ? 1.0f : __builtin_bit_cast(float, (unsigned)(k + kKeyBase) << 16));
 }
 constexpr float key_hi(int k) {
-    return k == kKeyMax ? 1.0f : __builtin_bit_cast(float, (unsigned)(k + 1 + kKeyBase) << 16);
+    return k >= kKeyMax ? 1.0f : __builtin_bit_cast(float, (unsigned)(k + 1 + kKeyBase) << 16);
 }
 
 template <int NL>
