@@ -73,6 +73,20 @@ def measured_traffic(kernel, src_hash):
     return e.get("bytes_per_launch")
 
 
+def measured_valu(kernel, src_hash):
+    """VALU issue rate of a kernel from a rocprofv3 SQ counter run, if taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", "valu.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    e = rec.get(kernel)
+    if not e or e.get("kernel_source") != src_hash:
+        return None
+    return {"instr_per_launch": e["valu_instr_per_launch"], "instr_per_s": e["valu_instr_per_s"],
+            "peak_instr_per_s": rec["peak_instr_per_s"], "frac": e["frac_of_valu_roof"]}
+
+
 def cpu_baseline(args, wl_name, budget, device):
     """The oracle as it stands, on host cores, on a bounded sample (inputs are
     drawn by the shared generator on the GPU and copied to the host)."""
@@ -192,6 +206,20 @@ def main():
                    "stats_traffic_ratio": 8.0 / (256 * 2), "class_counts": info["class_counts"]}
         del exact
 
+    # achievable HBM rate on this machine: a plain 1 GiB device-to-device copy
+    # (read + write), 10 repetitions, HIP events on the current stream
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 30) / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+    del src, dst
+
     copy_cal = None
     if args.copy_calibration_mib > 0:
         nb = args.copy_calibration_mib << 20
@@ -224,7 +252,9 @@ def main():
                      "kernel": "DAR hop, bf16 local (k_codec<hop,bf16>)",
                      "algorithmic_bytes_per_launch": bytes_per_launch,
                      "bytes_per_coord": bpc, "avg_launch_ms": avg_ms, "launches": hg["launches"],
-                     "kernel_source": src_hash},
+                     "kernel_source": src_hash,
+                     "achievable_copy_GBs": copy_gbs, "frac_of_copy": achieved / copy_gbs,
+                     "valu_issue": measured_valu("hop_grad", src_hash)},
         "dar_kernel_coords_per_s": (hg["coords"] / (hg["ms"] * 1e-3)) if hg["ms"] > 0 else None,
         "kernels": kernels,
         "quality": quality,
