@@ -21,8 +21,10 @@
  *   dq_finalize  decode, add back the mean, restore the original order
  *                (scribe notes, main all-reduce phase)
  *
- * Numerics and layouts not fixed by the pages follow the readings recorded in
- * the repository's design document; the CPU oracle implements the same ones.
+ * Numerics and layouts the pages leave open are fixed by one stated reading
+ * each (fp32 with round-to-nearest-even and no contraction, the level set,
+ * the region layout, the dither counters); the CPU oracle implements the same
+ * readings independently.
  *
  * Conventions
  *   - Every call returns a dq_status; errors are negative.  Nothing aborts or

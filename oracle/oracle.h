@@ -16,8 +16,9 @@
  *   - pith.science review, "What carries the argument" and Fig. 3 caption:
  *     widths {2,4,8}, thresholds locked by T12 = 5/32 T24, T24 = 17/512 T48,
  *     one scalar selects the allocation.
- * Every step the pages leave open is fixed by a stated reading (the design
- * document lists them); the oracle implements those readings literally.
+ * Every step the pages leave open is fixed by one stated reading, given in
+ * the comment of the function that implements it; the oracle implements
+ * those readings literally.
  *
  * Floating point: IEEE fp32, round to nearest even, no contraction (built with
  * -ffp-contract=off, no fast-math), denormals preserved.
