@@ -658,11 +658,26 @@ __global__ __launch_bounds__(256) void k_alloc_count(AllocArgs a, int pass) {
         t8[threadIdx.x] = 16384.0f * rho;
     }
     __syncthreads();
+    // count 0 adds to no suffix sum and is skipped; count n (F at or above
+    // every candidate threshold) is kept in a register
+    const float lo4 = t4[0], hi4 = t4[n - 1], lo8 = t8[0], hi8 = t8[n - 1];
+    uint32_t top4 = 0u, top8 = 0u;
     for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < a.J;
          j += (int64_t)gridDim.x * blockDim.x) {
         const float F = a.sumsq[j];
-        atomicAdd(&h4[count_le(t4, n, F)], 1u);
-        atomicAdd(&h8[count_le(t8, n, F)], 1u);
+        if (F >= hi4) top4++;
+        else if (F >= lo4) atomicAdd(&h4[count_le(t4, n, F)], 1u);
+        if (F >= hi8) top8++;
+        else if (F >= lo8) atomicAdd(&h8[count_le(t8, n, F)], 1u);
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        top4 += __shfl_xor(top4, d, 64);
+        top8 += __shfl_xor(top8, d, 64);
+    }
+    if ((threadIdx.x & 63) == 0) {
+        if (top4) atomicAdd(&h4[n], top4);
+        if (top8) atomicAdd(&h8[n], top8);
     }
     __syncthreads();
     for (int i = threadIdx.x; i < n + 1; i += blockDim.x) {
@@ -726,10 +741,20 @@ __global__ __launch_bounds__(256) void k_alloc_final(AllocArgs a) {
     const float t4 = 544.0f * rho, t8 = 16384.0f * rho;
     uint32_t cnt[3] = {0u, 0u, 0u};
     const int64_t j0 = (int64_t)blockIdx.x * kReorderSGPerBlock + threadIdx.x * 4;
+    if (j0 + 4 <= a.J) {
+        // widths are 256-byte aligned in the workspace and j0 is a multiple of 4
+        const float4 F4 = *reinterpret_cast<const float4 *>(a.sumsq + j0);
+        const float F[4] = {F4.x, F4.y, F4.z, F4.w};
+        uint32_t w = 0u;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int64_t j = j0 + i;
-        if (j < a.J) {
+        for (int i = 0; i < 4; i++) {
+            const int k = F[i] >= t8 ? 2 : (F[i] >= t4 ? 1 : 0);
+            w |= (2u << k) << (8 * i);
+            cnt[k]++;
+        }
+        *reinterpret_cast<uint32_t *>(a.widths + j0) = w;
+    } else {
+        for (int64_t j = j0; j < a.J; j++) {
             const float F = a.sumsq[j];
             const int k = F >= t8 ? 2 : (F >= t4 ? 1 : 0);
             a.widths[j] = (uint8_t)(2 << k);
@@ -742,17 +767,35 @@ __global__ __launch_bounds__(256) void k_alloc_final(AllocArgs a) {
     const unsigned long long tot = block_sum_u64(v);
     if (threadIdx.x == 0) {
 #pragma unroll
-        for (int k = 0; k < 3; k++) {
-            const uint32_t ck = (uint32_t)((tot >> (16 * k)) & 0xFFFFu);
-            a.blkcnt[k * a.nblk + blockIdx.x] = (int32_t)ck;
-            if (ck) atomicAdd(&c->class_counts[k], (unsigned long long)ck);
-        }
+        for (int k = 0; k < 3; k++)
+            a.blkcnt[k * a.nblk + blockIdx.x] = (int32_t)((tot >> (16 * k)) & 0xFFFFu);
     }
 }
 
-// ---------------------------------------------------------------------------
-// reorder: exclusive scan of per-block class counts, stable scatter
-// ---------------------------------------------------------------------------
+// Class totals from the per-block counts (one block; no contended atomics).
+__global__ __launch_bounds__(1024) void k_alloc_totals(AllocArgs a) {
+    __shared__ unsigned long long part[16][3];
+    unsigned long long s[3] = {0ull, 0ull, 0ull};
+    for (int64_t b = threadIdx.x; b < a.nblk; b += blockDim.x) {
+#pragma unroll
+        for (int k = 0; k < 3; k++) s[k] += (unsigned long long)a.blkcnt[k * a.nblk + b];
+    }
+#pragma unroll
+    for (int k = 0; k < 3; k++) {
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) s[k] += __shfl_xor(s[k], d, 64);
+    }
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+        for (int k = 0; k < 3; k++) part[threadIdx.x >> 6][k] = s[k];
+    }
+    __syncthreads();
+    if (threadIdx.x < 3) {
+        unsigned long long t = 0ull;
+        for (int w = 0; w < (int)(blockDim.x >> 6); w++) t += part[w][threadIdx.x];
+        a.ctrl->class_counts[threadIdx.x] = t;
+    }
+}
 
 __global__ __launch_bounds__(1024) void k_reorder_scan(ReorderArgs a) {
     __shared__ int64_t sh[1024];
@@ -975,6 +1018,9 @@ hipError_t launch_alloc_pass(const AllocArgs &a, int pass, hipStream_t s) {
 
 hipError_t launch_alloc_final(const AllocArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(k_alloc_final, dim3((unsigned)a.nblk), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_alloc_totals, dim3(1), dim3(1024), 0, s, a);
     return hipGetLastError();
 }
 
