@@ -111,6 +111,7 @@ struct or_ctx {
     uint64_t seed;
     uint32_t round;
     int32_t rounding;
+    int32_t alloc;
     double eps;
     float L[3][256];
     float W[3][256];
@@ -168,6 +169,12 @@ void or_destroy(or_ctx *c) {
 void or_set_seed(or_ctx *c, uint64_t seed) { c->seed = seed; }
 void or_set_round(or_ctx *c, uint32_t round) { c->round = round; }
 void or_set_rounding(or_ctx *c, int32_t mode) { c->rounding = mode; }
+void or_set_alloc(or_ctx *c, int32_t mode) {
+    c->alloc = mode;
+    c->allocated = 0;
+    c->reordered = 0;
+}
+
 void or_set_eps(or_ctx *c, double eps) { c->eps = eps; build_tables(c); }
 
 /* ------------------------------------------------------------------ */
@@ -238,13 +245,36 @@ void or_thresholds(uint32_t rho_bits, float out[3]) {
     out[2] = 16384.0f * rho;  /* T48 */
 }
 
-int64_t or_count_bits(const or_ctx *c, uint32_t rho_bits) {
+/* The squared norm of the mean-subtracted values (pith.science review,
+ * referee major 1): G_j = F_j - n S mu_j^2 with S = 256, as fl(F_j -
+ * fl(fl(256 n) * fl(mu_j * mu_j))), negative results (rounding) set to 0.
+ * Needs mu (computed at the start of the allocation). */
+static void mean_corrected_key(const or_ctx *c, float *G) {
+    const float denom = (float)(256 * c->n);
+    for (int64_t j = 0; j < c->J; j++) {
+        const float m2 = c->mu[j] * c->mu[j];
+        const float t = denom * m2;
+        const float g = c->F[j] - t;
+        G[j] = g < 0.0f ? 0.0f : g;
+    }
+}
+
+void or_get_alloc_key(const or_ctx *c, float *out) {
+    if (c->alloc == OR_ALLOC_MEAN_CORRECTED) mean_corrected_key(c, out);
+    else memcpy(out, c->F, (size_t)c->J * sizeof(float));
+}
+
+static int64_t count_bits_on(const float *key, int64_t J, uint32_t rho_bits) {
     float rho = f_from_bits(rho_bits);
     float t4 = 544.0f * rho, t8 = 16384.0f * rho;
     int64_t total = 0;
 #pragma omp parallel for reduction(+ : total) schedule(static)
-    for (int64_t j = 0; j < c->J; j++) total += width_of(c->F[j], t4, t8);
+    for (int64_t j = 0; j < J; j++) total += width_of(key[j], t4, t8);
     return total;
+}
+
+int64_t or_count_bits(const or_ctx *c, uint32_t rho_bits) {
+    return count_bits_on(c->F, c->J, rho_bits);
 }
 
 int or_allocate(or_ctx *c) {
@@ -252,26 +282,44 @@ int or_allocate(or_ctx *c) {
     const float denom = (float)(256 * c->n);
     for (int64_t j = 0; j < c->J; j++) c->mu[j] = c->sum[j] / denom;
     const int64_t budget = or_budget_bits(c);
+    c->C[0] = c->C[1] = c->C[2] = 0;
+    if (c->alloc == OR_ALLOC_UNIFORM) {
+        /* widest q in {2,4,8} with q <= B, i.e. q J <= floor(B J) */
+        const int q = c->budget >= 8.0f ? 8 : (c->budget >= 4.0f ? 4 : 2);
+        for (int64_t j = 0; j < c->J; j++) c->width[j] = (uint8_t)q;
+        c->C[q == 2 ? 0 : (q == 4 ? 1 : 2)] = c->J;
+        c->rho_bits = 0x7FC00000u;
+        c->allocated = 1;
+        c->reordered = 0;
+        return 0;
+    }
+    const float *key = c->F;
+    float *G = NULL;
+    if (c->alloc == OR_ALLOC_MEAN_CORRECTED) {
+        G = (float *)malloc((size_t)c->J * sizeof(float));
+        mean_corrected_key(c, G);
+        key = G;
+    }
     uint32_t rho;
-    if (or_count_bits(c, 0u) <= budget) {
+    if (count_bits_on(key, c->J, 0u) <= budget) {
         rho = 0u;
     } else {
         uint32_t lo = 0u, hi = 0x7F800000u; /* +inf: every width is 2 */
         while (hi - lo > 1u) {
             uint32_t mid = lo + (hi - lo) / 2u;
-            if (or_count_bits(c, mid) <= budget) hi = mid; else lo = mid;
+            if (count_bits_on(key, c->J, mid) <= budget) hi = mid; else lo = mid;
         }
         rho = hi;
     }
     c->rho_bits = rho;
     float r = f_from_bits(rho);
     float t4 = 544.0f * r, t8 = 16384.0f * r;
-    c->C[0] = c->C[1] = c->C[2] = 0;
     for (int64_t j = 0; j < c->J; j++) {
-        int q = width_of(c->F[j], t4, t8);
+        int q = width_of(key[j], t4, t8);
         c->width[j] = (uint8_t)q;
         c->C[q == 2 ? 0 : (q == 4 ? 1 : 2)]++;
     }
+    free(G);
     c->allocated = 1;
     c->reordered = 0;
     return 0;

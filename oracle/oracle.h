@@ -39,6 +39,14 @@ enum { OR_SG = 256, OR_GROUP = 16, OR_NGROUPS = 16 };
 enum { OR_RING = 0, OR_BUTTERFLY = 1 };
 enum { OR_BF16 = 0, OR_F32 = 1, OR_PACKED = 2 };
 enum { OR_CORRELATED = 0, OR_INDEPENDENT = 1 };
+/* Allocation variants (pith.science review, referee major 1: the thresholds
+ * see F_j although the quantised values have squared norm F_j - n S mu_j^2,
+ * and Table 6 compares variable with uniform widths):
+ *   OR_ALLOC_THRESHOLD      the method: thresholds on F_j
+ *   OR_ALLOC_MEAN_CORRECTED thresholds on G_j = max(F_j - fl(256 n) mu_j^2, 0)
+ *   OR_ALLOC_UNIFORM        every super-group at the widest q in {2,4,8}
+ *                           with q <= B (rho reported as NaN) */
+enum { OR_ALLOC_THRESHOLD = 0, OR_ALLOC_MEAN_CORRECTED = 1, OR_ALLOC_UNIFORM = 2 };
 
 typedef struct or_ctx or_ctx;
 
@@ -62,6 +70,7 @@ void or_set_seed(or_ctx *c, uint64_t seed);
 void or_set_round(or_ctx *c, uint32_t round);
 void or_set_rounding(or_ctx *c, int32_t mode);
 void or_set_eps(or_ctx *c, double eps);
+void or_set_alloc(or_ctx *c, int32_t mode);
 
 /* Stage 1: per-worker statistics, called in rank order 0..n-1. */
 int or_stats(or_ctx *c, int32_t worker, const void *grad, int32_t dtype);
@@ -73,6 +82,9 @@ int or_reorder(or_ctx *c);
 /* Accessors (host copies). */
 void or_get_stats(const or_ctx *c, float *sum, float *F, float *mu);
 uint32_t or_get_rho_bits(const or_ctx *c);
+/* the values the thresholds were applied to (F, or G for the mean-corrected
+ * variant); valid after or_allocate */
+void or_get_alloc_key(const or_ctx *c, float *out);
 void or_get_widths(const or_ctx *c, uint8_t *w);
 void or_get_perm(const or_ctx *c, int32_t *perm, int32_t *inv);
 void or_get_class_counts(const or_ctx *c, int64_t counts[3]);

@@ -13,6 +13,7 @@ from . import build as _build
 RING, BUTTERFLY = 0, 1
 BF16, F32, PACKED = 0, 1, 2
 CORRELATED, INDEPENDENT = 0, 1
+ALLOC_THRESHOLD, ALLOC_MEAN_CORRECTED, ALLOC_UNIFORM = 0, 1, 2
 Q_OF_CLASS = (2, 4, 8)
 
 _lib = None
@@ -37,6 +38,8 @@ def lib():
             "or_set_seed": (None, [vp, u64]),
             "or_set_round": (None, [vp, u32]),
             "or_set_rounding": (None, [vp, i32]),
+            "or_set_alloc": (None, [vp, i32]),
+            "or_get_alloc_key": (None, [vp, vp]),
             "or_set_eps": (None, [vp, f64]),
             "or_stats": (C.c_int, [vp, i32, vp, i32]),
             "or_allocate": (C.c_int, [vp]),
@@ -153,7 +156,7 @@ class Oracle:
     """One simulated round on the CPU (mirrors the stage order of the library)."""
 
     def __init__(self, n_coords, n_workers, topology=RING, avg_bits=5.0, seed=1, rnd=0,
-                 rounding=CORRELATED, eps=None):
+                 rounding=CORRELATED, eps=None, alloc=ALLOC_THRESHOLD):
         self.d = int(n_coords)
         self.n = int(n_workers)
         self.topology = int(topology)
@@ -166,6 +169,7 @@ class Oracle:
         lib().or_set_rounding(self.h, int(rounding))
         if eps is not None:
             lib().or_set_eps(self.h, float(eps))
+        lib().or_set_alloc(self.h, int(alloc))
         self.log2n = max(0, (self.n - 1).bit_length())
 
     def __del__(self):
@@ -199,6 +203,11 @@ class Oracle:
 
     def rho(self):
         return np.array([self.rho_bits()], np.uint32).view(np.float32)[0]
+
+    def alloc_key(self):
+        k = np.zeros(self.J, np.float32)
+        lib().or_get_alloc_key(self.h, _p(k))
+        return k
 
     def widths(self):
         w = np.zeros(self.J, np.uint8)

@@ -748,3 +748,119 @@ def test_mxfp8_schedule_composition():
     exp0 = po.mxfp8_roundtrip(po.mxfp8_roundtrip(g[1][:h]) + g[0][:h])
     exp1 = po.mxfp8_roundtrip(po.mxfp8_roundtrip(g[0][h:]) + g[1][h:])
     assert np.array_equal(outb, np.concatenate([exp0, exp1]))
+
+
+# ---------------------------------------------------------------------------
+# allocation variants (pith.science review, referee major 1; Table 6; the
+# "Load-bearing premise" on spatial locality and Fig. 1's shuffled norms)
+# ---------------------------------------------------------------------------
+
+def _variant_round(gs, budget, alloc, topo=po.RING):
+    n, d = len(gs), gs[0].size
+    o = po.Oracle(d, n, topo, budget, alloc=alloc)
+    for w in range(n):
+        o.stats(w, gs[w])
+    o.allocate()
+    return o
+
+
+def test_mean_corrected_key_is_centred_energy():
+    """G_j against the exact squared norm of the mean-subtracted values,
+    sum_w sum_i (x - mu_j)^2 in fp64, with large per-SG offsets so that the
+    correction term is most of F_j, and constant SGs (exactly 0 in exact
+    arithmetic)."""
+    rng = np.random.default_rng(21)
+    n, J = 4, 96
+    off = np.repeat(rng.standard_normal(J) * 10.0 ** rng.uniform(-3, 1, J), 256)
+    spread = np.repeat(10.0 ** rng.uniform(-6, 0, J), 256)
+    gs = [(off + spread * rng.standard_normal(256 * J)).astype(np.float32) for _ in range(n)]
+    for g in gs:   # constant super-groups, the same value on every worker
+        g[256 * 5:256 * 6] = np.float32(0.37)
+    o = _variant_round(gs, 5.0, po.ALLOC_MEAN_CORRECTED)
+    G = o.alloc_key().astype(np.float64)
+    _, F, mu = o.stats_arrays()
+    X = np.stack([g.reshape(J, 256).astype(np.float64) for g in gs])
+    mu64 = X.mean((0, 2))
+    centred = ((X - mu64[None, :, None]) ** 2).sum((0, 2))
+    F64 = (X * X).sum((0, 2))
+    eps = 2.0 ** -24
+    corr = 256 * n * mu.astype(np.float64) ** 2
+    bound = (12 + n) * eps * F64 * 1.01 + 4 * eps * corr + eps * centred \
+        + 256 * n * (mu.astype(np.float64) - mu64) ** 2 + 1e-30
+    assert (np.abs(G - centred) <= bound).all()
+    assert (G >= 0).all()
+    # with the offsets, the plain key overstates the quantised energy by far
+    assert np.median(F64 / np.maximum(centred, 1e-300)) > 10
+    # a sign error or a missing factor n would miss the bound by orders of magnitude
+    wrong = F.astype(np.float64) - 256 * mu.astype(np.float64) ** 2
+    assert (np.abs(wrong - centred) > bound).any()
+
+
+def test_mean_corrected_allocation_follows_its_key():
+    """Widths are the threshold rule on G at the returned rho; rho is the
+    smallest fp32 meeting the budget; SGs with large offsets and small
+    spread move to narrow widths."""
+    rng = np.random.default_rng(22)
+    n, J = 2, 256
+    off = np.repeat(np.where(rng.random(J) < 0.3, 50.0, 0.0), 256)
+    spread = np.repeat(10.0 ** rng.uniform(-2, 1, J), 256)
+    gs = [(off + spread * rng.standard_normal(256 * J)).astype(np.float32) for _ in range(n)]
+    for budget in (2.5, 4.0, 5.0, 6.5):
+        o = _variant_round(gs, budget, po.ALLOC_MEAN_CORRECTED)
+        G = o.alloc_key()
+        rb = o.rho_bits()
+        rho = f32_from_bits(rb)
+        t4, t8 = np.float32(544) * rho, np.float32(16384) * rho
+
+        def count(r):
+            r = f32_from_bits(r)
+            a4, a8 = np.float32(544) * r, np.float32(16384) * r
+            return int((2 + 2 * (G >= a4) + 4 * (G >= a8)).sum())
+
+        q = o.widths().astype(np.int64)
+        assert np.array_equal(q, 2 + 2 * (G >= t4) + 4 * (G >= t8))
+        assert q.sum() <= o.budget_bits()
+        if rb > 0:
+            assert count(rb - 1) > o.budget_bits()
+        plain = _variant_round(gs, budget, po.ALLOC_THRESHOLD).widths()
+        offset_sgs = off[::256] > 0
+        assert q[offset_sgs].mean() <= plain[offset_sgs].mean()
+        if budget == 5.0:
+            assert q[offset_sgs].mean() < plain[offset_sgs].mean()
+
+
+@pytest.mark.parametrize("budget,q", [(2.0, 2), (3.0, 2), (3.99, 2), (4.0, 4), (5.0, 4), (7.9, 4), (8.0, 8), (9.5, 8)])
+def test_uniform_allocation(budget, q):
+    rng = np.random.default_rng(23)
+    gs = [rng.standard_normal(256 * 40).astype(np.float32) for _ in range(3)]
+    o = _variant_round(gs, budget, po.ALLOC_UNIFORM)
+    assert (o.widths() == q).all()
+    assert o.rho_bits() == 0x7FC00000
+    assert o.class_counts().tolist() == [40 * (q == 2), 40 * (q == 4), 40 * (q == 8)]
+    assert 40 * q <= o.budget_bits()
+
+
+def test_variable_widths_beat_uniform_unless_shuffled():
+    """Table 6 direction: at 4 bits per coordinate, variable widths give a
+    lower vNMSE than uniform 4-bit codes on gradients with skewed, spatially
+    local SG norms.  Fig. 1 / the load-bearing premise: after a random
+    shuffle of coordinates (the same for every worker) the SG norms flatten
+    and the advantage mostly disappears."""
+    rng = np.random.default_rng(24)
+    n, J = 4, 1024
+    scale = np.repeat(10.0 ** rng.uniform(-4, 0, J), 256)
+    gs = [(scale * rng.standard_normal(256 * J)).astype(np.float32) for _ in range(n)]
+    perm = rng.permutation(256 * J)
+    shuffled = [g[perm].copy() for g in gs]
+
+    def vnmse(grads, alloc):
+        exact = np.sum([g.astype(np.float64) for g in grads], axis=0)
+        o = po.Oracle(256 * J, n, po.RING, 4.0, alloc=alloc, rounding=po.INDEPENDENT)
+        out = o.allreduce(grads)
+        return float(((out - exact) ** 2).sum() / (exact ** 2).sum())
+
+    local_ratio = vnmse(gs, po.ALLOC_UNIFORM) / vnmse(gs, po.ALLOC_THRESHOLD)
+    shuffled_ratio = vnmse(shuffled, po.ALLOC_UNIFORM) / vnmse(shuffled, po.ALLOC_THRESHOLD)
+    assert local_ratio > 2.0
+    assert shuffled_ratio < 1.5
+    assert shuffled_ratio < local_ratio / 2
