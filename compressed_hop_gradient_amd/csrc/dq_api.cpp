@@ -36,6 +36,7 @@ struct dq_plan {
     uint64_t seed = 1;
     uint32_t round = 0;
     int32_t rounding = DQ_ROUND_CORRELATED;
+    int32_t alloc = DQ_ALLOC_THRESHOLD;
     bool timing = false;
 
     uint8_t *ws = nullptr;
@@ -304,6 +305,11 @@ dq_status dq_plan_set_u64(dq_plan *p, int32_t option, uint64_t v) {
             if (v > 1) return DQ_EINVAL;
             p->timing = v == 1;
             return DQ_OK;
+        case DQ_OPT_ALLOC:
+            if (v != DQ_ALLOC_THRESHOLD && v != DQ_ALLOC_MEAN_CORRECTED && v != DQ_ALLOC_UNIFORM)
+                return DQ_EINVAL;
+            p->alloc = (int32_t)v;
+            return DQ_OK;
         default: return DQ_EINVAL;
     }
 }
@@ -383,13 +389,19 @@ dq_status dq_allocate(dq_plan *p, void *stream) {
     a.widths = p->ws + p->lay.widths;
     a.blkcnt = blkcnt_of(p);
     a.nblk = p->nblk;
+    a.sum = f32_at(p, p->lay.sum);
+    a.denom = (float)(256 * p->n);
+    a.mode = p->alloc;
+    // uniform: the widest class whose width fits the budget
+    a.uniform_k = p->budget >= 8.0f ? 2 : (p->budget >= 4.0f ? 1 : 0);
     Launch L;
     hipError_t e = timed_begin(p, DQ_K_ALLOCATE, 0, 0, s, L);
     // histograms, class counts, prefix and flag start at zero (a fill kernel,
     // graph-safe); nonfinite is kept (it belongs to the stats of this round)
     const int64_t nzero = (int64_t)(offsetof(Ctrl, rho_bits) / 4);
     if (e == hipSuccess) e = launch_zero(reinterpret_cast<uint32_t *>(a.ctrl), nzero, s);
-    for (int pass = 0; pass < kRadixPasses && e == hipSuccess; pass++) e = launch_alloc_pass(a, pass, s);
+    if (p->alloc != DQ_ALLOC_UNIFORM)
+        for (int pass = 0; pass < kRadixPasses && e == hipSuccess; pass++) e = launch_alloc_pass(a, pass, s);
     if (e == hipSuccess) e = launch_alloc_final(a, s);
     if (e == hipSuccess) e = timed_end(p, L, s);
     if (e != hipSuccess) return DQ_EHIP;

@@ -71,8 +71,14 @@ struct StatsArgs {
     int32_t *nonfinite;
 };
 
+enum AllocMode { kAllocThreshold = 0, kAllocMeanCorrected = 1, kAllocUniform = 2 };
+
 struct AllocArgs {
     const float *sumsq;
+    const float *sum;   // mean-corrected key: mu = fl(sum / denom)
+    float denom;        // fl(256 n)
+    int32_t mode;       // AllocMode
+    int32_t uniform_k;  // class of every super-group under kAllocUniform
     int64_t J;
     long long budget;   // floor(B * J)
     Ctrl *ctrl;

@@ -623,6 +623,18 @@ __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v
 __device__ __forceinline__ int radix_shift(int pass) { return pass == 0 ? 23 : (pass == 1 ? 15 : (pass == 2 ? 7 : 0)); }
 __device__ __forceinline__ int radix_ncand(int pass) { return pass == 3 ? 128 : 256; }
 
+// The value the thresholds compare: F_j, or under the mean-corrected variant
+// the squared norm of the mean-subtracted values, F_j - fl(256 n) mu_j^2 with
+// each product and difference rounded once and negative results set to 0.
+__device__ __forceinline__ float alloc_key(const AllocArgs &a, float F, float sum) {
+    if (a.mode != kAllocMeanCorrected) return F;
+    const float mu = sum / a.denom;
+    const float m2 = mu * mu;
+    const float t = a.denom * m2;
+    const float g = F - t;
+    return g < 0.0f ? 0.0f : g;
+}
+
 // number of entries of the non-decreasing t[0..n) that are <= F
 __device__ __forceinline__ uint32_t count_le(const float *t, int n, float F) {
     uint32_t lo = 0, len = (uint32_t)n;
@@ -664,7 +676,7 @@ __global__ __launch_bounds__(256) void k_alloc_count(AllocArgs a, int pass) {
     uint32_t top4 = 0u, top8 = 0u;
     for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < a.J;
          j += (int64_t)gridDim.x * blockDim.x) {
-        const float F = a.sumsq[j];
+        const float F = alloc_key(a, a.sumsq[j], a.mode == kAllocMeanCorrected ? a.sum[j] : 0.0f);
         if (F >= hi4) top4++;
         else if (F >= lo4) atomicAdd(&h4[count_le(t4, n, F)], 1u);
         if (F >= hi8) top8++;
@@ -736,31 +748,37 @@ __global__ __launch_bounds__(256) void k_alloc_decide(AllocArgs a, int pass) {
 // widths, per-block class counts for the reorder, global class counts
 __global__ __launch_bounds__(256) void k_alloc_final(AllocArgs a) {
     Ctrl *c = a.ctrl;
-    const uint32_t rb = c->rho_bits;
+    const bool uniform = a.mode == kAllocUniform, centred = a.mode == kAllocMeanCorrected;
+    // the uniform variant has no scalar (block 0 stores NaN below, nobody reads it)
+    const uint32_t rb = uniform ? 0u : c->rho_bits;
     const float rho = __uint_as_float(rb);
     const float t4 = 544.0f * rho, t8 = 16384.0f * rho;
     uint32_t cnt[3] = {0u, 0u, 0u};
     const int64_t j0 = (int64_t)blockIdx.x * kReorderSGPerBlock + threadIdx.x * 4;
     if (j0 + 4 <= a.J) {
-        // widths are 256-byte aligned in the workspace and j0 is a multiple of 4
+        // the arrays are 256-byte aligned in the workspace and j0 is a multiple of 4
         const float4 F4 = *reinterpret_cast<const float4 *>(a.sumsq + j0);
-        const float F[4] = {F4.x, F4.y, F4.z, F4.w};
+        float4 S4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (centred) S4 = *reinterpret_cast<const float4 *>(a.sum + j0);
+        const float F[4] = {F4.x, F4.y, F4.z, F4.w}, S[4] = {S4.x, S4.y, S4.z, S4.w};
         uint32_t w = 0u;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const int k = F[i] >= t8 ? 2 : (F[i] >= t4 ? 1 : 0);
+            const float G = alloc_key(a, F[i], S[i]);
+            const int k = uniform ? a.uniform_k : (G >= t8 ? 2 : (G >= t4 ? 1 : 0));
             w |= (2u << k) << (8 * i);
             cnt[k]++;
         }
         *reinterpret_cast<uint32_t *>(a.widths + j0) = w;
     } else {
         for (int64_t j = j0; j < a.J; j++) {
-            const float F = a.sumsq[j];
-            const int k = F >= t8 ? 2 : (F >= t4 ? 1 : 0);
+            const float G = alloc_key(a, a.sumsq[j], centred ? a.sum[j] : 0.0f);
+            const int k = uniform ? a.uniform_k : (G >= t8 ? 2 : (G >= t4 ? 1 : 0));
             a.widths[j] = (uint8_t)(2 << k);
             cnt[k]++;
         }
     }
+    if (uniform && blockIdx.x == 0 && threadIdx.x == 0) c->rho_bits = 0x7FC00000u;
     // pack three counts (each <= 1024) into 16-bit fields and reduce
     unsigned long long v = (unsigned long long)cnt[0] | ((unsigned long long)cnt[1] << 16) |
                            ((unsigned long long)cnt[2] << 32);

@@ -18,7 +18,8 @@ DQ_OK, DQ_EINVAL, DQ_EBUDGET, DQ_ESTATE, DQ_EWORKSPACE, DQ_ENULL, DQ_EHIP, DQ_EN
 RING, BUTTERFLY = 0, 1
 BF16, F32, PACKED = 0, 1, 2
 CORRELATED, INDEPENDENT = 0, 1
-OPT_SEED, OPT_ROUND, OPT_ROUNDING, OPT_TIMING = 0, 1, 2, 3
+OPT_SEED, OPT_ROUND, OPT_ROUNDING, OPT_TIMING, OPT_ALLOC = 0, 1, 2, 3, 4
+ALLOC_THRESHOLD, ALLOC_MEAN_CORRECTED, ALLOC_UNIFORM = 0, 1, 2
 KERNEL_KINDS = ("stats", "allocate", "reorder", "compress", "hop_grad", "hop_packed",
                 "finalize", "mxfp8")
 
@@ -131,7 +132,7 @@ class Plan:
     """
 
     def __init__(self, n_coords, n_workers, topology=RING, avg_bits=5.0, seed=1, rnd=0,
-                 rounding=CORRELATED, device="cuda", timing=False):
+                 rounding=CORRELATED, device="cuda", timing=False, alloc=ALLOC_THRESHOLD):
         self.d = int(n_coords)
         self.n = int(n_workers)
         self.J = self.d // 256
@@ -145,6 +146,7 @@ class Plan:
         self.set(OPT_ROUND, rnd)
         self.set(OPT_ROUNDING, rounding)
         self.set(OPT_TIMING, 1 if timing else 0)
+        self.set(OPT_ALLOC, alloc)
         nbytes = lib().dq_workspace_bytes(self.h)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _check(lib().dq_plan_bind(self.h, _ptr(self.workspace), nbytes), "dq_plan_bind")

@@ -72,11 +72,28 @@ typedef enum dq_rounding {
     DQ_ROUND_INDEPENDENT = 1   /* an independent dither per quantisation event */
 } dq_rounding;
 
+/* Allocation variants.  The method thresholds F_j, the squared norm before
+ * the mean is subtracted (pith.science review, "What carries the argument").
+ * The review's referee (major 1) notes that the quantised values have squared
+ * norm F_j - n S mu_j^2 (S = 256), and cites the paper's Table 6 comparison
+ * with uniform widths; both are offered for measurement:
+ *   DQ_ALLOC_MEAN_CORRECTED  thresholds on G_j = max(fl(F_j - fl(fl(256 n) *
+ *                            fl(mu_j * mu_j))), 0), same budget and search
+ *   DQ_ALLOC_UNIFORM         every super-group at the widest q in {2,4,8}
+ *                            with q <= avg_bits; rho is reported as NaN */
+typedef enum dq_alloc {
+    DQ_ALLOC_THRESHOLD = 0,
+    DQ_ALLOC_MEAN_CORRECTED = 1,
+    DQ_ALLOC_UNIFORM = 2
+} dq_alloc;
+
 typedef enum dq_option {
     DQ_OPT_SEED = 0,       /* 64-bit Philox key (default 1) */
     DQ_OPT_ROUND = 1,      /* round index, 32-bit, part of every Philox counter (default 0) */
     DQ_OPT_ROUNDING = 2,   /* dq_rounding (default DQ_ROUND_CORRELATED) */
-    DQ_OPT_TIMING = 3      /* 1: time every launch with HIP events on its stream */
+    DQ_OPT_TIMING = 3,     /* 1: time every launch with HIP events on its stream */
+    DQ_OPT_ALLOC = 4       /* dq_alloc (default DQ_ALLOC_THRESHOLD); takes effect at the
+                              next dq_allocate */
 } dq_option;
 
 typedef struct dq_plan dq_plan;

@@ -74,6 +74,9 @@ def test_options(lib):
     assert lib.dq_plan_set_u64(h, dq.OPT_ROUND, 2 ** 32) == dq.DQ_EINVAL
     assert lib.dq_plan_set_u64(h, dq.OPT_ROUNDING, 2) == dq.DQ_EINVAL
     assert lib.dq_plan_set_u64(h, dq.OPT_TIMING, 3) == dq.DQ_EINVAL
+    for mode in (dq.ALLOC_THRESHOLD, dq.ALLOC_MEAN_CORRECTED, dq.ALLOC_UNIFORM):
+        assert lib.dq_plan_set_u64(h, dq.OPT_ALLOC, mode) == dq.DQ_OK
+    assert lib.dq_plan_set_u64(h, dq.OPT_ALLOC, 3) == dq.DQ_EINVAL
     assert lib.dq_plan_set_u64(h, 99, 0) == dq.DQ_EINVAL
     assert lib.dq_plan_set_u64(None, 0, 0) == dq.DQ_ENULL
     lib.dq_plan_destroy(h)

@@ -75,14 +75,17 @@ class Round:
     """Drives the same schedule on the GPU and on the oracle, keeping every
     region both produce (fresh zeroed buffers per step)."""
 
-    def __init__(self, grads, topo, budget=5.0, seed=1, rnd=0, rounding=dq.CORRELATED):
+    def __init__(self, grads, topo, budget=5.0, seed=1, rnd=0, rounding=dq.CORRELATED,
+                 alloc=dq.ALLOC_THRESHOLD):
         self.grads = grads
         self.gnp = _grads_np(grads)
         self.n = len(grads)
         self.d = grads[0].numel()
         self.topo = topo
-        self.plan = dq.Plan(self.d, self.n, topo, budget, seed=seed, rnd=rnd, rounding=rounding)
-        self.orc = po.Oracle(self.d, self.n, topo, budget, seed=seed, rnd=rnd, rounding=rounding)
+        self.plan = dq.Plan(self.d, self.n, topo, budget, seed=seed, rnd=rnd, rounding=rounding,
+                            alloc=alloc)
+        self.orc = po.Oracle(self.d, self.n, topo, budget, seed=seed, rnd=rnd, rounding=rounding,
+                             alloc=alloc)
 
     def stages(self):
         for w in range(self.n):
@@ -223,6 +226,37 @@ def test_llama_shape_budget_sweep(budget):
     grads = _scaled("llama", 1537)
     r, info, out = full_round(grads, dq.RING, budget=budget)
     assert info["used_bits"] <= budget * r.plan.J
+
+
+def _with_offsets(grads, seed=5):
+    """Add a per-SG offset, the same on every worker, to a third of the SGs, of
+    the size of the SG's spread: the mean-corrected key then differs from F."""
+    J = grads[0].numel() // 256
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    spread = torch.stack([g.float().view(J, 256).abs().amax(1) for g in grads]).amax(0).cpu()
+    pick = (torch.rand(J, generator=gen) < 1 / 3).float()
+    off = (pick * spread * (2 * torch.rand(J, generator=gen) - 1) * 4).to(DEV)
+    return [(g.float().view(J, 256) + off[:, None]).view(-1).to(g.dtype) for g in grads]
+
+
+@pytest.mark.parametrize("alloc,budget,topo", [
+    (dq.ALLOC_MEAN_CORRECTED, 5.0, dq.RING), (dq.ALLOC_MEAN_CORRECTED, 3.0, dq.BUTTERFLY),
+    (dq.ALLOC_UNIFORM, 5.0, dq.RING), (dq.ALLOC_UNIFORM, 2.0, dq.BUTTERFLY),
+    (dq.ALLOC_UNIFORM, 8.0, dq.RING)])
+def test_allocation_variants_bit_exact(alloc, budget, topo):
+    """The variants of the allocation (mean-corrected key, uniform widths)
+    through every stage of a round, against the oracle."""
+    _need_gpu()
+    grads = _with_offsets(_scaled("llama" if topo == dq.RING else "gemma", 1031, workers=range(8)))
+    r, info, out = full_round(grads, topo, budget=budget, alloc=alloc)
+    if alloc == dq.ALLOC_UNIFORM:
+        q = 8 if budget >= 8 else (4 if budget >= 4 else 2)
+        assert info["class_counts"][{2: 0, 4: 1, 8: 2}[q]] == r.plan.J
+        assert info["rho_bits"] == 0x7FC00000
+    else:
+        plain = Round(grads, topo, budget=budget)
+        plain.stages()
+        assert not np.array_equal(plain.plan.widths().cpu().numpy(), r.plan.widths().cpu().numpy())
 
 
 @pytest.mark.parametrize("n,topo", [(1, dq.RING), (1, dq.BUTTERFLY), (2, dq.RING), (2, dq.BUTTERFLY),
