@@ -852,29 +852,39 @@ void or_roundtrip_batch(const float *y, int64_t K, int32_t q, const uint16_t *di
 }
 
 /* ------------------------------------------------------------------ */
-/* MXFP8 reference quantiser (OCP Microscaling Formats v1.0; the pages     */
-/* cite it as a baseline).  Blocks of 32 consecutive values share an E8M0  */
-/* scale X = 2^(floor(log2 max|v|) - 8) (8 = exponent of the largest E4M3  */
-/* normal, 448), clamped to [2^-127, 2^127]; each v / X is rounded to      */
-/* nearest-even on the E4M3 grid (3 mantissa bits, normals from 2^-6,      */
-/* subnormal quantum 2^-9) and saturated at +-448.                         */
+/* MX reference quantisers (OCP Microscaling Formats v1.0; the pages cite  */
+/* MXFP8 as a baseline and MXFP4/6 as estimated baselines: pith.science    */
+/* review, referee major 3).  Blocks of 32 consecutive values share an     */
+/* E8M0 scale X = 2^(floor(log2 max|v|) - emax), emax = exponent of the    */
+/* element format's largest normal, clamped to [2^-127, 2^127]; each v / X */
+/* is rounded to nearest-even on the element grid (mbits mantissa bits,    */
+/* normals from 2^emin, subnormal quantum 2^(emin - mbits)) and saturated  */
+/* at the largest finite element value.                                    */
+/*   E4M3 (FP8): mbits 3, emin -6, emax 8, max 448                         */
+/*   E3M2 (FP6): mbits 2, emin -2, emax 4, max 28                          */
+/*   E2M3 (FP6): mbits 3, emin  0, emax 2, max 7.5                         */
+/*   E2M1 (FP4): mbits 1, emin  0, emax 2, max 6                           */
 /* ------------------------------------------------------------------ */
 
-static double e4m3_round(double v) {
+typedef struct { int mbits, emin, emax; double max; } mx_elem;
+static const mx_elem MX_ELEM[4] = {{3, -6, 8, 448.0}, {2, -2, 4, 28.0}, {3, 0, 2, 7.5}, {1, 0, 2, 6.0}};
+
+static double mx_elem_round(const mx_elem *f, double v) {
     double a = fabs(v);
-    if (a >= 448.0) return v < 0 ? -448.0 : 448.0;
+    if (a >= f->max) return v < 0 ? -f->max : f->max;
     if (a == 0.0) return 0.0;
     int e;
     frexp(a, &e);               /* a = f * 2^e, f in [0.5, 1) -> floor(log2 a) = e - 1 */
     int ex = e - 1;
-    if (ex < -6) ex = -6;
-    double quantum = ldexp(1.0, ex - 3);
+    if (ex < f->emin) ex = f->emin;
+    double quantum = ldexp(1.0, ex - f->mbits);
     double r = nearbyint(a / quantum) * quantum;
-    if (r > 448.0) r = 448.0;
+    if (r > f->max) r = f->max;
     return v < 0 ? -r : r;
 }
 
-void or_mxfp8_roundtrip(const float *x, int64_t n, float *out) {
+void or_mx_roundtrip(int32_t fmt, const float *x, int64_t n, float *out) {
+    const mx_elem *f = &MX_ELEM[fmt];
 #pragma omp parallel for schedule(static)
     for (int64_t b = 0; b < (n + 31) / 32; b++) {
         int64_t lo = b * 32, hi = lo + 32 < n ? lo + 32 : n;
@@ -887,21 +897,24 @@ void or_mxfp8_roundtrip(const float *x, int64_t n, float *out) {
         if (amax > 0.0) {
             int e;
             frexp(amax, &e);
-            se = (e - 1) - 8;
+            se = (e - 1) - f->emax;
             if (se < -127) se = -127;
             if (se > 127) se = 127;
         }
         double X = ldexp(1.0, se);
-        for (int64_t i = lo; i < hi; i++) out[i] = (float)(e4m3_round((double)x[i] / X) * X);
+        for (int64_t i = lo; i < hi; i++) out[i] = (float)(mx_elem_round(f, (double)x[i] / X) * X);
     }
 }
 
+void or_mxfp8_roundtrip(const float *x, int64_t n, float *out) { or_mx_roundtrip(OR_MX_E4M3, x, n, out); }
+
 /* ------------------------------------------------------------------ */
-/* MXFP8 in the same schedule (reading: the pages compare DynamiQ with    */
-/* MXFP8 all-reduce, scribe notes "Evaluation").  No mean subtraction and */
-/* no reorder: part c of m is super-groups [floor(cJ/m), floor((c+1)J/m)) */
-/* of the original order.  Every compress and hop re-encodes in MXFP8; a  */
-/* hop adds the decoded incoming values and the local values in fp32.     */
+/* MX codecs in the same schedule (reading: the pages compare DynamiQ     */
+/* with MX all-reduce, scribe notes "Evaluation").  No mean subtraction   */
+/* and no reorder: part c of m is super-groups [floor(cJ/m),              */
+/* floor((c+1)J/m)) of the original order.  Every compress and hop        */
+/* re-encodes; a hop adds the decoded incoming values and the local       */
+/* values in fp32.                                                        */
 /* Regions are kept as their decoded fp32 values (decoding is exact).     */
 /* ------------------------------------------------------------------ */
 
@@ -910,13 +923,14 @@ static void mx_part(const or_ctx *c, int64_t m, int64_t part, int64_t *lo, int64
     *hi = (part + 1) * c->J / m * OR_SG;
 }
 
-int or_mxfp8_allreduce(or_ctx *c, const void *const *grads, int32_t dtype, float *out) {
+int or_mx_allreduce(or_ctx *c, int32_t fmt, const void *const *grads, int32_t dtype, float *out) {
+    if (fmt < 0 || fmt > 3) return -1;
     const int n = c->n;
     const int64_t d = c->d;
     float *tmp = (float *)malloc((size_t)d * sizeof(float));
     if (n == 1) {
         for (int64_t i = 0; i < d; i++) tmp[i] = load_elem(grads[0], dtype, i);
-        or_mxfp8_roundtrip(tmp, d, out);
+        or_mx_roundtrip(fmt, tmp, d, out);
         free(tmp);
         return 0;
     }
@@ -933,14 +947,14 @@ int or_mxfp8_allreduce(or_ctx *c, const void *const *grads, int32_t dtype, float
         for (int w = 0; w < n; w++) {
             mx_part(c, n, w, &lo, &hi);
             for (int64_t i = lo; i < hi; i++) tmp[i] = load_elem(grads[w], dtype, i);
-            or_mxfp8_roundtrip(tmp + lo, hi - lo, cur[w] + lo);
+            or_mx_roundtrip(fmt, tmp + lo, hi - lo, cur[w] + lo);
         }
         for (int t = 1; t < n; t++) {
             for (int w = 0; w < n; w++) {
                 const int src = (w - 1 + n) % n;
                 mx_part(c, n, ((int64_t)w - t % n + n) % n, &lo, &hi);
                 for (int64_t i = lo; i < hi; i++) tmp[i] = cur[src][i] + load_elem(grads[w], dtype, i);
-                or_mxfp8_roundtrip(tmp + lo, hi - lo, nxt[w] + lo);
+                or_mx_roundtrip(fmt, tmp + lo, hi - lo, nxt[w] + lo);
             }
             float **sw = cur; cur = nxt; nxt = sw;
         }
@@ -954,7 +968,7 @@ int or_mxfp8_allreduce(or_ctx *c, const void *const *grads, int32_t dtype, float
         for (int w = 0; w < n; w++) {
             mx_part(c, 2, ((int64_t)w >> (L - 1)) ^ 1, &lo, &hi);
             for (int64_t i = lo; i < hi; i++) tmp[i] = load_elem(grads[w], dtype, i);
-            or_mxfp8_roundtrip(tmp + lo, hi - lo, nxt[w] + lo);   /* nxt = sent halves */
+            or_mx_roundtrip(fmt, tmp + lo, hi - lo, nxt[w] + lo);   /* nxt = sent halves */
         }
         for (int s = 1; s <= L; s++) {
             for (int w = 0; w < n; w++) {
@@ -966,7 +980,7 @@ int or_mxfp8_allreduce(or_ctx *c, const void *const *grads, int32_t dtype, float
                     tmp[i] = in + own;
                 }
                 /* write into a scratch then swap after all workers of the level */
-                or_mxfp8_roundtrip(tmp + lo, hi - lo, (s == 1 ? cur[w] : nxt[w]) + lo);
+                or_mx_roundtrip(fmt, tmp + lo, hi - lo, (s == 1 ? cur[w] : nxt[w]) + lo);
             }
             if (s > 1) {
                 for (int w = 0; w < n; w++) {
@@ -983,4 +997,8 @@ int or_mxfp8_allreduce(or_ctx *c, const void *const *grads, int32_t dtype, float
     for (int w = 0; w < n; w++) { free(cur[w]); free(nxt[w]); }
     free(cur); free(nxt); free(tmp);
     return 0;
+}
+
+int or_mxfp8_allreduce(or_ctx *c, const void *const *grads, int32_t dtype, float *out) {
+    return or_mx_allreduce(c, OR_MX_E4M3, grads, dtype, out);
 }

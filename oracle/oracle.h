@@ -132,11 +132,15 @@ void or_dithers(uint64_t seed, uint32_t round, int64_t j, int32_t mode,
                 int32_t worker, int32_t n_workers, int32_t event,
                 uint16_t *d);
 
-/* MXFP8 (OCP MX v1.0: block 32, E8M0 shared scale, E4M3 elements). */
+/* MX formats (OCP MX v1.0: block 32, E8M0 shared scale; elements FP8 E4M3,
+ * FP6 E3M2 or E2M3, FP4 E2M1).  The mxfp8 names are the E4M3 case. */
+enum { OR_MX_E4M3 = 0, OR_MX_E3M2 = 1, OR_MX_E2M3 = 2, OR_MX_E2M1 = 3 };
+void or_mx_roundtrip(int32_t fmt, const float *x, int64_t n, float *out);
 void or_mxfp8_roundtrip(const float *x, int64_t n, float *out);
-/* The schedule of the context with MXFP8 re-encoding at every hop, on parts of
+/* The schedule of the context with MX re-encoding at every hop, on parts of
  * the original order; out = the decoded all-reduced sum. */
 int or_mxfp8_allreduce(or_ctx *c, const void *const *grads, int32_t dtype, float *out);
+int or_mx_allreduce(or_ctx *c, int32_t fmt, const void *const *grads, int32_t dtype, float *out);
 
 #ifdef __cplusplus
 }

@@ -62,6 +62,8 @@ def lib():
             "or_roundtrip_batch": (None, [vp, i64, i32, vp, f64, vp]),
             "or_dithers": (None, [u64, u32, i64, i32, i32, i32, i32, vp]),
             "or_mxfp8_roundtrip": (None, [vp, i64, vp]),
+            "or_mx_roundtrip": (None, [i32, vp, i64, vp]),
+            "or_mx_allreduce": (C.c_int, [vp, i32, vp, i32, vp]),
             "or_mxfp8_allreduce": (C.c_int, [vp, vp, i32, vp]),
         }
         for name, (res, args) in sig.items():
@@ -137,10 +139,20 @@ def roundtrip_batch(y, q, dither, eps=0.5):
     return out
 
 
+MX_E4M3, MX_E3M2, MX_E2M3, MX_E2M1 = 0, 1, 2, 3
+
+
 def mxfp8_roundtrip(x):
     x = np.ascontiguousarray(x, dtype=np.float32)
     out = np.zeros_like(x)
     lib().or_mxfp8_roundtrip(_p(x), x.size, _p(out))
+    return out
+
+
+def mx_roundtrip(fmt, x):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.zeros_like(x)
+    lib().or_mx_roundtrip(int(fmt), _p(x), x.size, _p(out))
     return out
 
 
@@ -263,6 +275,13 @@ class Oracle:
         ptrs = (C.c_void_p * self.n)(*[g.ctypes.data for g in grads])
         out = np.zeros(self.d, np.float32)
         _check(lib().or_mxfp8_allreduce(self.h, ptrs, _dtype_code(grads[0]), _p(out)), "mxfp8_allreduce")
+        return out
+
+    def mx_allreduce(self, fmt, grads):
+        grads = [np.ascontiguousarray(g) for g in grads]
+        ptrs = (C.c_void_p * self.n)(*[g.ctypes.data for g in grads])
+        out = np.zeros(self.d, np.float32)
+        _check(lib().or_mx_allreduce(self.h, int(fmt), ptrs, _dtype_code(grads[0]), _p(out)), "mx_allreduce")
         return out
 
     def allreduce(self, grads):

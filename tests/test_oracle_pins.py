@@ -864,3 +864,86 @@ def test_variable_widths_beat_uniform_unless_shuffled():
     assert local_ratio > 2.0
     assert shuffled_ratio < 1.5
     assert shuffled_ratio < local_ratio / 2
+
+
+# ---------------------------------------------------------------------------
+# MX element formats (OCP Microscaling v1.0), pinned by brute force: every
+# element value enumerated from the format's (E, M) fields, nearest value
+# with ties to the even code, saturation at the largest finite value
+# ---------------------------------------------------------------------------
+
+MX_FORMATS = {  # fmt: (ebits, mbits, emin, emax, max)
+    po.MX_E4M3: (4, 3, -6, 8, 448.0),
+    po.MX_E3M2: (3, 2, -2, 4, 28.0),
+    po.MX_E2M3: (2, 3, 0, 2, 7.5),
+    po.MX_E2M1: (2, 1, 0, 2, 6.0),
+}
+
+
+def _mx_values(fmt):
+    ebits, mbits, emin, emax, vmax = MX_FORMATS[fmt]
+    vals = []
+    for E in range(2 ** ebits):
+        for M in range(2 ** mbits):
+            v = M * 2.0 ** (emin - mbits) if E == 0 else (1 + M / 2 ** mbits) * 2.0 ** (E - 1 + emin)
+            if v <= vmax:
+                vals.append(v)
+    vals = np.array(vals)
+    assert np.all(np.diff(vals) > 0) and vals[-1] == vmax
+    assert np.floor(np.log2(vmax)) == emax
+    return vals
+
+
+def _mx_brute(fmt, x):
+    vals = _mx_values(fmt)
+    emax, vmax = MX_FORMATS[fmt][3], MX_FORMATS[fmt][4]
+    out = np.zeros_like(x)
+    for b in range(0, x.size, 32):
+        blk = x[b:b + 32].astype(np.float64)
+        amax = np.abs(blk).max()
+        se = -127 if amax == 0 else int(np.clip(np.floor(np.log2(amax)) - emax, -127, 127))
+        X = 2.0 ** se
+        for i, v in enumerate(blk / X):
+            a = abs(v)
+            if a >= vmax:
+                r = vmax
+            else:
+                k = np.searchsorted(vals, a)          # vals[k-1] < a <= vals[k]
+                lo, hi = vals[max(k - 1, 0)], vals[min(k, len(vals) - 1)]
+                if a - lo < hi - a:
+                    r = lo
+                elif hi - a < a - lo:
+                    r = hi
+                else:                                 # tie: the even code
+                    r = lo if (k - 1) % 2 == 0 else hi
+            out[b + i] = np.float32((-r if v < 0 else r) * X)
+    return out
+
+
+@pytest.mark.parametrize("fmt", [po.MX_E4M3, po.MX_E3M2, po.MX_E2M3, po.MX_E2M1])
+def test_mx_quantiser_brute_force(fmt):
+    rng = np.random.default_rng(31 + fmt)
+    nb = 300
+    x = (rng.standard_normal(32 * nb) * np.repeat(10.0 ** rng.uniform(-6, 3, nb), 32)).astype(np.float32)
+    # ties and exact values: blocks built from element values and midpoints
+    vals = _mx_values(fmt)
+    mids = (vals[:-1] + vals[1:]) / 2
+    for b in range(0, 60):
+        pick = np.concatenate([vals, mids])[rng.integers(0, 2 * len(vals) - 1, 32)]
+        pick[0] = vals[-1]                            # block max at the top value: scale 2^0
+        x[32 * b:32 * b + 32] = (pick * np.where(rng.random(32) < 0.5, -1, 1)).astype(np.float32)
+    x[32 * 60:32 * 61] = 0.0                          # an all-zero block
+    assert np.array_equal(po.mx_roundtrip(fmt, x), _mx_brute(fmt, x))
+    if fmt == po.MX_E4M3:
+        assert np.array_equal(po.mxfp8_roundtrip(x), po.mx_roundtrip(fmt, x))
+
+
+def test_mx_schedule_composition_fp4():
+    rng = np.random.default_rng(18)
+    J = 12
+    g = [(rng.standard_normal(256 * J) * np.repeat(10.0 ** rng.uniform(-4, 0, J), 256)).astype(np.float32)
+         for _ in range(2)]
+    h = 256 * (J // 2)
+    q = lambda v: po.mx_roundtrip(po.MX_E2M1, v)
+    out = po.Oracle(256 * J, 2, po.RING).mx_allreduce(po.MX_E2M1, g)
+    assert np.array_equal(out, np.concatenate([q(q(g[0][:h]) + g[1][:h]), q(q(g[1][h:]) + g[0][h:])]))
