@@ -199,11 +199,40 @@ def main():
         del p_ind
         mx_arena = torch.empty(int(dq.lib().dq_mxfp8_arena_bytes(plan.h)), dtype=torch.uint8, device=dev)
         v_mx = vnmse(plan.mxfp8_allreduce(grads, out=torch.empty_like(out), arena=mx_arena))
+        v_mx6a = vnmse(plan.mx_allreduce(dq.MX_FP6_E3M2, grads, out=torch.empty_like(out), arena=mx_arena))
+        v_mx6b = vnmse(plan.mx_allreduce(dq.MX_FP6_E2M3, grads, out=torch.empty_like(out), arena=mx_arena))
+        v_mx4 = vnmse(plan.mx_allreduce(dq.MX_FP4_E2M1, grads, out=torch.empty_like(out), arena=mx_arena))
         del mx_arena
+
+        def variant(gs, bits, alloc, ref):
+            p = dq.Plan(wl.d, wl.n, topo, bits, seed=wl.rounding_seed, alloc=alloc, device=dev)
+            a = torch.empty(p.arena_bytes(), dtype=torch.uint8, device=dev)
+            o = p.allreduce(gs, out=torch.empty_like(out), arena=a)
+            return ((o.double() - ref) ** 2).sum().item() / norm
+
+        # allocation variants: the mean-corrected key at the same budget;
+        # variable against uniform widths at 4 bits (Table 6's comparison), on
+        # the gradients and after one random coordinate shuffle shared by all
+        # workers (the spatial-locality premise, Fig. 1)
+        v_mc = variant(grads, budget, dq.ALLOC_MEAN_CORRECTED, exact)
+        v_var4 = variant(grads, 4.0, dq.ALLOC_THRESHOLD, exact)
+        v_uni4 = variant(grads, 4.0, dq.ALLOC_UNIFORM, exact)
+        gen = torch.Generator(device=dev).manual_seed(12345)
+        perm = torch.randperm(wl.d, device=dev, generator=gen)
+        shuffled = [g[perm] for g in grads]
+        exact_s = exact[perm]
+        del perm
+        v_var4_s = variant(shuffled, 4.0, dq.ALLOC_THRESHOLD, exact_s)
+        v_uni4_s = variant(shuffled, 4.0, dq.ALLOC_UNIFORM, exact_s)
+        del shuffled, exact_s
         quality = {"vnmse_correlated": v_corr, "vnmse_independent": v_ind, "vnmse_mxfp8": v_mx,
                    "mxfp8_over_dynamiq": v_mx / v_corr, "achieved_bits": b,
                    "wire_bits_per_coord": b + 0.625, "mxfp8_wire_bits_per_coord": 8.25,
-                   "stats_traffic_ratio": 8.0 / (256 * 2), "class_counts": info["class_counts"]}
+                   "stats_traffic_ratio": 8.0 / (256 * 2), "class_counts": info["class_counts"],
+                   "vnmse_mxfp6_e3m2": v_mx6a, "vnmse_mxfp6_e2m3": v_mx6b, "vnmse_mxfp4_e2m1": v_mx4,
+                   "vnmse_mean_corrected_alloc": v_mc,
+                   "vnmse_4bit_variable": v_var4, "vnmse_4bit_uniform": v_uni4,
+                   "vnmse_4bit_variable_shuffled": v_var4_s, "vnmse_4bit_uniform_shuffled": v_uni4_s}
         del exact
 
     # achievable HBM rate on this machine: a plain 1 GiB device-to-device copy

@@ -644,7 +644,7 @@ dq_status dq_timing_read(dq_plan *p, dq_timing *out) {
 
 }  // extern "C"
 
-// ---- MXFP8 reference in the same schedule (quality report) ---------------------
+// ---- MX reference codecs in the same schedule (quality report) ----------------
 
 namespace {
 
@@ -659,10 +659,10 @@ size_t mx_region_max(const dq_plan *p, int64_t m) {
     return align_up(coords + coords / 32, kAlign);
 }
 
-dq_status mx_launch(dq_plan *p, int mode, int local, const void *grad, const uint8_t *in,
+dq_status mx_launch(dq_plan *p, int fmt, int mode, int local, const void *grad, const uint8_t *in,
                     const uint8_t *own, int64_t in_m, int64_t in_c, uint8_t *out, float *out_f32,
                     int64_t m, int64_t c, hipStream_t s) {
-    Mxfp8Args a;
+    MxArgs a;
     std::memset(&a, 0, sizeof(a));
     a.grad = grad;
     a.in = in;
@@ -674,7 +674,7 @@ dq_status mx_launch(dq_plan *p, int mode, int local, const void *grad, const uin
     a.mode = mode;
     Launch L;
     hipError_t e = timed_begin(p, DQ_K_MXFP8, 0, 0, s, L);
-    if (e == hipSuccess && a.n > 0) e = launch_mxfp8(a, local, s);
+    if (e == hipSuccess && a.n > 0) e = launch_mx(a, fmt, local, s);
     if (e == hipSuccess) e = timed_end(p, L, s);
     return hip_status(e);
 }
@@ -692,9 +692,13 @@ size_t dq_mxfp8_arena_bytes(const dq_plan *p) {
     return (size_t)p->n * per_w;
 }
 
-dq_status dq_mxfp8_allreduce(dq_plan *p, const void *const *grads, int32_t kind, void *arena,
-                             size_t arena_bytes, float *out, void *stream) {
+size_t dq_mx_arena_bytes(const dq_plan *p) { return dq_mxfp8_arena_bytes(p); }
+
+dq_status dq_mx_allreduce(dq_plan *p, int32_t format, const void *const *grads, int32_t kind, void *arena,
+                          size_t arena_bytes, float *out, void *stream) {
     if (!p || !grads || !arena || !out) return DQ_ENULL;
+    if (format < DQ_MX_FP8_E4M3 || format > DQ_MX_FP4_E2M1) return DQ_EINVAL;
+    const int f = format;
     if (kind != DQ_BF16 && kind != DQ_F32) return DQ_EINVAL;
     if (arena_bytes < dq_mxfp8_arena_bytes(p) || !aligned(arena, kAlign)) return DQ_EWORKSPACE;
     for (int w = 0; w < p->n; w++)
@@ -704,26 +708,26 @@ dq_status dq_mxfp8_allreduce(dq_plan *p, const void *const *grads, int32_t kind,
     const int n = p->n, lk = local_of_kind(kind);
     dq_status st;
     if (n == 1) {
-        if ((st = mx_launch(p, kCompress, lk, grads[0], nullptr, nullptr, 1, 0, A, nullptr, 1, 0, s)))
+        if ((st = mx_launch(p, f, kCompress, lk, grads[0], nullptr, nullptr, 1, 0, A, nullptr, 1, 0, s)))
             return st;
-        return mx_launch(p, kFinalize, kLocalNone, nullptr, A, nullptr, 1, 0, nullptr, out, 1, 0, s);
+        return mx_launch(p, f, kFinalize, kLocalNone, nullptr, A, nullptr, 1, 0, nullptr, out, 1, 0, s);
     }
     if (p->topo == DQ_RING) {
         const size_t R = mx_region_max(p, n);
         auto slot = [&](int w, int t) { return A + ((size_t)(t & 1) * n + w) * R; };
         for (int w = 0; w < n; w++)
-            if ((st = mx_launch(p, kCompress, lk, grads[w], nullptr, nullptr, n, w, slot(w, 0), nullptr,
+            if ((st = mx_launch(p, f, kCompress, lk, grads[w], nullptr, nullptr, n, w, slot(w, 0), nullptr,
                                 n, w, s)))
                 return st;
         for (int t = 1; t < n; t++)
             for (int w = 0; w < n; w++) {
                 const int64_t c = ((int64_t)w - t % n + n) % n;
-                if ((st = mx_launch(p, kHop, lk, grads[w], slot((w - 1 + n) % n, t - 1), nullptr, n, c,
+                if ((st = mx_launch(p, f, kHop, lk, grads[w], slot((w - 1 + n) % n, t - 1), nullptr, n, c,
                                     slot(w, t), nullptr, n, c, s)))
                     return st;
             }
         for (int w = 0; w < n; w++)
-            if ((st = mx_launch(p, kFinalize, kLocalNone, nullptr, slot(w, n - 1), nullptr, n, (w + 1) % n,
+            if ((st = mx_launch(p, f, kFinalize, kLocalNone, nullptr, slot(w, n - 1), nullptr, n, (w + 1) % n,
                                 nullptr, out, n, (w + 1) % n, s)))
                 return st;
         return DQ_OK;
@@ -742,7 +746,7 @@ dq_status dq_mxfp8_allreduce(dq_plan *p, const void *const *grads, int32_t kind,
     auto slot = [&](int w, int l) { return A + off[(size_t)w * (L + 1) + l]; };   // l = 0: compress
     for (int w = 0; w < n; w++) {
         const int64_t c = ((int64_t)w >> (L - 1)) ^ 1;
-        if ((st = mx_launch(p, kCompress, lk, grads[w], nullptr, nullptr, 2, c, slot(w, 0), nullptr, 2, c, s)))
+        if ((st = mx_launch(p, f, kCompress, lk, grads[w], nullptr, nullptr, 2, c, slot(w, 0), nullptr, 2, c, s)))
             return st;
     }
     for (int l = 1; l <= L; l++)
@@ -750,20 +754,25 @@ dq_status dq_mxfp8_allreduce(dq_plan *p, const void *const *grads, int32_t kind,
             const int partner = w ^ (n >> l);
             const int64_t m = (int64_t)1 << l, c = (int64_t)w >> (L - l);
             if (l == 1) {
-                if ((st = mx_launch(p, kHop, lk, grads[w], slot(partner, 0), nullptr, m, c, slot(w, 1),
+                if ((st = mx_launch(p, f, kHop, lk, grads[w], slot(partner, 0), nullptr, m, c, slot(w, 1),
                                     nullptr, m, c, s)))
                     return st;
             } else {
                 // partner's and own level l-1 regions cover part c >> 1 of m / 2
-                if ((st = mx_launch(p, kHop, kLocalPacked, nullptr, slot(partner, l - 1), slot(w, l - 1),
+                if ((st = mx_launch(p, f, kHop, kLocalPacked, nullptr, slot(partner, l - 1), slot(w, l - 1),
                                     m / 2, c >> 1, slot(w, l), nullptr, m, c, s)))
                     return st;
             }
         }
     for (int w = 0; w < n; w++)
-        if ((st = mx_launch(p, kFinalize, kLocalNone, nullptr, slot(w, L), nullptr, n, w, nullptr, out, n, w, s)))
+        if ((st = mx_launch(p, f, kFinalize, kLocalNone, nullptr, slot(w, L), nullptr, n, w, nullptr, out, n, w, s)))
             return st;
     return DQ_OK;
+}
+
+dq_status dq_mxfp8_allreduce(dq_plan *p, const void *const *grads, int32_t kind, void *arena,
+                             size_t arena_bytes, float *out, void *stream) {
+    return dq_mx_allreduce(p, DQ_MX_FP8_E4M3, grads, kind, arena, arena_bytes, out, stream);
 }
 
 }  // extern "C"

@@ -99,9 +99,10 @@ struct ReorderArgs {
     float *mu_stream;
 };
 
-// MXFP8 reference codec (quality report only).  Regions hold one E4M3 byte per
-// coordinate of the part, then one E8M0 scale byte per 32 coordinates.
-struct Mxfp8Args {
+// MX reference codecs (quality report only).  Regions hold one element code
+// byte per coordinate of the part, then one E8M0 scale byte per 32 coordinates.
+enum MxFormat { kMxE4M3 = 0, kMxE3M2 = 1, kMxE2M3 = 2, kMxE2M1 = 3 };
+struct MxArgs {
     const void *grad;          // local gradient (original order), or nullptr
     int32_t grad_f32;
     const uint8_t *in;         // incoming region (hop / finalize), part [in_lo, in_lo + in_n)
@@ -126,6 +127,6 @@ int32_t part_table_entries(int32_t n, int32_t topology);
 int32_t part_table_index(int32_t n, int32_t topology, int64_t m, int64_t c);
 hipError_t launch_part_table(const unsigned long long *class_counts, int32_t n, int32_t topology,
                              PartInfo *table, hipStream_t s);
-hipError_t launch_mxfp8(const Mxfp8Args &a, int local, hipStream_t s);
+hipError_t launch_mx(const MxArgs &a, int fmt, int local, hipStream_t s);
 
 }  // namespace dq

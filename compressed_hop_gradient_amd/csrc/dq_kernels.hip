@@ -903,26 +903,64 @@ __device__ __forceinline__ int floor_log2(float a) {   // a > 0
     return (31 - __clz(b)) - 149;                      // subnormal
 }
 
-// E4M3 code of v (v already divided by the block scale)
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+// MX element formats (OCP Microscaling v1.0): mantissa bits, exponent of the
+// smallest normal and of the largest normal, largest finite value, sign bit,
+// and the code of the largest finite value.  Codes are stored one per byte.
+template <int FMT> struct MxElem;
+template <> struct MxElem<kMxE4M3> {
+    static constexpr int kM = 3, kEmin = -6, kEmax = 8, kSign = 7;
+    static constexpr float kMax = 448.0f;
+};
+template <> struct MxElem<kMxE3M2> {
+    static constexpr int kM = 2, kEmin = -2, kEmax = 4, kSign = 5;
+    static constexpr float kMax = 28.0f;
+};
+template <> struct MxElem<kMxE2M3> {
+    static constexpr int kM = 3, kEmin = 0, kEmax = 2, kSign = 5;
+    static constexpr float kMax = 7.5f;
+};
+template <> struct MxElem<kMxE2M1> {
+    static constexpr int kM = 1, kEmin = 0, kEmax = 2, kSign = 3;
+    static constexpr float kMax = 6.0f;
+};
+
+// magnitude code of a value a on the element grid: ((ex - emin) << M) + q
+// with ex = max(floor(log2 a), emin) and q = a 2^(M - ex) rounded to nearest
+// even (a carry into the next binade is the next code)
+template <int FMT>
+__host__ __device__ constexpr uint32_t mx_max_code() {
+    using F = MxElem<FMT>;
+    return (uint32_t)(((F::kEmax - F::kEmin) << F::kM) +
+                      (int)(F::kMax / (float)(1 << F::kEmax) * (float)(1 << F::kM)));
+}
+static_assert(mx_max_code<kMxE4M3>() == 0x7Eu && mx_max_code<kMxE3M2>() == 0x1Fu &&
+              mx_max_code<kMxE2M3>() == 0x1Fu && mx_max_code<kMxE2M1>() == 0x7u, "MX max codes");
+
+// element code of v (v already divided by the block scale)
+template <int FMT>
+__device__ __forceinline__ uint32_t mx_encode(float v) {
+    using F = MxElem<FMT>;
     const float a = fabsf(v);
     if (a == 0.0f) return 0u;
-    const uint32_t sign = (__float_as_uint(v) >> 31) << 7;
-    if (a >= 448.0f) return sign | 0x7Eu;
-    const int ex = max(floor_log2(a), -6);
-    const uint32_t q = (uint32_t)rintf(a * ldexpf(1.0f, 3 - ex));   // exact scaling, nearest even
-    return sign | ((uint32_t)((ex + 6) << 3) + q);
+    const uint32_t sign = (__float_as_uint(v) >> 31) << F::kSign;
+    if (a >= F::kMax) return sign | mx_max_code<FMT>();
+    const int ex = max(floor_log2(a), F::kEmin);
+    const uint32_t q = (uint32_t)rintf(a * ldexpf(1.0f, F::kM - ex));   // exact scaling, nearest even
+    return sign | ((uint32_t)((ex - F::kEmin) << F::kM) + q);
 }
 
-__device__ __forceinline__ float e4m3_decode(uint32_t code, int se) {
-    const uint32_t mag = code & 0x7Fu, E = mag >> 3, M = mag & 7u;
-    const float m = (float)(E ? 8u + M : M);
-    float v = ldexpf(m, (int)(E ? E : 1u) - 10 + se);
-    return (code & 0x80u) ? -v : v;
+template <int FMT>
+__device__ __forceinline__ float mx_decode(uint32_t code, int se) {
+    using F = MxElem<FMT>;
+    const uint32_t mag = code & ((1u << F::kSign) - 1u), E = mag >> F::kM, M = mag & ((1u << F::kM) - 1u);
+    const float m = (float)(E ? (1u << F::kM) + M : M);
+    float v = ldexpf(m, (int)(E ? E : 1u) + F::kEmin - 1 - F::kM + se);
+    return ((code >> F::kSign) & 1u) ? -v : v;
 }
 
-template <int MODE, int LOCAL>
-__global__ __launch_bounds__(256) void k_mxfp8(Mxfp8Args a) {
+template <int FMT, int MODE, int LOCAL>
+__global__ __launch_bounds__(256) void k_mx(MxArgs a) {
+    using F = MxElem<FMT>;
     const int64_t nthreads = a.n / 8;
     const int64_t in_codes = a.in_n, out_codes = a.n;
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nthreads;
@@ -934,7 +972,7 @@ __global__ __launch_bounds__(256) void k_mxfp8(Mxfp8Args a) {
             const int64_t r = i0 - a.in_lo;
             const uint2 cw = *reinterpret_cast<const uint2 *>(a.in + r);
             const int se = (int)a.in[in_codes + r / 32] - 127;
-            for (int i = 0; i < 8; i++) y[i] = e4m3_decode(((i < 4 ? cw.x : cw.y) >> (8 * (i & 3))) & 0xFFu, se);
+            for (int i = 0; i < 8; i++) y[i] = mx_decode<FMT>(((i < 4 ? cw.x : cw.y) >> (8 * (i & 3))) & 0xFFu, se);
         }
         if constexpr (MODE == kFinalize) {
             float4 *o = reinterpret_cast<float4 *>(a.out_f32 + i0);
@@ -956,7 +994,7 @@ __global__ __launch_bounds__(256) void k_mxfp8(Mxfp8Args a) {
                 const int64_t r = i0 - a.in_lo;
                 const uint2 cw = *reinterpret_cast<const uint2 *>(a.own + r);
                 const int se = (int)a.own[in_codes + r / 32] - 127;
-                for (int i = 0; i < 8; i++) e[i] = e4m3_decode(((i < 4 ? cw.x : cw.y) >> (8 * (i & 3))) & 0xFFu, se);
+                for (int i = 0; i < 8; i++) e[i] = mx_decode<FMT>(((i < 4 ? cw.x : cw.y) >> (8 * (i & 3))) & 0xFFu, se);
             }
             for (int i = 0; i < 8; i++) y[i] = (MODE == kHop) ? y[i] + e[i] : e[i];
         }
@@ -965,10 +1003,10 @@ __global__ __launch_bounds__(256) void k_mxfp8(Mxfp8Args a) {
         amax = fmaxf(amax, dpp_mov<0xB1>(amax));
         amax = fmaxf(amax, dpp_mov<0x4E>(amax));
         int se = -127;
-        if (amax > 0.0f) se = min(max(floor_log2(amax) - 8, -127), 127);
+        if (amax > 0.0f) se = min(max(floor_log2(amax) - F::kEmax, -127), 127);
         uint32_t w0 = 0u, w1 = 0u;
         for (int i = 0; i < 8; i++) {
-            const uint32_t c = e4m3_encode(ldexpf(y[i], -se));
+            const uint32_t c = mx_encode<FMT>(ldexpf(y[i], -se));
             if (i < 4) w0 |= c << (8 * i);
             else w1 |= c << (8 * (i - 4));
         }
@@ -978,16 +1016,27 @@ __global__ __launch_bounds__(256) void k_mxfp8(Mxfp8Args a) {
     }
 }
 
-hipError_t launch_mxfp8(const Mxfp8Args &a, int local, hipStream_t s) {
-    const dim3 grid(grid_for(a.n / 8, 256, 4096)), block(256);
-    if (a.mode == kCompress && local == kLocalBF16) hipLaunchKernelGGL((k_mxfp8<kCompress, kLocalBF16>), grid, block, 0, s, a);
-    else if (a.mode == kCompress && local == kLocalF32) hipLaunchKernelGGL((k_mxfp8<kCompress, kLocalF32>), grid, block, 0, s, a);
-    else if (a.mode == kHop && local == kLocalBF16) hipLaunchKernelGGL((k_mxfp8<kHop, kLocalBF16>), grid, block, 0, s, a);
-    else if (a.mode == kHop && local == kLocalF32) hipLaunchKernelGGL((k_mxfp8<kHop, kLocalF32>), grid, block, 0, s, a);
-    else if (a.mode == kHop && local == kLocalPacked) hipLaunchKernelGGL((k_mxfp8<kHop, kLocalPacked>), grid, block, 0, s, a);
-    else if (a.mode == kFinalize) hipLaunchKernelGGL((k_mxfp8<kFinalize, kLocalNone>), grid, block, 0, s, a);
+template <int FMT>
+static hipError_t launch_mx_fmt(const MxArgs &a, int local, dim3 grid, dim3 block, hipStream_t s) {
+    if (a.mode == kCompress && local == kLocalBF16) hipLaunchKernelGGL((k_mx<FMT, kCompress, kLocalBF16>), grid, block, 0, s, a);
+    else if (a.mode == kCompress && local == kLocalF32) hipLaunchKernelGGL((k_mx<FMT, kCompress, kLocalF32>), grid, block, 0, s, a);
+    else if (a.mode == kHop && local == kLocalBF16) hipLaunchKernelGGL((k_mx<FMT, kHop, kLocalBF16>), grid, block, 0, s, a);
+    else if (a.mode == kHop && local == kLocalF32) hipLaunchKernelGGL((k_mx<FMT, kHop, kLocalF32>), grid, block, 0, s, a);
+    else if (a.mode == kHop && local == kLocalPacked) hipLaunchKernelGGL((k_mx<FMT, kHop, kLocalPacked>), grid, block, 0, s, a);
+    else if (a.mode == kFinalize) hipLaunchKernelGGL((k_mx<FMT, kFinalize, kLocalNone>), grid, block, 0, s, a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
+}
+
+hipError_t launch_mx(const MxArgs &a, int fmt, int local, hipStream_t s) {
+    const dim3 grid(grid_for(a.n / 8, 256, 4096)), block(256);
+    switch (fmt) {
+        case kMxE4M3: return launch_mx_fmt<kMxE4M3>(a, local, grid, block, s);
+        case kMxE3M2: return launch_mx_fmt<kMxE3M2>(a, local, grid, block, s);
+        case kMxE2M3: return launch_mx_fmt<kMxE2M3>(a, local, grid, block, s);
+        case kMxE2M1: return launch_mx_fmt<kMxE2M1>(a, local, grid, block, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 // ---------------------------------------------------------------------------

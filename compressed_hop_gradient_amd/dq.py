@@ -20,6 +20,7 @@ BF16, F32, PACKED = 0, 1, 2
 CORRELATED, INDEPENDENT = 0, 1
 OPT_SEED, OPT_ROUND, OPT_ROUNDING, OPT_TIMING, OPT_ALLOC = 0, 1, 2, 3, 4
 ALLOC_THRESHOLD, ALLOC_MEAN_CORRECTED, ALLOC_UNIFORM = 0, 1, 2
+MX_FP8_E4M3, MX_FP6_E3M2, MX_FP6_E2M3, MX_FP4_E2M1 = 0, 1, 2, 3
 KERNEL_KINDS = ("stats", "allocate", "reorder", "compress", "hop_grad", "hop_packed",
                 "finalize", "mxfp8")
 
@@ -72,6 +73,9 @@ _SIGS = {
     "dq_mxfp8_arena_bytes": (C.c_size_t, [C.c_void_p]),
     "dq_mxfp8_allreduce": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
                                      C.c_void_p, C.c_void_p]),
+    "dq_mx_arena_bytes": (C.c_size_t, [C.c_void_p]),
+    "dq_mx_allreduce": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
+                                  C.c_void_p, C.c_void_p]),
     "dq_get_info": (C.c_int, [C.c_void_p, C.POINTER(dq_info), C.c_void_p]),
     "dq_timing_read": (C.c_int, [C.c_void_p, C.POINTER(dq_timing)]),
     "dq_status_string": (C.c_char_p, [C.c_int32]),
@@ -224,6 +228,19 @@ class Plan:
         ptrs = (C.c_void_p * self.n)(*[g.data_ptr() for g in grads])
         _check(lib().dq_mxfp8_allreduce(self.h, ptrs, kind, _ptr(arena), arena.numel(), _ptr(out),
                                         _stream(stream)), "dq_mxfp8_allreduce")
+        return out
+
+    def mx_allreduce(self, fmt, grads, out=None, arena=None, stream=None):
+        kind = _kind(grads[0])
+        dev = grads[0].device
+        if arena is None:
+            arena = torch.empty(max(1, int(lib().dq_mx_arena_bytes(self.h))), dtype=torch.uint8,
+                                device=dev)
+        if out is None:
+            out = torch.empty(self.d, dtype=torch.float32, device=dev)
+        ptrs = (C.c_void_p * self.n)(*[g.data_ptr() for g in grads])
+        _check(lib().dq_mx_allreduce(self.h, int(fmt), ptrs, kind, _ptr(arena), arena.numel(), _ptr(out),
+                                     _stream(stream)), "dq_mx_allreduce")
         return out
 
     # ---- inspection ------------------------------------------------------

@@ -233,6 +233,27 @@ size_t dq_mxfp8_arena_bytes(const dq_plan *plan);
 dq_status dq_mxfp8_allreduce(dq_plan *plan, const void *const *h_grads, int32_t kind,
                              void *d_arena, size_t arena_bytes, float *d_out, void *stream);
 
+/* MX element formats (OCP MX v1.0).  The pages list MXFP4, MXFP6 and MXFP8 as
+ * baselines and the review notes that MXFP4/6 were only estimated
+ * (pith.science review, referee major 3); these run them in the same
+ * schedule.  Every format stores one code byte per coordinate plus one E8M0
+ * byte per 32 (the wire would carry 4.25, 6.25 or 8.25 bits). */
+typedef enum dq_mx_format {
+    DQ_MX_FP8_E4M3 = 0,   /* max 448, 3 mantissa bits */
+    DQ_MX_FP6_E3M2 = 1,   /* max 28, 2 mantissa bits */
+    DQ_MX_FP6_E2M3 = 2,   /* max 7.5, 3 mantissa bits */
+    DQ_MX_FP4_E2M1 = 3    /* max 6, 1 mantissa bit */
+} dq_mx_format;
+
+/* As dq_mxfp8_allreduce with the element format `format` (dq_mx_format);
+ * the block scale is 2^(floor(log2 max|v|) - emax), emax = exponent of the
+ * format's largest value, elements round to nearest even and saturate.
+ * Errors: DQ_ENULL, DQ_EINVAL (format, kind, gradient alignment),
+ * DQ_EWORKSPACE (arena smaller than dq_mx_arena_bytes), DQ_EHIP. */
+size_t dq_mx_arena_bytes(const dq_plan *plan);
+dq_status dq_mx_allreduce(dq_plan *plan, int32_t format, const void *const *h_grads, int32_t kind,
+                          void *d_arena, size_t arena_bytes, float *d_out, void *stream);
+
 /* ---- inspection ----------------------------------------------------------- */
 
 /* Copy the allocation result to the host.  SYNCHRONISES `stream`.
