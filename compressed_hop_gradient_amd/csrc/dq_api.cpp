@@ -38,6 +38,7 @@ struct dq_plan {
     int32_t rounding = DQ_ROUND_CORRELATED;
     int32_t alloc = DQ_ALLOC_THRESHOLD;
     bool timing = false;
+    uint32_t timing_kinds = (1u << DQ_K_COUNT) - 1u;   // kinds timed while timing is on
 
     uint8_t *ws = nullptr;
     size_t ws_bytes = 0;
@@ -90,7 +91,7 @@ hipError_t timed_begin(dq_plan *p, int kind, int64_t m, int64_t part, hipStream_
     L.m = m;
     L.part = part;
     L.e0 = L.e1 = nullptr;
-    if (!p->timing) return hipSuccess;
+    if (!p->timing || !((p->timing_kinds >> kind) & 1u)) return hipSuccess;
     for (hipEvent_t *e : {&L.e0, &L.e1}) {
         if (!p->pool.empty()) {
             *e = p->pool.back();
@@ -104,7 +105,7 @@ hipError_t timed_begin(dq_plan *p, int kind, int64_t m, int64_t part, hipStream_
 }
 
 hipError_t timed_end(dq_plan *p, Launch &L, hipStream_t s) {
-    if (!p->timing) return hipSuccess;
+    if (!p->timing || !L.e0) return hipSuccess;
     hipError_t err = hipEventRecord(L.e1, s);
     p->launches.push_back(L);
     return err;
@@ -304,6 +305,10 @@ dq_status dq_plan_set_u64(dq_plan *p, int32_t option, uint64_t v) {
         case DQ_OPT_TIMING:
             if (v > 1) return DQ_EINVAL;
             p->timing = v == 1;
+            return DQ_OK;
+        case DQ_OPT_TIMING_KINDS:
+            if (v == 0 || v >= (1ull << DQ_K_COUNT)) return DQ_EINVAL;
+            p->timing_kinds = (uint32_t)v;
             return DQ_OK;
         case DQ_OPT_ALLOC:
             if (v != DQ_ALLOC_THRESHOLD && v != DQ_ALLOC_MEAN_CORRECTED && v != DQ_ALLOC_UNIFORM)

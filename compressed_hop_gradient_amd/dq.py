@@ -18,7 +18,7 @@ DQ_OK, DQ_EINVAL, DQ_EBUDGET, DQ_ESTATE, DQ_EWORKSPACE, DQ_ENULL, DQ_EHIP, DQ_EN
 RING, BUTTERFLY = 0, 1
 BF16, F32, PACKED = 0, 1, 2
 CORRELATED, INDEPENDENT = 0, 1
-OPT_SEED, OPT_ROUND, OPT_ROUNDING, OPT_TIMING, OPT_ALLOC = 0, 1, 2, 3, 4
+OPT_SEED, OPT_ROUND, OPT_ROUNDING, OPT_TIMING, OPT_ALLOC, OPT_TIMING_KINDS = 0, 1, 2, 3, 4, 5
 ALLOC_THRESHOLD, ALLOC_MEAN_CORRECTED, ALLOC_UNIFORM = 0, 1, 2
 MX_FP8_E4M3, MX_FP6_E3M2, MX_FP6_E2M3, MX_FP4_E2M1 = 0, 1, 2, 3
 KERNEL_KINDS = ("stats", "allocate", "reorder", "compress", "hop_grad", "hop_packed",

@@ -92,8 +92,10 @@ typedef enum dq_option {
     DQ_OPT_ROUND = 1,      /* round index, 32-bit, part of every Philox counter (default 0) */
     DQ_OPT_ROUNDING = 2,   /* dq_rounding (default DQ_ROUND_CORRELATED) */
     DQ_OPT_TIMING = 3,     /* 1: time every launch with HIP events on its stream */
-    DQ_OPT_ALLOC = 4       /* dq_alloc (default DQ_ALLOC_THRESHOLD); takes effect at the
+    DQ_OPT_ALLOC = 4,      /* dq_alloc (default DQ_ALLOC_THRESHOLD); takes effect at the
                               next dq_allocate */
+    DQ_OPT_TIMING_KINDS = 5  /* bit mask of dq_kernel_kind: which launches DQ_OPT_TIMING
+                                times (default all); fewer events, less overhead */
 } dq_option;
 
 typedef struct dq_plan dq_plan;

@@ -77,6 +77,9 @@ def test_options(lib):
     for mode in (dq.ALLOC_THRESHOLD, dq.ALLOC_MEAN_CORRECTED, dq.ALLOC_UNIFORM):
         assert lib.dq_plan_set_u64(h, dq.OPT_ALLOC, mode) == dq.DQ_OK
     assert lib.dq_plan_set_u64(h, dq.OPT_ALLOC, 3) == dq.DQ_EINVAL
+    assert lib.dq_plan_set_u64(h, dq.OPT_TIMING_KINDS, 1 << 4) == dq.DQ_OK
+    assert lib.dq_plan_set_u64(h, dq.OPT_TIMING_KINDS, 0) == dq.DQ_EINVAL
+    assert lib.dq_plan_set_u64(h, dq.OPT_TIMING_KINDS, 1 << 8) == dq.DQ_EINVAL
     assert lib.dq_plan_set_u64(h, 99, 0) == dq.DQ_EINVAL
     assert lib.dq_plan_set_u64(None, 0, 0) == dq.DQ_ENULL
     lib.dq_plan_destroy(h)

@@ -1,0 +1,43 @@
+"""A whole round captured in a HIP graph (torch.cuda.CUDAGraph on ROCm): the
+library enqueues only kernels on the caller's stream -- no memset, no
+allocation, no synchronisation -- so the round can be captured once and
+replayed.  Every replay, with new inputs written between replays, must give
+the bytes of an eager round on the same inputs."""
+import pytest
+import torch
+
+from compressed_hop_gradient_amd import dq, synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("topo,name", [(dq.RING, "bert"), (dq.BUTTERFLY, "gemma")])
+def test_round_in_graph_replays(topo, name):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    J, n = 1031, 8
+    grads = synth.generate(name, d=256 * J, device="cuda", workers=range(n))
+    bufs = [g.clone() for g in grads]                    # the inputs the graph reads
+    plan = dq.Plan(256 * J, n, topo, 5.0)
+    arena = torch.empty(plan.arena_bytes(), dtype=torch.uint8, device="cuda")
+    out = torch.empty(256 * J, dtype=torch.float32, device="cuda")
+    ref = dq.Plan(256 * J, n, topo, 5.0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                        # warm-up off the default stream
+        plan.allreduce(bufs, out=out, arena=arena)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan.allreduce(bufs, out=out, arena=arena)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for w in range(n):                               # new inputs: rotated workers, scaled
+            bufs[w].copy_(grads[(w + rep) % n] * (rep + 1))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        eager = ref.allreduce([b.clone() for b in bufs])
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), eager.view(torch.int32)), f"replay {rep}"
