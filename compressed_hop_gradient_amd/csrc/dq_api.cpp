@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "dq_internal.h"
+#include "dq_tables.h"
 
 using namespace dq;
 
@@ -39,6 +40,8 @@ struct dq_plan {
     int32_t alloc = DQ_ALLOC_THRESHOLD;
     bool timing = false;
     uint32_t timing_kinds = (1u << DQ_K_COUNT) - 1u;   // kinds timed while timing is on
+    double eps = kDefaultEps;                          // level shape
+    bool tables_dirty = true;                          // workspace tables to (re)build
 
     uint8_t *ws = nullptr;
     size_t ws_bytes = 0;
@@ -79,6 +82,7 @@ void compute_layout(dq_plan *p) {
     p->lay.perm = off; off = align_up(off + 4 * J, kAlign);
     p->lay.inv = off; off = align_up(off + 4 * J, kAlign);
     p->lay.mu_stream = off; off = align_up(off + 4 * J, kAlign);
+    p->lay.tables = off; off = align_up(off + sizeof(DeviceTables), kAlign);
     p->lay.ctrl = off;
     off = align_up(off + sizeof(Ctrl), kAlign);
     off = align_up(off + 4 * 3 * (size_t)p->nblk, kAlign);
@@ -175,6 +179,7 @@ void fill_rng(const dq_plan *p, int32_t w, int32_t step, CodecArgs &a) {
 
 void fill_common(dq_plan *p, CodecArgs &a) {
     std::memset(&a, 0, sizeof(a));
+    a.tab = reinterpret_cast<const DeviceTables *>(p->ws + p->lay.tables);
     a.perm = i32_at(p, p->lay.perm);
     a.mu_stream = f32_at(p, p->lay.mu_stream);
     a.n_workers_f = (float)p->n;
@@ -319,12 +324,24 @@ dq_status dq_plan_set_u64(dq_plan *p, int32_t option, uint64_t v) {
     }
 }
 
+dq_status dq_plan_set_f64(dq_plan *p, int32_t option, double v) {
+    if (!p) return DQ_ENULL;
+    if (option != DQ_OPT_EPS) return DQ_EINVAL;
+    // (0, 1], and every bucket of the interval search may hold at most one
+    // level boundary for this shape
+    if (!(v > 0.0 && v <= 1.0) || !level_shape_ok(v)) return DQ_EINVAL;
+    p->eps = v;
+    p->tables_dirty = true;
+    return DQ_OK;
+}
+
 size_t dq_workspace_bytes(const dq_plan *p) { return p ? p->lay.total : 0; }
 
 dq_status dq_plan_bind(dq_plan *p, void *ws, size_t bytes) {
     if (!p || !ws) return DQ_ENULL;
     if (bytes < p->lay.total || !aligned(ws, kAlign)) return DQ_EWORKSPACE;
     p->ws = static_cast<uint8_t *>(ws);
+    p->tables_dirty = true;
     p->ws_bytes = bytes;
     p->stats_done = 0;
     p->allocated = p->reordered = false;
@@ -363,7 +380,12 @@ dq_status dq_stats(dq_plan *p, int32_t w, const void *grad, int32_t kind, void *
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (w == 0) {
         hipError_t e = launch_zero(reinterpret_cast<uint32_t *>(&ctrl_of(p)->nonfinite), 1, s);
+        // the first round after a bind or a new level shape builds the tables
+        // on the device, ahead of every codec launch on this stream
+        if (e == hipSuccess && p->tables_dirty)
+            e = launch_build_tables(reinterpret_cast<DeviceTables *>(p->ws + p->lay.tables), p->eps, s);
         if (e != hipSuccess) return DQ_EHIP;
+        p->tables_dirty = false;
     }
     StatsArgs a;
     a.grad = grad;

@@ -49,7 +49,10 @@ enum Local { kLocalNone = 0, kLocalBF16 = 1, kLocalF32 = 2, kLocalPacked = 3 };
 // the super-groups of one output part (m_out, part_out); the input regions
 // (incoming and own packed) hold the part (m_in, part_in) that contains it
 // (the same part, or its parent when a hop writes the two children).
+struct DeviceTables;
+
 struct CodecArgs {
+    const DeviceTables *tab;                 // level and bucket tables (plan workspace)
     const PartInfo *part_out;                // device part table entries
     const PartInfo *part_in;
     const int32_t *perm;
@@ -116,6 +119,7 @@ struct MxArgs {
 
 // launchers (dq_kernels.hip); each returns the hipError_t of its launch
 hipError_t launch_zero(uint32_t *p, int64_t n, hipStream_t s);
+hipError_t launch_build_tables(DeviceTables *t, double eps, hipStream_t s);
 hipError_t launch_stats(const StatsArgs &a, int f32, hipStream_t s);
 hipError_t launch_alloc_pass(const AllocArgs &a, int pass, hipStream_t s);
 hipError_t launch_alloc_final(const AllocArgs &a, hipStream_t s);

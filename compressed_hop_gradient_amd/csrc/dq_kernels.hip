@@ -23,9 +23,6 @@ namespace dq {
 
 static int grid_for(int64_t items, int64_t per_block, int64_t cap);
 
-__device__ const LevelTables g_tables = kLevelTables;
-__device__ const BucketTable<256> g_buckets8 = kBuckets8;
-__device__ const BucketTable<16> g_buckets4 = kBuckets4;
 
 // ---------------------------------------------------------------------------
 // small device helpers
@@ -132,12 +129,13 @@ __device__ __forceinline__ uint32_t search_levels(float v, const uint8_t *est_ta
     return r;
 }
 
-__device__ __forceinline__ int search_levels2(float v, float &Lr, float &Wr) {
-    constexpr float l0 = kLevelTables.L2[0], l1 = kLevelTables.L2[1], l2 = kLevelTables.L2[2];
-    constexpr float w0 = kLevelTables.W2[0], w1 = kLevelTables.W2[1], w2 = kLevelTables.W2[2];
-    const int r = (v >= l1 ? 1 : 0) + (v >= l2 ? 1 : 0);
-    Lr = r == 0 ? l0 : (r == 1 ? l1 : l2);
-    Wr = r == 0 ? w0 : (r == 1 ? w1 : w2);
+// 2-bit search: two compares against the inner levels c1 = L[1], c2 = L[2]
+__device__ __forceinline__ uint32_t search_levels2(float v, float c1, float c2, const Pair *lw,
+                                                   float &Lr, float &Wr) {
+    const uint32_t r = (v >= c1 ? 1u : 0u) + (v >= c2 ? 1u : 0u);
+    const Pair p = lw[r];
+    Lr = p.l;
+    Wr = p.w;
     return r;
 }
 
@@ -174,6 +172,7 @@ __device__ __forceinline__ void part_info(const unsigned long long *C, int64_t m
 
 struct SharedTables {
     float dec2[4];
+    Pair lw2[3];
     float dec4[16];
     float dec8[256];
     float cl4[16];
@@ -318,6 +317,11 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po,
     const int c = group_code(amax, s);
     const float sigma = (float)c * s;
     const float inv = sigma == 0.0f ? 0.0f : 1.0f / sigma;
+    float c1 = 0.0f, c2 = 0.0f;
+    if constexpr (Q == 2) {
+        c1 = T.dec2[1];
+        c2 = T.dec2[2];
+    }
 
     typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
     const ushort2_t stag = {(unsigned short)a.stagger, (unsigned short)a.stagger};
@@ -350,7 +354,7 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po,
             const float v = y[i] * inv;
             float Lr, Wr;
             uint32_t r;
-            if constexpr (Q == 2) r = (uint32_t)search_levels2(v, Lr, Wr);
+            if constexpr (Q == 2) r = search_levels2(v, c1, c2, T.lw2, Lr, Wr);
             else if constexpr (Q == 4) r = search_levels<16>(v, T.b4, T.cl4, T.lw4, Lr, Wr);
             else r = search_levels<256>(v, T.b8, T.cl8, T.lw8, Lr, Wr);
             const float P = (v - Lr) * Wr;
@@ -369,21 +373,23 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po,
 template <int MODE, int LOCAL>
 __global__ __launch_bounds__(256) void k_codec(CodecArgs a) {
     __shared__ __align__(16) SharedTables T;
+    const LevelTables &lev = a.tab->lev;
     for (int i = threadIdx.x; i < 256; i += blockDim.x) {
-        T.dec8[i] = g_tables.L8[i];
-        T.cl8[i] = g_tables.CL8[i];
+        T.dec8[i] = lev.L8[i];
+        T.cl8[i] = lev.CL8[i];
     }
-    for (int i = threadIdx.x; i < 255; i += blockDim.x) T.lw8[i] = g_tables.LW8[i];
+    for (int i = threadIdx.x; i < 255; i += blockDim.x) T.lw8[i] = lev.LW8[i];
     for (int i = threadIdx.x; i < 2 * kKeys; i += blockDim.x) {
-        T.b8[i] = g_buckets8.est[i];
-        T.b4[i] = g_buckets4.est[i];
+        T.b8[i] = a.tab->b8.est[i];
+        T.b4[i] = a.tab->b4.est[i];
     }
     if (threadIdx.x < 16) {
-        T.dec4[threadIdx.x] = g_tables.L4[threadIdx.x];
-        T.cl4[threadIdx.x] = g_tables.CL4[threadIdx.x];
+        T.dec4[threadIdx.x] = lev.L4[threadIdx.x];
+        T.cl4[threadIdx.x] = lev.CL4[threadIdx.x];
     }
-    if (threadIdx.x < 15) T.lw4[threadIdx.x] = g_tables.LW4[threadIdx.x];
-    if (threadIdx.x < 4) T.dec2[threadIdx.x] = g_tables.L2[threadIdx.x];
+    if (threadIdx.x < 15) T.lw4[threadIdx.x] = lev.LW4[threadIdx.x];
+    if (threadIdx.x < 4) T.dec2[threadIdx.x] = lev.L2[threadIdx.x];
+    if (threadIdx.x < 3) T.lw2[threadIdx.x] = Pair{lev.L2[threadIdx.x], lev.W2[threadIdx.x]};
     __syncthreads();
     // part layouts: uniform loads from the per-round part table
     const PartInfo Po = *a.part_out, Pi = *a.part_in;
@@ -446,9 +452,10 @@ __device__ __forceinline__ void finalize_sg(const CodecArgs &a, const PartInfo &
 
 __global__ __launch_bounds__(256) void k_finalize(CodecArgs a) {
     __shared__ __align__(16) SharedTables T;
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) T.dec8[i] = g_tables.L8[i];
-    if (threadIdx.x < 16) T.dec4[threadIdx.x] = g_tables.L4[threadIdx.x];
-    if (threadIdx.x < 4) T.dec2[threadIdx.x] = g_tables.L2[threadIdx.x];
+    const LevelTables &lev = a.tab->lev;
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) T.dec8[i] = lev.L8[i];
+    if (threadIdx.x < 16) T.dec4[threadIdx.x] = lev.L4[threadIdx.x];
+    if (threadIdx.x < 4) T.dec2[threadIdx.x] = lev.L2[threadIdx.x];
     __syncthreads();
     const PartInfo P = *a.part_in;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1042,6 +1049,53 @@ hipError_t launch_mx(const MxArgs &a, int fmt, int local, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // utility
 // ---------------------------------------------------------------------------
+
+// Level, compare-level, (L, W) and bucket tables of the level shape eps, from
+// the same constexpr definitions the compile-time checks use (fp64, rounded
+// once to fp32); bucket entries by binary search for the largest r <= NL - 2
+// with L[r] <= the bucket's lower end (v >= 0) or <= -(its upper end) (v < 0).
+template <int NL>
+__device__ int est_of(float x, double eps) {
+    int lo = 0, len = NL - 1;          // search r in [0, NL - 2]; L[0] = -1 <= x always
+    while (len > 1) {
+        const int half = len >> 1;
+        if (level_f(lo + half, NL, eps) <= x) {
+            lo += half;
+            len -= half;
+        } else {
+            len = half;
+        }
+    }
+    return lo;
+}
+
+__global__ __launch_bounds__(256) void k_build_tables(DeviceTables *t, double eps) {
+    LevelTables &v = t->lev;
+    for (int r = threadIdx.x; r < 256; r += blockDim.x) {
+        v.L8[r] = level_f(r, 256, eps);
+        v.CL8[r] = compare_level(r, 256, eps);
+        if (r < 255) v.LW8[r] = Pair{level_f(r, 256, eps), weight_f(r, 256, eps)};
+        if (r < 16) {
+            v.L4[r] = level_f(r, 16, eps);
+            v.CL4[r] = compare_level(r, 16, eps);
+        }
+        if (r < 15) v.LW4[r] = Pair{level_f(r, 16, eps), weight_f(r, 16, eps)};
+        if (r < 4) v.L2[r] = level_f(r, 4, eps);
+        if (r < 3) v.W2[r] = weight_f(r, 4, eps);
+    }
+    for (int k = threadIdx.x; k < kKeys; k += blockDim.x) {
+        const float lo = key_lo(k), nh = -key_hi(k);
+        t->b8.est[2 * k] = (unsigned char)est_of<256>(lo, eps);
+        t->b8.est[2 * k + 1] = (unsigned char)est_of<256>(nh, eps);
+        t->b4.est[2 * k] = (unsigned char)est_of<16>(lo, eps);
+        t->b4.est[2 * k + 1] = (unsigned char)est_of<16>(nh, eps);
+    }
+}
+
+hipError_t launch_build_tables(DeviceTables *t, double eps, hipStream_t s) {
+    hipLaunchKernelGGL(k_build_tables, dim3(1), dim3(256), 0, s, t, eps);
+    return hipGetLastError();
+}
 
 __global__ void k_zero_u32(uint32_t *p, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;

@@ -21,6 +21,7 @@ CORRELATED, INDEPENDENT = 0, 1
 OPT_SEED, OPT_ROUND, OPT_ROUNDING, OPT_TIMING, OPT_ALLOC, OPT_TIMING_KINDS = 0, 1, 2, 3, 4, 5
 ALLOC_THRESHOLD, ALLOC_MEAN_CORRECTED, ALLOC_UNIFORM = 0, 1, 2
 MX_FP8_E4M3, MX_FP6_E3M2, MX_FP6_E2M3, MX_FP4_E2M1 = 0, 1, 2, 3
+OPT_EPS = 0   # dq_option_f64
 KERNEL_KINDS = ("stats", "allocate", "reorder", "compress", "hop_grad", "hop_packed",
                 "finalize", "mxfp8")
 
@@ -34,7 +35,7 @@ class dq_info(C.Structure):
 
 class dq_layout(C.Structure):
     _fields_ = [(n, C.c_size_t) for n in ("sum", "sumsq", "widths", "perm", "inv", "mu_stream",
-                                          "ctrl", "total")]
+                                          "tables", "ctrl", "total")]
 
 
 class dq_timing(C.Structure):
@@ -74,6 +75,7 @@ _SIGS = {
     "dq_mxfp8_allreduce": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
                                      C.c_void_p, C.c_void_p]),
     "dq_mx_arena_bytes": (C.c_size_t, [C.c_void_p]),
+    "dq_plan_set_f64": (C.c_int, [C.c_void_p, C.c_int32, C.c_double]),
     "dq_mx_allreduce": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
                                   C.c_void_p, C.c_void_p]),
     "dq_get_info": (C.c_int, [C.c_void_p, C.POINTER(dq_info), C.c_void_p]),
@@ -136,7 +138,7 @@ class Plan:
     """
 
     def __init__(self, n_coords, n_workers, topology=RING, avg_bits=5.0, seed=1, rnd=0,
-                 rounding=CORRELATED, device="cuda", timing=False, alloc=ALLOC_THRESHOLD):
+                 rounding=CORRELATED, device="cuda", timing=False, alloc=ALLOC_THRESHOLD, eps=None):
         self.d = int(n_coords)
         self.n = int(n_workers)
         self.J = self.d // 256
@@ -151,6 +153,8 @@ class Plan:
         self.set(OPT_ROUNDING, rounding)
         self.set(OPT_TIMING, 1 if timing else 0)
         self.set(OPT_ALLOC, alloc)
+        if eps is not None:
+            _check(lib().dq_plan_set_f64(self.h, OPT_EPS, float(eps)), "dq_plan_set_f64")
         nbytes = lib().dq_workspace_bytes(self.h)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _check(lib().dq_plan_bind(self.h, _ptr(self.workspace), nbytes), "dq_plan_bind")

@@ -120,6 +120,7 @@ typedef struct dq_layout {
     size_t perm;       /* int32[J]  stream position -> SG */
     size_t inv;        /* int32[J]  SG -> stream position */
     size_t mu_stream;  /* float[J]  global mean mu in stream order */
+    size_t tables;     /* level and bucket tables of the plan's level shape */
     size_t ctrl;       /* control block (counts, rho, flags) */
     size_t total;
 } dq_layout;
@@ -150,11 +151,26 @@ void dq_plan_destroy(dq_plan *plan);
 /* Set a dq_option.  Errors: DQ_ENULL, DQ_EINVAL (unknown option or value). */
 dq_status dq_plan_set_u64(dq_plan *plan, int32_t option, uint64_t value);
 
+/* Real-valued options. */
+typedef enum dq_option_f64 {
+    /* Level shape eps of phi(t) = t (eps + (1 - eps) t) (the pith.science
+     * review's ledger names the level set Q = {f(eps, r)} and notes that the
+     * paper never states eps).  Default 1/2; 1 is the uniform grid.  Accepted
+     * for eps in (0, 1] when every bucket of the kernels' interval search holds
+     * at most one level boundary (true at least for eps >= 0.01).  Rebuilds the
+     * plan's tables; if a workspace is bound they are copied into it at once
+     * (synchronous).  Set it between rounds, not inside one. */
+    DQ_OPT_EPS = 0
+} dq_option_f64;
+dq_status dq_plan_set_f64(dq_plan *plan, int32_t option, double value);
+
 /* Device bytes the caller must provide for the plan state. */
 size_t dq_workspace_bytes(const dq_plan *plan);
 
 /* Bind caller-owned device memory (>= dq_workspace_bytes, 256-byte aligned).
- * Errors: DQ_ENULL, DQ_EWORKSPACE. */
+ * Copies the plan's level and bucket tables into it (a synchronous
+ * host-to-device copy, the only one the library makes).
+ * Errors: DQ_ENULL, DQ_EWORKSPACE, DQ_EHIP. */
 dq_status dq_plan_bind(dq_plan *plan, void *d_workspace, size_t bytes);
 
 dq_status dq_workspace_layout(const dq_plan *plan, dq_layout *out);

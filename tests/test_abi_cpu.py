@@ -82,6 +82,13 @@ def test_options(lib):
     assert lib.dq_plan_set_u64(h, dq.OPT_TIMING_KINDS, 1 << 8) == dq.DQ_EINVAL
     assert lib.dq_plan_set_u64(h, 99, 0) == dq.DQ_EINVAL
     assert lib.dq_plan_set_u64(None, 0, 0) == dq.DQ_ENULL
+    # level shape: (0, 1] and one level boundary per search bucket
+    for eps in (1.0, 0.5, 0.3, 0.05, 0.01):
+        assert lib.dq_plan_set_f64(h, dq.OPT_EPS, eps) == dq.DQ_OK
+    for eps in (0.0, -0.5, 1.5, float("nan"), float("inf")):
+        assert lib.dq_plan_set_f64(h, dq.OPT_EPS, eps) == dq.DQ_EINVAL
+    assert lib.dq_plan_set_f64(h, 1, 0.5) == dq.DQ_EINVAL
+    assert lib.dq_plan_set_f64(None, dq.OPT_EPS, 0.5) == dq.DQ_ENULL
     lib.dq_plan_destroy(h)
 
 
@@ -93,7 +100,7 @@ def test_workspace_and_region_sizes(lib):
     lay = dq.dq_layout()
     assert lib.dq_workspace_layout(h, C.byref(lay)) == dq.DQ_OK
     assert lay.total == ws
-    offs = [lay.sum, lay.sumsq, lay.widths, lay.perm, lay.inv, lay.mu_stream, lay.ctrl]
+    offs = [lay.sum, lay.sumsq, lay.widths, lay.perm, lay.inv, lay.mu_stream, lay.tables, lay.ctrl]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert lay.sumsq - lay.sum >= 4 * J and lay.perm - lay.widths >= J
     # regions: worst case of any part of m is at most (J/m + 3) SGs of 276 bytes

@@ -76,16 +76,16 @@ class Round:
     region both produce (fresh zeroed buffers per step)."""
 
     def __init__(self, grads, topo, budget=5.0, seed=1, rnd=0, rounding=dq.CORRELATED,
-                 alloc=dq.ALLOC_THRESHOLD):
+                 alloc=dq.ALLOC_THRESHOLD, eps=None):
         self.grads = grads
         self.gnp = _grads_np(grads)
         self.n = len(grads)
         self.d = grads[0].numel()
         self.topo = topo
         self.plan = dq.Plan(self.d, self.n, topo, budget, seed=seed, rnd=rnd, rounding=rounding,
-                            alloc=alloc)
+                            alloc=alloc, eps=eps)
         self.orc = po.Oracle(self.d, self.n, topo, budget, seed=seed, rnd=rnd, rounding=rounding,
-                             alloc=alloc)
+                             alloc=alloc, eps=eps)
 
     def stages(self):
         for w in range(self.n):
@@ -257,6 +257,55 @@ def test_allocation_variants_bit_exact(alloc, budget, topo):
         plain = Round(grads, topo, budget=budget)
         plain.stages()
         assert not np.array_equal(plain.plan.widths().cpu().numpy(), r.plan.widths().cpu().numpy())
+
+
+@pytest.mark.parametrize("eps,topo", [(1.0, dq.RING), (0.25, dq.BUTTERFLY), (0.05, dq.RING),
+                                      (0.8, dq.BUTTERFLY)])
+def test_level_shapes_bit_exact(eps, topo):
+    """Other level shapes phi(t) = t (eps + (1 - eps) t): eps = 1 is the
+    uniform grid; smaller eps packs the levels towards zero."""
+    _need_gpu()
+    grads = _scaled("llama" if topo == dq.RING else "gemma", 1031, workers=range(8))
+    full_round(grads, topo, budget=5.0, eps=eps)
+
+
+@pytest.mark.parametrize("eps", [0.5, 1.0, 0.1])
+def test_device_tables_match_the_definition(eps):
+    """The tables the plan builds in its workspace: levels and (L, W) pairs
+    equal the oracle's; compare levels end in +inf; every bucket entry is
+    the largest r <= NL - 2 whose level is at most the bucket's end."""
+    _need_gpu()
+    d = 256 * 64
+    grads = [torch.zeros(d, dtype=torch.bfloat16, device=DEV)]
+    p = dq.Plan(d, 1, dq.RING, 5.0, eps=eps)
+    p.stats(0, grads[0])                     # the first stage builds the tables
+    torch.cuda.synchronize()
+    off = p.layout["tables"]
+    raw = p.workspace[off:off + 11020].cpu().numpy()
+    f = lambda o, n: raw[o:o + 4 * n].view(np.float32)
+    L2, L4, L8, W2 = f(0, 4), f(16, 16), f(80, 256), f(1104, 3)
+    CL4, CL8 = f(1116, 16), f(1180, 256)
+    LW4, LW8 = f(2204, 30).reshape(15, 2), f(2324, 510).reshape(255, 2)
+    for q, L, CL, LW in ((2, L2, None, None), (4, L4, CL4, LW4), (8, L8, CL8, LW8)):
+        Lo, Wo = po.levels(q, eps)
+        assert np.array_equal(_bits(L), _bits(Lo))
+        if q == 2:
+            assert np.array_equal(_bits(W2), _bits(Wo[:3]))
+            continue
+        assert np.array_equal(_bits(CL[:-1]), _bits(Lo[:-1])) and np.isposinf(CL[-1])
+        assert np.array_equal(_bits(LW[:, 0]), _bits(Lo[:-1]))
+        assert np.array_equal(_bits(LW[:, 1]), _bits(Wo[:len(Lo) - 1]))
+    base, nkeys = 0x3980, 0x4000 - 0x3980
+    k = np.arange(nkeys, dtype=np.uint32)
+    lo = np.where(k == 0, 0, ((np.minimum(k, 0x3F80 - base) + base) << 16)).astype(np.uint32).view(np.float32)
+    hi = np.where(k >= 0x3F80 - base, np.float32(1.0).view(np.uint32),
+                  (k + 1 + base) << 16).astype(np.uint32).view(np.float32)
+    for q, o in ((8, 4364), (4, 4364 + 2 * nkeys)):
+        est = raw[o:o + 2 * nkeys]
+        Lo = po.levels(q, eps)[0][:-1]
+        exp_pos = np.searchsorted(Lo, lo, side="right") - 1
+        exp_neg = np.searchsorted(Lo, -hi, side="right") - 1
+        assert np.array_equal(est[0::2], exp_pos) and np.array_equal(est[1::2], exp_neg)
 
 
 @pytest.mark.parametrize("n,topo", [(1, dq.RING), (1, dq.BUTTERFLY), (2, dq.RING), (2, dq.BUTTERFLY),

@@ -5,8 +5,8 @@ tables of the reading (generated here and by the oracle), on the CPU.
    threshold P of the last interval already exceeds every d + 0.5 (d < 2^16),
    and just below -1 it is negative, so codes cannot change.
 2. The interval search looks up a bucket of v keyed by the sign, the exponent
-   and 7 mantissa bits of |v| (all |v| < 2^-9 share one bucket): each bucket
-   holds at most one level boundary.
+   and 7 mantissa bits of |v| (all |v| < 2^-12 share one bucket): each bucket
+   holds at most one level boundary, for level shapes eps from 0.01 to 1.
 """
 import numpy as np
 import pytest
@@ -42,9 +42,13 @@ def test_no_clamp_needed_at_the_ends(q):
 
 
 @pytest.mark.parametrize("q", [4, 8])
-def test_buckets_hold_at_most_one_boundary(q):
-    L, _ = po.levels(q)
-    base, kmax = 0x3B00, 0x3F80 - 0x3B00
+@pytest.mark.parametrize("eps", [1.0, 0.75, 0.5, 0.3, 0.1, 0.05, 0.01])
+def test_buckets_hold_at_most_one_boundary(q, eps):
+    """Buckets of 7 mantissa bits per exponent of |v|, all |v| < 2^-12 in one
+    bucket: at most one level boundary per bucket, for level shapes from
+    eps = 0.01 to the uniform grid."""
+    L, _ = po.levels(q, eps)
+    base, kmax = 0x3980, 0x3F80 - 0x3980
     keys = np.arange(kmax + 1, dtype=np.uint32)
     lo = ((keys + base) << 16).view(np.float32).copy()
     lo[0] = 0.0
@@ -57,5 +61,12 @@ def test_buckets_hold_at_most_one_boundary(q):
     # v < 0 in (-hi, -lo]
     inside = ((Lp[None, :] > -hi[:, None]) & (Lp[None, :] <= -lo[:, None])).sum(1)
     assert inside.max() <= 1
-    # the smallest positive level is above the shared bucket of tiny |v|
-    assert L[(1 << q) // 2] > np.float32(2.0 ** -9) * np.float32(1 + 2.0 ** -7) or q == 4
+
+
+def test_higher_tiny_bucket_would_fail_small_shapes():
+    """Were the shared bucket of tiny |v| to end at 2^-9, the 8-bit levels of
+    eps = 0.1 would put two boundaries into it: ending it at 2^-12 is what
+    admits the small shapes."""
+    L, _ = po.levels(8, 0.1)
+    assert ((L > 0) & (L < np.float32(2.0 ** -9))).sum() >= 2
+    assert ((L > 0) & (L < np.float32(2.0 ** -12))).sum() <= 1
