@@ -212,8 +212,8 @@ def main():
         v_mx4 = vnmse(plan.mx_allreduce(dq.MX_FP4_E2M1, grads, out=torch.empty_like(out), arena=mx_arena))
         del mx_arena
 
-        def variant(gs, bits, alloc, ref):
-            p = dq.Plan(wl.d, wl.n, topo, bits, seed=wl.rounding_seed, alloc=alloc, device=dev)
+        def variant(gs, bits, alloc, ref, eps=None):
+            p = dq.Plan(wl.d, wl.n, topo, bits, seed=wl.rounding_seed, alloc=alloc, device=dev, eps=eps)
             a = torch.empty(p.arena_bytes(), dtype=torch.uint8, device=dev)
             o = p.allreduce(gs, out=torch.empty_like(out), arena=a)
             return ((o.double() - ref) ** 2).sum().item() / norm
@@ -223,6 +223,9 @@ def main():
         # the gradients and after one random coordinate shuffle shared by all
         # workers (the spatial-locality premise, Fig. 1)
         v_mc = variant(grads, budget, dq.ALLOC_MEAN_CORRECTED, exact)
+        # the level shape eps the pages leave open (review's ledger)
+        v_eps = {str(e): variant(grads, budget, dq.ALLOC_THRESHOLD, exact, eps=e)
+                 for e in (0.05, 0.25, 0.5, 0.75, 1.0)}
         v_var4 = variant(grads, 4.0, dq.ALLOC_THRESHOLD, exact)
         v_uni4 = variant(grads, 4.0, dq.ALLOC_UNIFORM, exact)
         gen = torch.Generator(device=dev).manual_seed(12345)
@@ -238,7 +241,7 @@ def main():
                    "wire_bits_per_coord": b + 0.625, "mxfp8_wire_bits_per_coord": 8.25,
                    "stats_traffic_ratio": 8.0 / (256 * 2), "class_counts": info["class_counts"],
                    "vnmse_mxfp6_e3m2": v_mx6a, "vnmse_mxfp6_e2m3": v_mx6b, "vnmse_mxfp4_e2m1": v_mx4,
-                   "vnmse_mean_corrected_alloc": v_mc,
+                   "vnmse_mean_corrected_alloc": v_mc, "vnmse_by_level_shape_eps": v_eps,
                    "vnmse_4bit_variable": v_var4, "vnmse_4bit_uniform": v_uni4,
                    "vnmse_4bit_variable_shuffled": v_var4_s, "vnmse_4bit_uniform_shuffled": v_uni4_s}
         del exact
