@@ -112,6 +112,7 @@ struct or_ctx {
     uint32_t round;
     int32_t rounding;
     int32_t alloc;
+    int32_t own;
     double eps;
     float L[3][256];
     float W[3][256];
@@ -169,6 +170,8 @@ void or_destroy(or_ctx *c) {
 void or_set_seed(or_ctx *c, uint64_t seed) { c->seed = seed; }
 void or_set_round(or_ctx *c, uint32_t round) { c->round = round; }
 void or_set_rounding(or_ctx *c, int32_t mode) { c->rounding = mode; }
+void or_set_own(or_ctx *c, int32_t mode) { c->own = mode; }
+
 void or_set_alloc(or_ctx *c, int32_t mode) {
     c->alloc = mode;
     c->allocated = 0;
@@ -404,6 +407,13 @@ int64_t or_region_bytes(const or_ctx *c, int64_t m, int64_t part, int64_t counts
     layout_part(c, m, part, &pl);
     if (counts_out) for (int k = 0; k < 3; k++) counts_out[k] = pl.cnt[k];
     return pl.bytes;
+}
+
+/* index of a super-group in its part (stream order) */
+static int64_t part_index(const part_layout *pl, int k, int64_t idx_in_class) {
+    int64_t before = 0;
+    for (int t = 0; t < k; t++) before += pl->cnt[t];
+    return before + idx_in_class;
 }
 
 /* pointers to the pieces of one super-group inside a region */
@@ -672,9 +682,16 @@ int or_hop(or_ctx *c, int32_t worker, int32_t step, const uint8_t *region_in,
     if (worker < 0 || worker >= c->n) return -1;
     sched_part sp;
     if (hop_part(c, worker, step, &sp)) return -1;
-    const int want_packed = (c->topo == OR_BUTTERFLY && step >= 2);
-    if (want_packed != (local_kind == OR_PACKED)) return -1;
+    /* butterfly levels >= 2 take the worker's own kept child as the local
+       operand: packed, or fp32 partial sums under OR_OWN_F32 */
+    const int own32 = c->topo == OR_BUTTERFLY && c->own == OR_OWN_F32;
+    const int want_own = (c->topo == OR_BUTTERFLY && step >= 2);
+    const int own_kind = own32 ? OR_PARTIAL : OR_PACKED;
+    if (want_own != (local_kind == own_kind)) return -1;
+    if (!want_own && local_kind != OR_BF16 && local_kind != OR_F32) return -1;
     if (sp.two_children && !out1) return -1;
+    /* the child this worker keeps for the next level (the other is sent) */
+    const int keep = sp.two_children ? (worker >> (c->log2n - step - 1)) & 1 : -1;
     part_layout pl, ch[2];
     layout_part(c, sp.m, sp.part, &pl);
     if (sp.two_children) {
@@ -701,9 +718,21 @@ int or_hop(or_ctx *c, int32_t worker, int32_t step, const uint8_t *region_in,
             slot_of(&pl, (uint8_t *)local, k, refs[t].idx, &sown);
             read_sg(c, &sown, xown);
             for (int i = 0; i < OR_SG; i++) y[i] = xin[i] + xown[i];
+        } else if (local_kind == OR_PARTIAL) {
+            /* the worker's own fp32 partial sums, part order */
+            const float *own = (const float *)local + part_index(&pl, k, refs[t].idx) * OR_SG;
+            for (int i = 0; i < OR_SG; i++) y[i] = xin[i] + own[i];
         } else {
             for (int i = 0; i < OR_SG; i++)
                 y[i] = xin[i] + (load_elem(local, local_kind, j * OR_SG + i) - mu);
+        }
+        const int h = sp.two_children ? (refs[t].pos < ch[0].lo[k] + ch[0].cnt[k] ? 0 : 1) : 0;
+        if (own32 && h == keep) {
+            /* the kept child stays fp32: no quantisation */
+            float *dst = (float *)(h == 0 ? out0 : out1) +
+                         part_index(&ch[h], k, refs[t].pos - ch[h].lo[k]) * OR_SG;
+            memcpy(dst, y, sizeof(y));
+            continue;
         }
         uint16_t d[OR_SG];
         or_dithers(c->seed, c->round, j, c->rounding, worker, c->n, event, d);
@@ -712,9 +741,7 @@ int or_hop(or_ctx *c, int32_t worker, int32_t step, const uint8_t *region_in,
         encode_sg(y, Q_OF_CLASS[k], c->L[k], c->W[k], d, codes, &s, cg);
         sg_slot so;
         if (sp.two_children) {
-            int64_t split = ch[0].lo[k] + ch[0].cnt[k];
-            if (refs[t].pos < split) slot_of(&ch[0], out0, k, refs[t].pos - ch[0].lo[k], &so);
-            else slot_of(&ch[1], out1, k, refs[t].pos - ch[1].lo[k], &so);
+            slot_of(&ch[h], h == 0 ? out0 : out1, k, refs[t].pos - ch[h].lo[k], &so);
         } else {
             slot_of(&pl, out0, k, refs[t].idx, &so);
         }
@@ -792,11 +819,15 @@ int or_allreduce(or_ctx *c, const void *const *grads, int32_t dtype, float *out)
         free(buf);
         return rc;
     }
-    /* butterfly: per worker a compress buffer and two child buffers per level */
+    /* butterfly: per worker a compress buffer and two child buffers per level
+       (sized for an fp32 partial when the kept child stays fp32) */
     const int L = c->log2n;
-    uint8_t *buf = (uint8_t *)calloc((size_t)n * (size_t)(1 + 2 * L) * (size_t)RB, 1);
-#define BF_CMP(w) (buf + ((size_t)(w) * (1 + 2 * L)) * (size_t)RB)
-#define BF_OUT(w, s, h) (buf + ((size_t)(w) * (1 + 2 * L) + 1 + 2 * ((s) - 1) + (h)) * (size_t)RB)
+    const int own32 = c->own == OR_OWN_F32;
+    const int64_t RBp = (c->J / 2 + 3) * OR_SG * (int64_t)sizeof(float);
+    const int64_t RB2 = own32 && RBp > RB ? RBp : RB;
+    uint8_t *buf = (uint8_t *)calloc((size_t)n * (size_t)(1 + 2 * L) * (size_t)RB2, 1);
+#define BF_CMP(w) (buf + ((size_t)(w) * (1 + 2 * L)) * (size_t)RB2)
+#define BF_OUT(w, s, h) (buf + ((size_t)(w) * (1 + 2 * L) + 1 + 2 * ((s) - 1) + (h)) * (size_t)RB2)
     for (int w = 0; w < n && !rc; w++)
         rc = or_compress(c, w, 1, grads[w], dtype, BF_CMP(w), NULL, 0);
     for (int s = 1; s <= L && !rc; s++) {
@@ -805,7 +836,7 @@ int or_allreduce(or_ctx *c, const void *const *grads, int32_t dtype, float *out)
             const int keep = (w >> (L - s)) & 1; /* which child of the level s-1 part */
             const uint8_t *in = (s == 1) ? BF_CMP(partner) : BF_OUT(partner, s - 1, keep);
             const void *local = (s == 1) ? grads[w] : (const void *)BF_OUT(w, s - 1, keep);
-            const int kind = (s == 1) ? dtype : OR_PACKED;
+            const int kind = (s == 1) ? dtype : (own32 ? OR_PARTIAL : OR_PACKED);
             rc = or_hop(c, w, s, in, local, kind, BF_OUT(w, s, 0),
                         s < L ? BF_OUT(w, s, 1) : NULL, NULL, 0);
         }

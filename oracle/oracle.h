@@ -37,7 +37,14 @@ extern "C" {
 
 enum { OR_SG = 256, OR_GROUP = 16, OR_NGROUPS = 16 };
 enum { OR_RING = 0, OR_BUTTERFLY = 1 };
-enum { OR_BF16 = 0, OR_F32 = 1, OR_PACKED = 2 };
+enum { OR_BF16 = 0, OR_F32 = 1, OR_PACKED = 2, OR_PARTIAL = 3 };
+/* The worker's own operand at butterfly levels >= 2 (scribe notes: no
+ * intermediate tensors, so the method re-quantises the half it keeps;
+ * the fp32 variant keeps that half unquantised, as fp32 partial sums in the
+ * part's stream order, 256 floats per super-group):
+ *   OR_OWN_PACKED  the kept child is a packed region, local kind OR_PACKED
+ *   OR_OWN_F32     the kept child is fp32, local kind OR_PARTIAL */
+enum { OR_OWN_PACKED = 0, OR_OWN_F32 = 1 };
 enum { OR_CORRELATED = 0, OR_INDEPENDENT = 1 };
 /* Allocation variants (pith.science review, referee major 1: the thresholds
  * see F_j although the quantised values have squared norm F_j - n S mu_j^2,
@@ -71,6 +78,7 @@ void or_set_round(or_ctx *c, uint32_t round);
 void or_set_rounding(or_ctx *c, int32_t mode);
 void or_set_eps(or_ctx *c, double eps);
 void or_set_alloc(or_ctx *c, int32_t mode);
+void or_set_own(or_ctx *c, int32_t mode);
 
 /* Stage 1: per-worker statistics, called in rank order 0..n-1. */
 int or_stats(or_ctx *c, int32_t worker, const void *grad, int32_t dtype);

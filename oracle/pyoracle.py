@@ -11,9 +11,10 @@ import numpy as np
 from . import build as _build
 
 RING, BUTTERFLY = 0, 1
-BF16, F32, PACKED = 0, 1, 2
+BF16, F32, PACKED, PARTIAL = 0, 1, 2, 3
 CORRELATED, INDEPENDENT = 0, 1
 ALLOC_THRESHOLD, ALLOC_MEAN_CORRECTED, ALLOC_UNIFORM = 0, 1, 2
+OWN_PACKED, OWN_F32 = 0, 1
 Q_OF_CLASS = (2, 4, 8)
 
 _lib = None
@@ -39,6 +40,7 @@ def lib():
             "or_set_round": (None, [vp, u32]),
             "or_set_rounding": (None, [vp, i32]),
             "or_set_alloc": (None, [vp, i32]),
+            "or_set_own": (None, [vp, i32]),
             "or_get_alloc_key": (None, [vp, vp]),
             "or_set_eps": (None, [vp, f64]),
             "or_stats": (C.c_int, [vp, i32, vp, i32]),
@@ -168,7 +170,7 @@ class Oracle:
     """One simulated round on the CPU (mirrors the stage order of the library)."""
 
     def __init__(self, n_coords, n_workers, topology=RING, avg_bits=5.0, seed=1, rnd=0,
-                 rounding=CORRELATED, eps=None, alloc=ALLOC_THRESHOLD):
+                 rounding=CORRELATED, eps=None, alloc=ALLOC_THRESHOLD, own=OWN_PACKED):
         self.d = int(n_coords)
         self.n = int(n_workers)
         self.topology = int(topology)
@@ -182,6 +184,7 @@ class Oracle:
         if eps is not None:
             lib().or_set_eps(self.h, float(eps))
         lib().or_set_alloc(self.h, int(alloc))
+        lib().or_set_own(self.h, int(own))
         self.log2n = max(0, (self.n - 1).bit_length())
 
     def __del__(self):
@@ -256,8 +259,9 @@ class Oracle:
         _check(lib().or_compress(self.h, int(w), int(step), _p(g), _dtype_code(g), _p(region),
                                  _p(f), 0 if f is None else f.size), "compress")
 
-    def hop(self, w, step, region_in, local, out0, out1=None, filt=None):
-        kind = PACKED if local.dtype == np.uint8 else _dtype_code(local)
+    def hop(self, w, step, region_in, local, out0, out1=None, filt=None, partial=False):
+        """partial=True: `local` is the worker's fp32 partial sums (own-fp32 variant)."""
+        kind = PARTIAL if partial else (PACKED if local.dtype == np.uint8 else _dtype_code(local))
         f = None if filt is None else np.ascontiguousarray(filt, np.int64)
         _check(lib().or_hop(self.h, int(w), int(step), _p(region_in), _p(local), kind, _p(out0),
                             _p(out1), _p(f), 0 if f is None else f.size), "hop")

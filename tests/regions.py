@@ -89,3 +89,17 @@ def unpack(raw, q):
     bits = np.unpackbits(raw, bitorder="little").reshape(256, q)
     weights = (1 << np.arange(q)).astype(np.uint16)
     return (bits.astype(np.uint16) * weights).sum(1).astype(np.uint8)
+
+
+def part_positions(C, m, c):
+    """Stream positions of part c of m, in the part's order (class by class)."""
+    return [p for lo, n in part_ranges(C, m, c) for p in range(lo, lo + n)]
+
+
+def decode_sg(region, C, m, c, pos, levels):
+    """Decoded values of stream position pos: fl(fl(c_g s) L[code]) per
+    coordinate; levels[k] is the level table of class k."""
+    k, codes, s, cg = sg_fields(region, C, m, c, pos)
+    sigma = (cg.astype(np.float32) * np.float32(s)).astype(np.float32)
+    L = np.asarray(levels[k], np.float32)
+    return (np.repeat(sigma, 16) * L[codes]).astype(np.float32)

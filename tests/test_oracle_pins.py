@@ -947,3 +947,70 @@ def test_mx_schedule_composition_fp4():
     q = lambda v: po.mx_roundtrip(po.MX_E2M1, v)
     out = po.Oracle(256 * J, 2, po.RING).mx_allreduce(po.MX_E2M1, g)
     assert np.array_equal(out, np.concatenate([q(q(g[0][:h]) + g[1][:h]), q(q(g[1][h:]) + g[0][h:])]))
+
+
+# ---------------------------------------------------------------------------
+# butterfly variant: the worker's kept half stays fp32 (no re-quantisation by
+# its owner at levels >= 2), against the method's packed own child
+# ---------------------------------------------------------------------------
+
+def test_own_fp32_partial_variant():
+    rng = np.random.default_rng(41)
+    n, J = 8, 96
+    scale = np.repeat(10.0 ** rng.uniform(-4, 0, J), 256)
+    gs = [(scale * rng.standard_normal(256 * J)).astype(np.float32) for _ in range(n)]
+    exact = np.sum([g.astype(np.float64) for g in gs], axis=0)
+
+    def vnmse(own, rounds):
+        err = 0.0
+        for r in rounds:
+            o = po.Oracle(256 * J, n, po.BUTTERFLY, 5.0, rnd=r, rounding=po.INDEPENDENT, own=own)
+            err += ((o.allreduce(gs) - exact) ** 2).sum()
+        return err / len(rounds) / (exact ** 2).sum()
+
+    packed, f32 = vnmse(po.OWN_PACKED, range(6)), vnmse(po.OWN_F32, range(6))
+    # the kept half skips one quantisation per level >= 2: lower error
+    assert f32 < 0.85 * packed
+    # n = 2 has no level >= 2: the variants coincide bit for bit
+    o1 = po.Oracle(256 * J, 2, po.BUTTERFLY, 5.0, own=po.OWN_PACKED).allreduce(gs[:2])
+    o2 = po.Oracle(256 * J, 2, po.BUTTERFLY, 5.0, own=po.OWN_F32).allreduce(gs[:2])
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+    # the ring never uses an own operand: unchanged
+    r1 = po.Oracle(256 * J, 4, po.RING, 5.0, own=po.OWN_PACKED).allreduce(gs[:4])
+    r2 = po.Oracle(256 * J, 4, po.RING, 5.0, own=po.OWN_F32).allreduce(gs[:4])
+    assert np.array_equal(r1.view(np.uint32), r2.view(np.uint32))
+
+
+def test_own_fp32_partial_is_the_exact_partial_sum():
+    """n = 4: after level 1 the kept child holds x_in + (g - mu) without any
+    rounding beyond the one fp32 add, and level 2 adds the partner's decoded
+    region to it."""
+    rng = np.random.default_rng(42)
+    n, J = 4, 40
+    gs = [rng.standard_normal(256 * J).astype(np.float32) for _ in range(n)]
+    o = po.Oracle(256 * J, n, po.BUTTERFLY, 5.0, own=po.OWN_F32)
+    for w in range(n):
+        o.stats(w, gs[w])
+    o.allocate()
+    o.reorder()
+    perm, _ = o.perm()
+    _, _, mu = o.stats_arrays()
+    C = o.class_counts()
+    RB = o.worst_region_bytes()
+    cmp = {w: np.zeros(RB, np.uint8) for w in range(n)}
+    for w in range(n):
+        o.compress(w, 1, gs[w], cmp[w])
+    # worker 0 at level 1: part 0 of 2; keeps child 0 (bit of w at level 1 is 0)
+    w, partner = 0, 2
+    sent = np.zeros(RB, np.uint8)
+    kept = np.zeros((J, 256), np.float32)
+    o.hop(w, 1, cmp[partner], gs[w], kept, sent)
+    # expected kept values: decoded incoming + (g - mu) for the SGs of child (4, 0)
+    levels = [po.levels(q)[0] for q in (2, 4, 8)]
+    for t, p in enumerate(R.part_positions(C, 4, 0)):
+        j = perm[p]
+        dec = R.decode_sg(cmp[partner], C, 2, 0, p, levels)
+        y = (dec + (gs[w][256 * j:256 * j + 256] - mu[j]).astype(np.float32)).astype(np.float32)
+        assert np.array_equal(kept[t].view(np.uint32), y.view(np.uint32))
+    # and the sent child is a packed region of part (4, 1)
+    assert R.region_bytes(C, 4, 1) > 0 and sent[:R.region_bytes(C, 4, 1)].any()
