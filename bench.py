@@ -233,6 +233,21 @@ def main():
         shuffled = [g[perm] for g in grads]
         exact_s = exact[perm]
         del perm
+        own32 = None
+        if topo == dq.BUTTERFLY:
+            # the butterfly variant whose kept half stays fp32: error and round time
+            p32 = dq.Plan(wl.d, wl.n, topo, budget, seed=wl.rounding_seed, own=dq.OWN_F32, device=dev)
+            a32 = torch.empty(p32.arena_bytes(), dtype=torch.uint8, device=dev)
+            o32 = torch.empty_like(out)
+            p32.allreduce(grads, out=o32, arena=a32)
+            torch.cuda.synchronize()
+            t32 = time.perf_counter()
+            for _ in range(3):
+                p32.allreduce(grads, out=o32, arena=a32)
+            torch.cuda.synchronize()
+            own32 = {"vnmse": vnmse(o32), "ms_per_round": 1e3 * (time.perf_counter() - t32) / 3,
+                     "arena_bytes": p32.arena_bytes(), "arena_bytes_packed_own": plan.arena_bytes()}
+            del p32, a32, o32
         v_var4_s = variant(shuffled, 4.0, dq.ALLOC_THRESHOLD, exact_s)
         v_uni4_s = variant(shuffled, 4.0, dq.ALLOC_UNIFORM, exact_s)
         del shuffled, exact_s
@@ -242,6 +257,7 @@ def main():
                    "stats_traffic_ratio": 8.0 / (256 * 2), "class_counts": info["class_counts"],
                    "vnmse_mxfp6_e3m2": v_mx6a, "vnmse_mxfp6_e2m3": v_mx6b, "vnmse_mxfp4_e2m1": v_mx4,
                    "vnmse_mean_corrected_alloc": v_mc, "vnmse_by_level_shape_eps": v_eps,
+                   "own_fp32_butterfly": own32,
                    "vnmse_4bit_variable": v_var4, "vnmse_4bit_uniform": v_uni4,
                    "vnmse_4bit_variable_shuffled": v_var4_s, "vnmse_4bit_uniform_shuffled": v_uni4_s}
         del exact

@@ -38,6 +38,7 @@ struct dq_plan {
     uint32_t round = 0;
     int32_t rounding = DQ_ROUND_CORRELATED;
     int32_t alloc = DQ_ALLOC_THRESHOLD;
+    int32_t own = DQ_OWN_PACKED;           // butterfly own operand at levels >= 2
     bool timing = false;
     uint32_t timing_kinds = (1u << DQ_K_COUNT) - 1u;   // kinds timed while timing is on
     double eps = kDefaultEps;                          // level shape
@@ -191,6 +192,7 @@ int local_of_kind(int32_t kind) {
     if (kind == DQ_BF16) return kLocalBF16;
     if (kind == DQ_F32) return kLocalF32;
     if (kind == DQ_PACKED) return kLocalPacked;
+    if (kind == DQ_F32_PARTIAL) return kLocalPartial;
     return -1;
 }
 
@@ -223,8 +225,16 @@ ArenaPlan arena_plan(const dq_plan *p) {
             add(2);
             for (int s = 1; s <= p->L; s++) {
                 if (s < p->L) {
-                    add((int64_t)1 << (s + 1));
-                    add((int64_t)1 << (s + 1));
+                    const int64_t m = (int64_t)1 << (s + 1);
+                    const int keep = (w >> (p->L - s - 1)) & 1;
+                    for (int h = 0; h < 2; h++) {
+                        if (p->own == DQ_OWN_F32 && h == keep) {
+                            ap.off.push_back(ap.total);
+                            ap.total += dq_partial_bytes_max(p, m);
+                        } else {
+                            add(m);
+                        }
+                    }
                 } else {
                     add(p->n);
                 }
@@ -315,6 +325,10 @@ dq_status dq_plan_set_u64(dq_plan *p, int32_t option, uint64_t v) {
             if (v == 0 || v >= (1ull << DQ_K_COUNT)) return DQ_EINVAL;
             p->timing_kinds = (uint32_t)v;
             return DQ_OK;
+        case DQ_OPT_OWN:
+            if (v != DQ_OWN_PACKED && v != DQ_OWN_F32) return DQ_EINVAL;
+            p->own = (int32_t)v;
+            return DQ_OK;
         case DQ_OPT_ALLOC:
             if (v != DQ_ALLOC_THRESHOLD && v != DQ_ALLOC_MEAN_CORRECTED && v != DQ_ALLOC_UNIFORM)
                 return DQ_EINVAL;
@@ -352,6 +366,11 @@ dq_status dq_workspace_layout(const dq_plan *p, dq_layout *out) {
     if (!p || !out) return DQ_ENULL;
     *out = p->lay;
     return DQ_OK;
+}
+
+size_t dq_partial_bytes_max(const dq_plan *p, int64_t m) {
+    if (!p || m < 1 || m > p->n || (p->n % m) != 0) return 0;
+    return align_up((size_t)max_part_sg(p, m) * kSG * sizeof(float), kAlign);
 }
 
 size_t dq_region_bytes_max(const dq_plan *p, int64_t m) {
@@ -493,9 +512,13 @@ dq_status dq_hop(dq_plan *p, int32_t w, int32_t step, const void *in, const void
     if (!p->reordered) return DQ_ESTATE;
     SchedPart sp;
     if (w < 0 || w >= p->n || !hop_part(p, w, step, sp)) return DQ_EINVAL;
-    const bool want_packed = p->topo == DQ_BUTTERFLY && step >= 2;
-    if (want_packed != (local_kind == DQ_PACKED)) return DQ_EINVAL;
-    if (local_kind != DQ_BF16 && local_kind != DQ_F32 && local_kind != DQ_PACKED) return DQ_EINVAL;
+    // butterfly levels >= 2 take the worker's own kept child: packed, or fp32
+    // partial sums under DQ_OWN_F32
+    const bool own32 = p->topo == DQ_BUTTERFLY && p->own == DQ_OWN_F32;
+    const bool want_own = p->topo == DQ_BUTTERFLY && step >= 2;
+    const int32_t own_kind = own32 ? DQ_F32_PARTIAL : DQ_PACKED;
+    if (want_own != (local_kind == own_kind)) return DQ_EINVAL;
+    if (!want_own && local_kind != DQ_BF16 && local_kind != DQ_F32) return DQ_EINVAL;
     if (sp.two_children && !out1) return DQ_ENULL;
     if (!aligned(in, 16) || !aligned(local, 16) || !aligned(out0, 16) ||
         (sp.two_children && !aligned(out1, 16)))
@@ -507,20 +530,25 @@ dq_status dq_hop(dq_plan *p, int32_t w, int32_t step, const void *in, const void
     a.part_in = part_entry(p, sp.m, sp.part);
     a.region_in = static_cast<const uint8_t *>(in);
     if (local_kind == DQ_PACKED) a.region_own = static_cast<const uint8_t *>(local);
+    else if (local_kind == DQ_F32_PARTIAL) a.partial_in = static_cast<const float *>(local);
     else a.grad = local;
-    const int kindk = local_kind == DQ_PACKED ? DQ_K_HOP_PACKED : DQ_K_HOP_GRAD;
+    const int kindk = want_own ? DQ_K_HOP_PACKED : DQ_K_HOP_GRAD;
+    // the child this worker keeps for the next level (own-fp32: written as fp32)
+    const int keep = (own32 && sp.two_children) ? (w >> (p->L - step - 1)) & 1 : -1;
     // one launch per output region: the part itself, or each of its two children
     const int nout = sp.two_children ? 2 : 1;
     hipError_t e = hipSuccess;
     for (int h = 0; h < nout && e == hipSuccess; h++) {
         const int64_t m_out = sp.two_children ? 2 * sp.m : sp.m;
         const int64_t c_out = sp.two_children ? 2 * sp.part + h : sp.part;
+        void *dst = h == 0 ? out0 : out1;
         a.part_out = part_entry(p, m_out, c_out);
-        a.out = static_cast<uint8_t *>(h == 0 ? out0 : out1);
+        a.out = h == keep ? nullptr : static_cast<uint8_t *>(dst);
+        a.partial_out = h == keep ? static_cast<float *>(dst) : nullptr;
         Launch L;
         e = timed_begin(p, kindk, m_out, c_out, s, L);
         if (e == hipSuccess)
-            e = launch_codec(a, kHop, local_of_kind(local_kind), max_part_sg(p, m_out), s);
+            e = launch_codec(a, h == keep ? kPartial : kHop, local_of_kind(local_kind), max_part_sg(p, m_out), s);
         if (e == hipSuccess) e = timed_end(p, L, s);
     }
     return hip_status(e);
@@ -593,7 +621,7 @@ dq_status dq_allreduce(dq_plan *p, const void *const *grads, int32_t kind, void 
             const int keep = (w >> (L - s)) & 1;
             const void *in = s == 1 ? (const void *)cmp(partner) : (const void *)lvl(partner, s - 1, keep);
             const void *local = s == 1 ? grads[w] : (const void *)lvl(w, s - 1, keep);
-            const int32_t lk = s == 1 ? kind : DQ_PACKED;
+            const int32_t lk = s == 1 ? kind : (p->own == DQ_OWN_F32 ? DQ_F32_PARTIAL : DQ_PACKED);
             if ((st = dq_hop(p, w, s, in, local, lk, lvl(w, s, 0), s < L ? lvl(w, s, 1) : nullptr,
                              stream)) != DQ_OK)
                 return st;

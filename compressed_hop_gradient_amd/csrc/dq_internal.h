@@ -28,7 +28,9 @@ struct Ctrl {
     int32_t nonfinite;
 };
 
-enum Mode { kCompress = 0, kHop = 1, kFinalize = 2 };
+// kPartial: a hop whose output (the child a worker keeps, own-fp32 variant)
+// is the fp32 partial sum itself instead of a packed region
+enum Mode { kCompress = 0, kHop = 1, kFinalize = 2, kPartial = 3 };
 
 // Layout of one part (m, c) of the bitwidth-sorted stream and of its region;
 // computed once per round on the device (k_part_table) for every part the
@@ -43,7 +45,9 @@ struct PartInfo {
     int64_t offg;      // region byte offset of the UINT8 group codes
     int64_t bytes;     // region size
 };
-enum Local { kLocalNone = 0, kLocalBF16 = 1, kLocalF32 = 2, kLocalPacked = 3 };
+// kLocalPartial: the worker's own fp32 partial sums, 256 floats per
+// super-group in the input part's order
+enum Local { kLocalNone = 0, kLocalBF16 = 1, kLocalF32 = 2, kLocalPacked = 3, kLocalPartial = 4 };
 
 // arguments of one codec launch (compress / hop / finalize).  A launch covers
 // the super-groups of one output part (m_out, part_out); the input regions
@@ -60,6 +64,8 @@ struct CodecArgs {
     const void *grad;                        // local gradient (bf16 / f32)
     const uint8_t *region_in;                // incoming region (hop, finalize)
     const uint8_t *region_own;               // own packed region (butterfly level >= 2)
+    const float *partial_in;                 // own fp32 partial sums (own-fp32 variant)
+    float *partial_out;                      // kPartial output: fp32 partial sums of the part
     uint8_t *out;                            // output region of (m_out, part_out)
     float *out_f32;                          // finalize output, original order
     float n_workers_f;                       // finalize: fl(n * mu)

@@ -280,7 +280,7 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po,
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             const float e0 = bf16_lo(hw[i]) - mu, e1 = bf16_hi(hw[i]) - mu;
-            if constexpr (MODE == kHop) {
+            if constexpr (MODE == kHop || MODE == kPartial) {
                 y[2 * i] = y[2 * i] + e0;
                 y[2 * i + 1] = y[2 * i + 1] + e1;
             } else {
@@ -297,7 +297,7 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po,
             const float e[4] = {f.x - mu, f.y - mu, f.z - mu, f.w - mu};
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                if constexpr (MODE == kHop) y[4 * v + i] = y[4 * v + i] + e[i];
+                if constexpr (MODE == kHop || MODE == kPartial) y[4 * v + i] = y[4 * v + i] + e[i];
                 else y[4 * v + i] = e[i];
             }
         }
@@ -306,7 +306,25 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po,
         decode_group<Q, K>(Own, t_in, idx_in, g, T, own);
 #pragma unroll
         for (int i = 0; i < 16; i++) y[i] = y[i] + own[i];
+    } else if constexpr (LOCAL == kLocalPartial) {
+        const float4 *src = reinterpret_cast<const float4 *>(a.partial_in + ((uint64_t)t_in * kSG + (uint32_t)g * kGroup));
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            const float4 f = src[v];
+            y[4 * v] = y[4 * v] + f.x;
+            y[4 * v + 1] = y[4 * v + 1] + f.y;
+            y[4 * v + 2] = y[4 * v + 2] + f.z;
+            y[4 * v + 3] = y[4 * v + 3] + f.w;
+        }
     }
+
+    if constexpr (MODE == kPartial) {
+        // the kept child of the own-fp32 variant: store y, no quantisation
+        float4 *dst = reinterpret_cast<float4 *>(a.partial_out + ((uint64_t)t * kSG + (uint32_t)g * kGroup));
+#pragma unroll
+        for (int v = 0; v < 4; v++) dst[v] = make_float4(y[4 * v], y[4 * v + 1], y[4 * v + 2], y[4 * v + 3]);
+        return;
+    } else {
 
     // ---- encode ----
     float amax = 0.0f;
@@ -368,6 +386,7 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po,
     store_codes<Q>(out_codes + (idx * (32u * Q) + (uint32_t)g * (2u * Q)), w);
     const_cast<uint8_t *>(Out.g)[16u * t + (uint32_t)g] = (uint8_t)c;
     if (g == 0) *reinterpret_cast<float *>(const_cast<uint8_t *>(Out.s) + 4u * t) = s;
+    }   // MODE != kPartial
 }
 
 template <int MODE, int LOCAL>
@@ -1162,6 +1181,10 @@ hipError_t launch_codec(const CodecArgs &a, int mode, int local, int64_t max_sg,
     else if (mode == kHop && local == kLocalBF16) hipLaunchKernelGGL((k_codec<kHop, kLocalBF16>), grid, block, 0, s, a);
     else if (mode == kHop && local == kLocalF32) hipLaunchKernelGGL((k_codec<kHop, kLocalF32>), grid, block, 0, s, a);
     else if (mode == kHop && local == kLocalPacked) hipLaunchKernelGGL((k_codec<kHop, kLocalPacked>), grid, block, 0, s, a);
+    else if (mode == kHop && local == kLocalPartial) hipLaunchKernelGGL((k_codec<kHop, kLocalPartial>), grid, block, 0, s, a);
+    else if (mode == kPartial && local == kLocalBF16) hipLaunchKernelGGL((k_codec<kPartial, kLocalBF16>), grid, block, 0, s, a);
+    else if (mode == kPartial && local == kLocalF32) hipLaunchKernelGGL((k_codec<kPartial, kLocalF32>), grid, block, 0, s, a);
+    else if (mode == kPartial && local == kLocalPartial) hipLaunchKernelGGL((k_codec<kPartial, kLocalPartial>), grid, block, 0, s, a);
     else if (mode == kFinalize) hipLaunchKernelGGL(k_finalize, grid, block, 0, s, a);
     else return hipErrorInvalidValue;
     return hipGetLastError();

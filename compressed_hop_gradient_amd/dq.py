@@ -16,9 +16,10 @@ LIB_PATH = os.path.join(_PKG, "libdq.so")
 DQ_OK, DQ_EINVAL, DQ_EBUDGET, DQ_ESTATE, DQ_EWORKSPACE, DQ_ENULL, DQ_EHIP, DQ_ENONFINITE = \
     0, -1, -2, -3, -4, -5, -6, -7
 RING, BUTTERFLY = 0, 1
-BF16, F32, PACKED = 0, 1, 2
+BF16, F32, PACKED, F32_PARTIAL = 0, 1, 2, 3
+OWN_PACKED, OWN_F32 = 0, 1
 CORRELATED, INDEPENDENT = 0, 1
-OPT_SEED, OPT_ROUND, OPT_ROUNDING, OPT_TIMING, OPT_ALLOC, OPT_TIMING_KINDS = 0, 1, 2, 3, 4, 5
+OPT_SEED, OPT_ROUND, OPT_ROUNDING, OPT_TIMING, OPT_ALLOC, OPT_TIMING_KINDS, OPT_OWN = 0, 1, 2, 3, 4, 5, 6
 ALLOC_THRESHOLD, ALLOC_MEAN_CORRECTED, ALLOC_UNIFORM = 0, 1, 2
 MX_FP8_E4M3, MX_FP6_E3M2, MX_FP6_E2M3, MX_FP4_E2M1 = 0, 1, 2, 3
 OPT_EPS = 0   # dq_option_f64
@@ -75,6 +76,7 @@ _SIGS = {
     "dq_mxfp8_allreduce": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
                                      C.c_void_p, C.c_void_p]),
     "dq_mx_arena_bytes": (C.c_size_t, [C.c_void_p]),
+    "dq_partial_bytes_max": (C.c_size_t, [C.c_void_p, C.c_int64]),
     "dq_plan_set_f64": (C.c_int, [C.c_void_p, C.c_int32, C.c_double]),
     "dq_mx_allreduce": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
                                   C.c_void_p, C.c_void_p]),
@@ -138,7 +140,8 @@ class Plan:
     """
 
     def __init__(self, n_coords, n_workers, topology=RING, avg_bits=5.0, seed=1, rnd=0,
-                 rounding=CORRELATED, device="cuda", timing=False, alloc=ALLOC_THRESHOLD, eps=None):
+                 rounding=CORRELATED, device="cuda", timing=False, alloc=ALLOC_THRESHOLD, eps=None,
+                 own=OWN_PACKED):
         self.d = int(n_coords)
         self.n = int(n_workers)
         self.J = self.d // 256
@@ -153,6 +156,7 @@ class Plan:
         self.set(OPT_ROUNDING, rounding)
         self.set(OPT_TIMING, 1 if timing else 0)
         self.set(OPT_ALLOC, alloc)
+        self.set(OPT_OWN, own)
         if eps is not None:
             _check(lib().dq_plan_set_f64(self.h, OPT_EPS, float(eps)), "dq_plan_set_f64")
         nbytes = lib().dq_workspace_bytes(self.h)
@@ -186,9 +190,12 @@ class Plan:
         _check(lib().dq_compress(self.h, int(worker), int(step), _ptr(grad), _kind(grad),
                                  _ptr(region_out), _stream(stream)), "dq_compress")
 
-    def hop(self, worker, step, region_in, local, out0, out1=None, stream=None):
+    def hop(self, worker, step, region_in, local, out0, out1=None, stream=None, local_kind=None):
+        """local_kind: F32_PARTIAL for the own fp32 partial sums (OWN_F32);
+        otherwise taken from the tensor's dtype."""
+        kind = _kind(local) if local_kind is None else int(local_kind)
         _check(lib().dq_hop(self.h, int(worker), int(step), _ptr(region_in), _ptr(local),
-                            _kind(local), _ptr(out0), None if out1 is None else _ptr(out1),
+                            kind, _ptr(out0), None if out1 is None else _ptr(out1),
                             _stream(stream)), "dq_hop")
 
     def finalize(self, part, region, out, stream=None):
@@ -201,6 +208,9 @@ class Plan:
     # ---- whole round -----------------------------------------------------
     def region_bytes_max(self, m):
         return int(lib().dq_region_bytes_max(self.h, int(m)))
+
+    def partial_bytes_max(self, m):
+        return int(lib().dq_partial_bytes_max(self.h, int(m)))
 
     def new_region(self, m, device="cuda"):
         return torch.zeros(self.region_bytes_max(m), dtype=torch.uint8, device=device)

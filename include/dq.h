@@ -65,7 +65,18 @@ typedef enum dq_topology { DQ_RING = 0, DQ_BUTTERFLY = 1 } dq_topology;
 
 /* element kinds: gradients are DQ_BF16 or DQ_F32; the local operand of a
  * butterfly hop at level >= 2 is DQ_PACKED (the worker's own region) */
-typedef enum dq_kind { DQ_BF16 = 0, DQ_F32 = 1, DQ_PACKED = 2 } dq_kind;
+typedef enum dq_kind {
+    DQ_BF16 = 0, DQ_F32 = 1, DQ_PACKED = 2,
+    DQ_F32_PARTIAL = 3   /* the worker's own fp32 partial sums (DQ_OWN_F32 butterfly) */
+} dq_kind;
+
+/* The worker's own operand at butterfly levels >= 2.  The method adds the
+ * child region the worker itself re-quantised at the level before (scribe
+ * notes: no intermediate tensors).  DQ_OWN_F32 keeps that child as fp32
+ * partial sums (256 floats per super-group, in the part's stream order):
+ * one quantisation less per level, 4 bytes per coordinate of HBM instead of
+ * (b + 0.625)/8.  A variant for measurement, off by default. */
+typedef enum dq_own { DQ_OWN_PACKED = 0, DQ_OWN_F32 = 1 } dq_own;
 
 typedef enum dq_rounding {
     DQ_ROUND_CORRELATED = 0,   /* one shared dither per coordinate, staggered by worker rank */
@@ -94,8 +105,9 @@ typedef enum dq_option {
     DQ_OPT_TIMING = 3,     /* 1: time every launch with HIP events on its stream */
     DQ_OPT_ALLOC = 4,      /* dq_alloc (default DQ_ALLOC_THRESHOLD); takes effect at the
                               next dq_allocate */
-    DQ_OPT_TIMING_KINDS = 5  /* bit mask of dq_kernel_kind: which launches DQ_OPT_TIMING
+    DQ_OPT_TIMING_KINDS = 5, /* bit mask of dq_kernel_kind: which launches DQ_OPT_TIMING
                                 times (default all); fewer events, less overhead */
+    DQ_OPT_OWN = 6           /* dq_own (default DQ_OWN_PACKED); set between rounds */
 } dq_option;
 
 typedef struct dq_plan dq_plan;
@@ -178,6 +190,9 @@ dq_status dq_workspace_layout(const dq_plan *plan, dq_layout *out);
 /* Worst-case bytes of the region of any part of m (m = n for the ring,
  * m = 2^s for butterfly level s, m = 1 for n = 1).  0 if m is not valid. */
 size_t dq_region_bytes_max(const dq_plan *plan, int64_t m);
+/* Worst-case bytes of the fp32 partial sums of one part of m (DQ_OWN_F32):
+ * 1024 bytes per super-group, 256-byte multiple; 0 on bad arguments. */
+size_t dq_partial_bytes_max(const dq_plan *plan, int64_t m);
 
 /* ---- stages (enqueue on `stream`) ----------------------------------------- */
 
@@ -211,6 +226,9 @@ dq_status dq_compress(dq_plan *plan, int32_t worker, int32_t step, const void *d
  *     s = 1, the worker's own packed region of the same part (DQ_PACKED) at
  *     s >= 2; for s < L the output is the two child regions (parts 2c and
  *     2c+1 of 2^(s+1)) in d_region_out0 and d_region_out1, for s = L one region.
+ *   Under DQ_OWN_F32 the child the worker keeps (index (w >> (L-s-1)) & 1) is
+ *     written as fp32 partial sums (>= dq_partial_bytes_max of its m) instead of
+ *     a region, and the local at s >= 2 is that buffer (kind DQ_F32_PARTIAL).
  * d_region_in is the region of the same part produced by the previous hop (or
  * compress) of the sending worker.  Errors: DQ_ENULL, DQ_EINVAL, DQ_ESTATE,
  * DQ_EHIP. */

@@ -404,3 +404,93 @@ def test_timing_counts_coordinates():
     assert t["finalize"]["coords"] == J * 256
     assert t["stats"]["coords"] == 8 * J * 256
     assert all(v["ms"] >= 0 for v in t.values())
+
+
+# ---------------------------------------------------------------------------
+# butterfly variant: the kept child stays fp32 (DQ_OWN_F32)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,rounding", [(2, dq.CORRELATED), (4, dq.INDEPENDENT), (8, dq.CORRELATED),
+                                        (16, dq.INDEPENDENT)])
+def test_own_fp32_round_bit_exact(n, rounding):
+    _need_gpu()
+    J = 777
+    grads = _scaled("gemma", J, workers=range(n))
+    p = dq.Plan(256 * J, n, dq.BUTTERFLY, 5.0, rounding=rounding, own=dq.OWN_F32)
+    out = p.allreduce(grads)
+    torch.cuda.synchronize()
+    o = po.Oracle(256 * J, n, po.BUTTERFLY, 5.0, rounding=rounding, own=po.OWN_F32)
+    ref = o.allreduce(_grads_np(grads))
+    assert np.array_equal(_bits(out.cpu().numpy()), _bits(ref))
+
+
+def test_own_fp32_every_step_bit_exact():
+    """n = 8, step by step: every sent region and every kept fp32 partial of
+    every hop, GPU against oracle."""
+    _need_gpu()
+    n, J = 8, 1031
+    L = 3
+    grads = _scaled("gemma", J, workers=range(n))
+    gnp = _grads_np(grads)
+    plan = dq.Plan(256 * J, n, dq.BUTTERFLY, 5.0, own=dq.OWN_F32)
+    orc = po.Oracle(256 * J, n, po.BUTTERFLY, 5.0, own=po.OWN_F32)
+    for w in range(n):
+        plan.stats(w, grads[w])
+        orc.stats(w, gnp[w])
+    plan.allocate(); orc.allocate()
+    plan.reorder(); orc.reorder()
+    torch.cuda.synchronize()
+    C = orc.class_counts()
+    RB = orc.worst_region_bytes()
+    g_out, o_out = {}, {}
+    for w in range(n):
+        gr = plan.new_region(2)
+        orr = np.zeros(RB, np.uint8)
+        plan.compress(w, 1, grads[w], gr)
+        orc.compress(w, 1, gnp[w], orr)
+        g_out[(w, 0)], o_out[(w, 0)] = [gr], [orr]
+    for s in range(1, L + 1):
+        for w in range(n):
+            partner = w ^ (n >> s)
+            keep_prev = (w >> (L - s)) & 1
+            if s == 1:
+                g_in, o_in, g_loc, o_loc = g_out[(partner, 0)][0], o_out[(partner, 0)][0], grads[w], gnp[w]
+            else:
+                g_in, o_in = g_out[(partner, s - 1)][keep_prev], o_out[(partner, s - 1)][keep_prev]
+                g_loc, o_loc = g_out[(w, s - 1)][keep_prev], o_out[(w, s - 1)][keep_prev]
+            c = w >> (L - s)
+            if s < L:
+                keep = (w >> (L - s - 1)) & 1
+                m = 2 ** (s + 1)
+                gs_, os_ = [], []
+                for h in range(2):
+                    if h == keep:
+                        gs_.append(torch.full((plan.partial_bytes_max(m) // 4,), float("nan"),
+                                              dtype=torch.float32, device=DEV))
+                        os_.append(np.full(plan.partial_bytes_max(m) // 4, np.nan, np.float32))
+                    else:
+                        gs_.append(plan.new_region(m))
+                        os_.append(np.zeros(RB, np.uint8))
+            else:
+                gs_, os_ = [plan.new_region(n)], [np.zeros(RB, np.uint8)]
+            kind = None if s == 1 else dq.F32_PARTIAL
+            plan.hop(w, s, g_in, g_loc, gs_[0], gs_[1] if len(gs_) > 1 else None, local_kind=kind)
+            orc.hop(w, s, o_in, o_loc, os_[0], os_[1] if len(os_) > 1 else None, partial=(s > 1))
+            torch.cuda.synchronize()
+            for h, (gb, ob) in enumerate(zip(gs_, os_)):
+                m_out, c_out = (2 ** (s + 1), 2 * c + h) if s < L else (n, c)
+                if s < L and h == keep:
+                    N = sum(cnt for _, cnt in R.part_ranges(C, m_out, c_out))
+                    a = gb.cpu().numpy()[:256 * N]
+                    assert np.array_equal(_bits(a), _bits(ob[:256 * N])), f"partial w{w} s{s}"
+                else:
+                    size = R.region_bytes(C, m_out, c_out)
+                    assert np.array_equal(gb[:size].cpu().numpy(), ob[:size]), f"region w{w} s{s} h{h}"
+            g_out[(w, s)], o_out[(w, s)] = gs_, os_
+    out_g = torch.empty(256 * J, dtype=torch.float32, device=DEV)
+    out_o = np.zeros(256 * J, np.float32)
+    for w in range(n):
+        plan.finalize(plan.final_part(w), g_out[(w, L)][0], out_g)
+        orc.finalize(orc.final_part(w), o_out[(w, L)][0], out_o)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(out_g.cpu().numpy()), _bits(out_o))
