@@ -88,7 +88,12 @@ __device__ __forceinline__ void philox4x32_10(uint32_t &x0, uint32_t &x1, uint32
 // part in 2^24 of A, and one ulp of s adds 255 ulps to it); the second guard
 // keeps the definition's loop semantics without a loop.
 __device__ __forceinline__ float scale_unit(float A) {
-    float s = A / 255.0f;
+    // fl(A / 255) by a product and two FMAs: equal to the correctly rounded
+    // quotient for every non-negative finite A (exhaustive CPU check)
+    constexpr float R = 1.0f / 255.0f;
+    const float y = A * R;
+    const float rem = __builtin_fmaf(-y, 255.0f, A);
+    float s = __builtin_fmaf(rem, R, y);
     if (255.0f * s < A) s = __uint_as_float(__float_as_uint(s) + 1u);
     if (255.0f * s < A) s = __uint_as_float(__float_as_uint(s) + 1u);
     return s;

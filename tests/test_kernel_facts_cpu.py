@@ -8,6 +8,8 @@ tables of the reading (generated here and by the oracle), on the CPU.
    and 7 mantissa bits of |v| (all |v| < 2^-12 share one bucket): each bucket
    holds at most one level boundary, for level shapes eps from 0.01 to 1.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -70,3 +72,26 @@ def test_higher_tiny_bucket_would_fail_small_shapes():
     L, _ = po.levels(8, 0.1)
     assert ((L > 0) & (L < np.float32(2.0 ** -9))).sum() >= 2
     assert ((L > 0) & (L < np.float32(2.0 ** -12))).sum() <= 1
+
+
+def test_scale_unit_division_by_255_with_two_fmas(tmp_path):
+    """The codec kernels compute the scale unit's first guess fl(A / 255) as
+    y = fl(A R), r = fma(-y, 255, A), q = fma(r, R, y) with R = fl(1/255).
+    Checked here for every non-negative finite fp32 A (all 255 exponent
+    fields, subnormals included; about 20 s, most of it in the subnormal
+    binades)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = os.path.join(os.path.dirname(__file__), "native", "div255_check.c")
+    exe = str(tmp_path / "div255_check")
+    # hardware FMA where the host has it (glibc's fmaf is correctly rounded either way)
+    if subprocess.run([cc, "-O2", "-mfma", "-ffp-contract=off", "-o", exe, src, "-lm"]).returncode:
+        subprocess.run([cc, "-O2", "-ffp-contract=off", "-o", exe, src, "-lm"], check=True)
+    ranges = ["0", "254"]
+    out = subprocess.run([exe] + ranges, check=True, capture_output=True, text=True).stdout.split()
+    checked, bad = int(out[0]), int(out[1])
+    assert checked == 255 * (1 << 23)
+    assert bad == 0
