@@ -180,6 +180,27 @@ def main():
     plan.allreduce(grads, out=out, arena=arena, stream=stream)
     tim = plan.timing()
     info = plan.info()
+    # the same round captured once in a HIP graph and replayed (no per-launch
+    # host work): what a launch-bound configuration gains from graphs
+    plan.set(dq.OPT_TIMING, 0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        plan.allreduce(grads, out=out, arena=arena)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan.allreduce(grads, out=out, arena=arena)
+    graph.replay()
+    torch.cuda.synchronize()
+    tg = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_ms = 1e3 * (time.perf_counter() - tg) / args.steps
+    del graph
+    plan.set(dq.OPT_TIMING, 1)
     secs = t1 - t0
     ms_per_step = 1e3 * secs / args.steps
     dar_coords = args.steps * (tim["hop_grad"]["coords"] + tim["hop_packed"]["coords"])
@@ -326,6 +347,7 @@ def main():
                      "valu_issue": measured_valu("hop_grad", src_hash)},
         "dar_kernel_coords_per_s": (hg["coords"] / (hg["ms"] * 1e-3)) if hg["ms"] > 0 else None,
         "kernels": kernels,
+        "graph_replay_ms_per_step": graph_ms,
         "quality": quality,
         "copy_calibration": copy_cal,
     }
