@@ -408,7 +408,7 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po,
 }
 
 template <int MODE, int LOCAL>
-__global__ __launch_bounds__(256) void k_codec(CodecArgs a) {
+__global__ __launch_bounds__(kCodecThreads) void k_codec(CodecArgs a) {
     __shared__ __align__(16) SharedTables T;
     const LevelTables &lev = a.tab->lev;
     for (int i = threadIdx.x; i < 256; i += blockDim.x) {
@@ -436,7 +436,7 @@ __global__ __launch_bounds__(256) void k_codec(CodecArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane & 15, row = lane >> 4;
     const uint32_t N = (uint32_t)Po.N, pre1 = (uint32_t)Po.pre[1], pre2 = (uint32_t)Po.pre[2];
-    for (uint32_t base = blockIdx.x * kSGPerBlock; base < N; base += gridDim.x * kSGPerBlock) {
+    for (uint32_t base = blockIdx.x * kCodecSGPerBlock; base < N; base += gridDim.x * kCodecSGPerBlock) {
         const uint32_t t = base + wave * 4 + row;
         if (t >= N) continue;
         if (t < pre1) codec_sg<2, MODE, LOCAL>(a, Po, Pi, In, Own, Out, t, g, T);
@@ -1203,24 +1203,25 @@ static int64_t device_cus() {
     return cus;
 }
 
-// Grid of a codec launch over n super-groups: whole "waves" of 6 blocks per CU
-// (the hop kernels' occupancy; a partial last wave leaves CUs idle at the
-// end): one wave while that gives each block fewer than about 18 grid-stride
-// iterations, else two.  Measured on launches of 1.6e5 to 2e6 super-groups
-// (BERT-, LLaMA- and Gemma-shaped parts): one wave up to 3e5, two from 4.9e5
-// on, 3-9% faster than a fixed grid at the small end; the compress kernel,
-// which could hold 8 blocks per CU, is also fastest this way.
-constexpr int64_t kCodecBlocksPerCU = 6;
+// Grid of a codec launch over n super-groups: whole "waves" of 3 blocks of 8
+// waves per CU (the hop kernels' occupancy, 6 waves per SIMD; a partial last
+// wave leaves CUs idle at the end): one wave while that gives each block
+// fewer than about 18 grid-stride iterations, else two.  Measured on launches
+// of 1.6e5 to 2e6 super-groups (BERT-, LLaMA- and Gemma-shaped parts): one
+// wave up to 3e5, two from 4.9e5 on, 3-9% faster than a fixed grid at the
+// small end; the compress kernel, which could hold more, is also fastest this
+// way.  512-thread blocks beat 256 (half the per-block table copies) by 1-3%.
+constexpr int64_t kCodecBlocksPerCU = 3;
 static dim3 codec_grid(int64_t n) {
     const int64_t wave = device_cus() * kCodecBlocksPerCU;
-    int64_t waves = (n + wave * kSGPerBlock * 6) / (wave * kSGPerBlock * 12);
+    int64_t waves = (n + wave * kCodecSGPerBlock * 6) / (wave * kCodecSGPerBlock * 12);
     waves = waves < 1 ? 1 : (waves > 2 ? 2 : waves);
-    return dim3(grid_for(n, kSGPerBlock, wave * waves));
+    return dim3(grid_for(n, kCodecSGPerBlock, wave * waves));
 }
 
 template <int MODE, int LOCAL>
 static hipError_t launch_codec_t(const CodecArgs &a, int64_t max_sg, hipStream_t s) {
-    hipLaunchKernelGGL((k_codec<MODE, LOCAL>), codec_grid(max_sg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_codec<MODE, LOCAL>), codec_grid(max_sg), dim3(kCodecThreads), 0, s, a);
     return hipGetLastError();
 }
 
