@@ -505,8 +505,11 @@ dq_status dq_compress(dq_plan *p, int32_t w, int32_t step, const void *grad, int
     return hip_status(e);
 }
 
-dq_status dq_hop(dq_plan *p, int32_t w, int32_t step, const void *in, const void *local,
-                 int32_t local_kind, void *out0, void *out1, void *stream) {
+namespace {
+
+// dq_hop, and dq_hop_finalize when final_out is set (the schedule's last step)
+dq_status hop_impl(dq_plan *p, int32_t w, int32_t step, const void *in, const void *local,
+                   int32_t local_kind, void *out0, void *out1, float *final_out, void *stream) {
     if (!p || !in || !local || !out0) return DQ_ENULL;
     if (!p->ws) return DQ_EWORKSPACE;
     if (!p->reordered) return DQ_ESTATE;
@@ -522,6 +525,10 @@ dq_status dq_hop(dq_plan *p, int32_t w, int32_t step, const void *in, const void
     if (sp.two_children && !out1) return DQ_ENULL;
     if (!aligned(in, 16) || !aligned(local, 16) || !aligned(out0, 16) ||
         (sp.two_children && !aligned(out1, 16)))
+        return DQ_EINVAL;
+    // the fused final step: only where the hop's part is a final part
+    if (final_out && (sp.two_children || sp.m != p->n || (p->topo == DQ_RING && step != p->n - 1) ||
+                      !aligned(final_out, 16)))
         return DQ_EINVAL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     CodecArgs a;
@@ -545,13 +552,27 @@ dq_status dq_hop(dq_plan *p, int32_t w, int32_t step, const void *in, const void
         a.part_out = part_entry(p, m_out, c_out);
         a.out = h == keep ? nullptr : static_cast<uint8_t *>(dst);
         a.partial_out = h == keep ? static_cast<float *>(dst) : nullptr;
+        a.out_f32 = final_out;
+        const int mode = h == keep ? kPartial : (final_out ? kHopFinal : kHop);
         Launch L;
         e = timed_begin(p, kindk, m_out, c_out, s, L);
-        if (e == hipSuccess)
-            e = launch_codec(a, h == keep ? kPartial : kHop, local_of_kind(local_kind), max_part_sg(p, m_out), s);
+        if (e == hipSuccess) e = launch_codec(a, mode, local_of_kind(local_kind), max_part_sg(p, m_out), s);
         if (e == hipSuccess) e = timed_end(p, L, s);
     }
     return hip_status(e);
+}
+
+}  // namespace
+
+dq_status dq_hop(dq_plan *p, int32_t w, int32_t step, const void *in, const void *local,
+                 int32_t local_kind, void *out0, void *out1, void *stream) {
+    return hop_impl(p, w, step, in, local, local_kind, out0, out1, nullptr, stream);
+}
+
+dq_status dq_hop_finalize(dq_plan *p, int32_t w, int32_t step, const void *in, const void *local,
+                          int32_t local_kind, void *region_out, float *out, void *stream) {
+    if (!out) return DQ_ENULL;
+    return hop_impl(p, w, step, in, local, local_kind, region_out, nullptr, out, stream);
 }
 
 dq_status dq_finalize(dq_plan *p, int64_t part, const void *region, float *out, void *stream) {
@@ -599,14 +620,14 @@ dq_status dq_allreduce(dq_plan *p, const void *const *grads, int32_t kind, void 
         auto slot = [&](int w, int t) { return A + ap.off[(size_t)(t & 1) * n + w]; };
         for (int w = 0; w < n; w++)
             if ((st = dq_compress(p, w, 0, grads[w], kind, slot(w, 0), stream)) != DQ_OK) return st;
+        // the last step's hops also write the decoded sum (no separate finalize)
         for (int t = 1; t < n; t++)
-            for (int w = 0; w < n; w++)
-                if ((st = dq_hop(p, w, t, slot((w - 1 + n) % n, t - 1), grads[w], kind, slot(w, t),
-                                 nullptr, stream)) != DQ_OK)
-                    return st;
-        for (int w = 0; w < n; w++)
-            if ((st = dq_finalize(p, dq_final_part(p, w), slot(w, n - 1), out, stream)) != DQ_OK)
-                return st;
+            for (int w = 0; w < n; w++) {
+                const void *in = slot((w - 1 + n) % n, t - 1);
+                st = t < n - 1 ? dq_hop(p, w, t, in, grads[w], kind, slot(w, t), nullptr, stream)
+                               : dq_hop_finalize(p, w, t, in, grads[w], kind, slot(w, t), out, stream);
+                if (st != DQ_OK) return st;
+            }
         return DQ_OK;
     }
     const int L = p->L;
@@ -622,13 +643,11 @@ dq_status dq_allreduce(dq_plan *p, const void *const *grads, int32_t kind, void 
             const void *in = s == 1 ? (const void *)cmp(partner) : (const void *)lvl(partner, s - 1, keep);
             const void *local = s == 1 ? grads[w] : (const void *)lvl(w, s - 1, keep);
             const int32_t lk = s == 1 ? kind : (p->own == DQ_OWN_F32 ? DQ_F32_PARTIAL : DQ_PACKED);
-            if ((st = dq_hop(p, w, s, in, local, lk, lvl(w, s, 0), s < L ? lvl(w, s, 1) : nullptr,
-                             stream)) != DQ_OK)
-                return st;
+            st = s < L ? dq_hop(p, w, s, in, local, lk, lvl(w, s, 0), lvl(w, s, 1), stream)
+                       : dq_hop_finalize(p, w, s, in, local, lk, lvl(w, s, 0), out, stream);
+            if (st != DQ_OK) return st;
         }
     }
-    for (int w = 0; w < n; w++)
-        if ((st = dq_finalize(p, dq_final_part(p, w), lvl(w, L, 0), out, stream)) != DQ_OK) return st;
     return DQ_OK;
 }
 

@@ -31,8 +31,10 @@ struct Ctrl {
 };
 
 // kPartial: a hop whose output (the child a worker keeps, own-fp32 variant)
-// is the fp32 partial sum itself instead of a packed region
-enum Mode { kCompress = 0, kHop = 1, kFinalize = 2, kPartial = 3 };
+// is the fp32 partial sum itself instead of a packed region.
+// kHopFinal: the last hop of a schedule; writes its region and also the
+// decoded final sum of its part (what finalize would compute from it).
+enum Mode { kCompress = 0, kHop = 1, kFinalize = 2, kPartial = 3, kHopFinal = 4 };
 
 // Layout of one part (m, c) of the bitwidth-sorted stream and of its region;
 // computed once per round on the device (k_part_table) for every part the

@@ -278,7 +278,7 @@ template <int Q, int MODE, int LOCAL>
 __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po, const PartInfo &Pi,
                                          const RegionBase &In, const RegionBase &Own,
                                          const RegionBase &Out, uint32_t t, int g,
-                                         const SharedTables &T) {
+                                         const SharedTables &T, float *stage_row) {
     constexpr int K = Q == 2 ? 0 : (Q == 4 ? 1 : 2);
     const uint32_t idx = t - (uint32_t)Po.pre[K];        // index in the class, output part
     const uint32_t pos = (uint32_t)Po.lo[K] + idx;       // stream position
@@ -298,7 +298,7 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po,
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             const float e0 = bf16_lo(hw[i]) - mu, e1 = bf16_hi(hw[i]) - mu;
-            if constexpr (MODE == kHop || MODE == kPartial) {
+            if constexpr (MODE == kHop || MODE == kPartial || MODE == kHopFinal) {
                 y[2 * i] = y[2 * i] + e0;
                 y[2 * i + 1] = y[2 * i + 1] + e1;
             } else {
@@ -315,7 +315,7 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po,
             const float e[4] = {f.x - mu, f.y - mu, f.z - mu, f.w - mu};
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                if constexpr (MODE == kHop || MODE == kPartial) y[4 * v + i] = y[4 * v + i] + e[i];
+                if constexpr (MODE == kHop || MODE == kPartial || MODE == kHopFinal) y[4 * v + i] = y[4 * v + i] + e[i];
                 else y[4 * v + i] = e[i];
             }
         }
@@ -404,11 +404,41 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po,
     store_codes<Q>(out_codes + (idx * (32u * Q) + (uint32_t)g * (2u * Q)), w);
     const_cast<uint8_t *>(Out.g)[16u * t + (uint32_t)g] = (uint8_t)c;
     if (g == 0) *reinterpret_cast<float *>(const_cast<uint8_t *>(Out.s) + 4u * t) = s;
+
+    if constexpr (MODE == kHopFinal) {
+        // the decoded final sum of these coordinates, as finalize computes it
+        // from the region just written: fl(fl(c s) L[code]) + fl(n mu).  The
+        // row's 1 KB goes through LDS so that every store instruction writes
+        // 256 contiguous bytes of the super-group (lane g: floats 64v + 4g).
+        const float add = a.n_workers_f * mu;
+        f32x4_t *stage = reinterpret_cast<f32x4_t *>(stage_row);
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            float x[4];
+#pragma unroll
+            for (int ii = 0; ii < 4; ii++) {
+                const int i = 4 * v + ii;
+                const uint32_t code = (w[(i * Q) / 32] >> ((i * Q) % 32)) & ((1u << Q) - 1u);
+                x[ii] = sigma * level_of<Q>(T, code) + add;
+            }
+            stage[4 * g + v] = f32x4_t{x[0], x[1], x[2], x[3]};
+        }
+        // the row lives in one wave: a wavefront-scope fence orders the LDS
+        // writes above before the other lanes' reads below
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        f32x4_t *dst = reinterpret_cast<f32x4_t *>(a.out_f32 + (uint64_t)j * kSG);
+#pragma unroll
+        for (int v = 0; v < 4; v++) __builtin_nontemporal_store(stage[16 * v + g], dst + 16 * v + g);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    }
     }   // MODE != kPartial
 }
 
 template <int MODE, int LOCAL>
-__global__ __launch_bounds__(kCodecThreads) void k_codec(CodecArgs a) {
+// three 512-thread blocks per CU: six waves per SIMD, at most 80 VGPRs
+__global__ __launch_bounds__(kCodecThreads) __attribute__((amdgpu_waves_per_eu(6))) void k_codec(CodecArgs a) {
     __shared__ __align__(16) SharedTables T;
     const LevelTables &lev = a.tab->lev;
     for (int i = threadIdx.x; i < 256; i += blockDim.x) {
@@ -436,12 +466,16 @@ __global__ __launch_bounds__(kCodecThreads) void k_codec(CodecArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane & 15, row = lane >> 4;
     const uint32_t N = (uint32_t)Po.N, pre1 = (uint32_t)Po.pre[1], pre2 = (uint32_t)Po.pre[2];
+    // the fused final hop stages each row's decoded super-group here
+    constexpr int kStageRows = MODE == kHopFinal ? kCodecThreads / 16 : 1;
+    __shared__ __align__(16) float stage[kStageRows][kSG];
+    float *stage_row = stage[MODE == kHopFinal ? threadIdx.x / 16 : 0];
     for (uint32_t base = blockIdx.x * kCodecSGPerBlock; base < N; base += gridDim.x * kCodecSGPerBlock) {
         const uint32_t t = base + wave * 4 + row;
         if (t >= N) continue;
-        if (t < pre1) codec_sg<2, MODE, LOCAL>(a, Po, Pi, In, Own, Out, t, g, T);
-        else if (t < pre2) codec_sg<4, MODE, LOCAL>(a, Po, Pi, In, Own, Out, t, g, T);
-        else codec_sg<8, MODE, LOCAL>(a, Po, Pi, In, Own, Out, t, g, T);
+        if (t < pre1) codec_sg<2, MODE, LOCAL>(a, Po, Pi, In, Own, Out, t, g, T, stage_row);
+        else if (t < pre2) codec_sg<4, MODE, LOCAL>(a, Po, Pi, In, Own, Out, t, g, T, stage_row);
+        else codec_sg<8, MODE, LOCAL>(a, Po, Pi, In, Own, Out, t, g, T, stage_row);
     }
 }
 
@@ -1235,6 +1269,10 @@ hipError_t launch_codec(const CodecArgs &a, int mode, int local, int64_t max_sg,
     if (mode == kPartial && local == kLocalBF16) return launch_codec_t<kPartial, kLocalBF16>(a, max_sg, s);
     if (mode == kPartial && local == kLocalF32) return launch_codec_t<kPartial, kLocalF32>(a, max_sg, s);
     if (mode == kPartial && local == kLocalPartial) return launch_codec_t<kPartial, kLocalPartial>(a, max_sg, s);
+    if (mode == kHopFinal && local == kLocalBF16) return launch_codec_t<kHopFinal, kLocalBF16>(a, max_sg, s);
+    if (mode == kHopFinal && local == kLocalF32) return launch_codec_t<kHopFinal, kLocalF32>(a, max_sg, s);
+    if (mode == kHopFinal && local == kLocalPacked) return launch_codec_t<kHopFinal, kLocalPacked>(a, max_sg, s);
+    if (mode == kHopFinal && local == kLocalPartial) return launch_codec_t<kHopFinal, kLocalPartial>(a, max_sg, s);
     if (mode == kFinalize) {
         // finalize streams at memory speed: 8 blocks per CU
         hipLaunchKernelGGL(k_finalize, dim3(grid_for(max_sg, kSGPerBlock, device_cus() * 8)), dim3(256), 0, s, a);

@@ -76,6 +76,8 @@ _SIGS = {
     "dq_mxfp8_allreduce": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
                                      C.c_void_p, C.c_void_p]),
     "dq_mx_arena_bytes": (C.c_size_t, [C.c_void_p]),
+    "dq_hop_finalize": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_int32,
+                                  C.c_void_p, C.c_void_p, C.c_void_p]),
     "dq_partial_bytes_max": (C.c_size_t, [C.c_void_p, C.c_int64]),
     "dq_plan_set_f64": (C.c_int, [C.c_void_p, C.c_int32, C.c_double]),
     "dq_mx_allreduce": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
@@ -197,6 +199,11 @@ class Plan:
         _check(lib().dq_hop(self.h, int(worker), int(step), _ptr(region_in), _ptr(local),
                             kind, _ptr(out0), None if out1 is None else _ptr(out1),
                             _stream(stream)), "dq_hop")
+
+    def hop_finalize(self, worker, step, region_in, local, region_out, out, stream=None, local_kind=None):
+        kind = _kind(local) if local_kind is None else int(local_kind)
+        _check(lib().dq_hop_finalize(self.h, int(worker), int(step), _ptr(region_in), _ptr(local), kind,
+                                     _ptr(region_out), _ptr(out), _stream(stream)), "dq_hop_finalize")
 
     def finalize(self, part, region, out, stream=None):
         _check(lib().dq_finalize(self.h, int(part), _ptr(region), _ptr(out), _stream(stream)),

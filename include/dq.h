@@ -236,6 +236,16 @@ dq_status dq_hop(dq_plan *plan, int32_t worker, int32_t step, const void *d_regi
                  const void *d_local, int32_t local_kind, void *d_region_out0,
                  void *d_region_out1, void *stream);
 
+/* The schedule's last hop fused with the finalize of its part: ring step
+ * n - 1, butterfly level L (n >= 2).  Writes the region exactly as dq_hop
+ * does (the bytes an all-gather would forward) and, in the same pass, the
+ * decoded sum of its part into d_out (float[n_coords], original order) --
+ * the values dq_finalize would compute from that region.  Errors: as dq_hop;
+ * DQ_EINVAL at any other step. */
+dq_status dq_hop_finalize(dq_plan *plan, int32_t worker, int32_t step, const void *d_region_in,
+                          const void *d_local, int32_t local_kind, void *d_region_out,
+                          float *d_out, void *stream);
+
 /* Decode the final region of part `part` (of m = n), add fl(n * mu), and write
  * its super-groups at their original positions of d_out (float[n_coords]).
  * The result is the sum over workers.  Errors: DQ_ENULL, DQ_EINVAL, DQ_ESTATE,

@@ -401,7 +401,8 @@ def test_timing_counts_coordinates():
     assert t["hop_grad"]["launches"] == 8 * 7
     assert t["hop_grad"]["coords"] == 7 * J * 256       # each ring step covers every SG once
     assert t["compress"]["coords"] == J * 256
-    assert t["finalize"]["coords"] == J * 256
+    # the last ring step's hops also decode the final sum: no finalize launch
+    assert t["finalize"]["launches"] == 0
     assert t["stats"]["coords"] == 8 * J * 256
     assert all(v["ms"] >= 0 for v in t.values())
 
@@ -494,3 +495,38 @@ def test_own_fp32_every_step_bit_exact():
         orc.finalize(orc.final_part(w), o_out[(w, L)][0], out_o)
     torch.cuda.synchronize()
     assert np.array_equal(_bits(out_g.cpu().numpy()), _bits(out_o))
+
+
+@pytest.mark.parametrize("n,topo", [(4, dq.RING), (8, dq.BUTTERFLY), (3, dq.RING)])
+def test_fused_final_hop_matches_hop_then_finalize(n, topo):
+    """dq_hop_finalize at the schedule's last step writes the region dq_hop
+    writes and the output dq_finalize computes from it; at other steps it is
+    refused."""
+    _need_gpu()
+    J = 515
+    grads = _scaled("gemma" if topo == dq.BUTTERFLY else "llama", J, workers=range(n))
+    r = Round(grads, topo)
+    r.stages()
+    r.check_stages()
+    r.run_hops(check_every=False)
+    out_ref = r.finalize()
+    L = n.bit_length() - 1
+    last = n - 1 if topo == dq.RING else L
+    out = torch.full((256 * J,), float("nan"), dtype=torch.float32, device=DEV)
+    for w in range(n):
+        if topo == dq.RING:
+            g_in, loc = r.g_reg[((w - 1) % n, last - 1)][0], grads[w]
+        else:
+            partner = w ^ (n >> last)
+            keep = (w >> (L - last)) & 1
+            g_in, loc = r.g_reg[(partner, last - 1)][keep], r.g_reg[(w, last - 1)][keep]
+        reg = r.plan.new_region(n)
+        r.plan.hop_finalize(w, last, g_in, loc, reg, out)
+        torch.cuda.synchronize()
+        part = r.plan.final_part(w)
+        size = R.region_bytes(r.C, n, part)
+        assert np.array_equal(reg[:size].cpu().numpy(), r.g_reg[(w, last)][0][:size].cpu().numpy())
+        if topo == dq.RING and last > 1:
+            with pytest.raises(dq.DQError):
+                r.plan.hop_finalize(w, last - 1, g_in, loc, reg, out)
+    assert np.array_equal(_bits(out.cpu().numpy()), _bits(out_ref))
