@@ -539,7 +539,7 @@ dq_status hop_impl(dq_plan *p, int32_t w, int32_t step, const void *in, const vo
     if (local_kind == DQ_PACKED) a.region_own = static_cast<const uint8_t *>(local);
     else if (local_kind == DQ_F32_PARTIAL) a.partial_in = static_cast<const float *>(local);
     else a.grad = local;
-    const int kindk = want_own ? DQ_K_HOP_PACKED : DQ_K_HOP_GRAD;
+    const int kindk = final_out ? DQ_K_HOP_FINAL : (want_own ? DQ_K_HOP_PACKED : DQ_K_HOP_GRAD);
     // the child this worker keeps for the next level (own-fp32: written as fp32)
     const int keep = (own32 && sp.two_children) ? (w >> (p->L - step - 1)) & 1 : -1;
     // one launch per output region: the part itself, or each of its two children

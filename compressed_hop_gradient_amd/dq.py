@@ -24,7 +24,7 @@ ALLOC_THRESHOLD, ALLOC_MEAN_CORRECTED, ALLOC_UNIFORM = 0, 1, 2
 MX_FP8_E4M3, MX_FP6_E3M2, MX_FP6_E2M3, MX_FP4_E2M1 = 0, 1, 2, 3
 OPT_EPS = 0   # dq_option_f64
 KERNEL_KINDS = ("stats", "allocate", "reorder", "compress", "hop_grad", "hop_packed",
-                "finalize", "mxfp8")
+                "finalize", "mxfp8", "hop_final")
 
 
 class dq_info(C.Structure):
@@ -40,7 +40,8 @@ class dq_layout(C.Structure):
 
 
 class dq_timing(C.Structure):
-    _fields_ = [("ms", C.c_double * 8), ("launches", C.c_int64 * 8), ("coords", C.c_int64 * 8)]
+    _fields_ = [("ms", C.c_double * len(KERNEL_KINDS)), ("launches", C.c_int64 * len(KERNEL_KINDS)),
+                ("coords", C.c_int64 * len(KERNEL_KINDS))]
 
 
 class DQError(RuntimeError):

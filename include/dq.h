@@ -141,7 +141,8 @@ typedef struct dq_layout {
 typedef enum dq_kernel_kind {
     DQ_K_STATS = 0, DQ_K_ALLOCATE = 1, DQ_K_REORDER = 2, DQ_K_COMPRESS = 3,
     DQ_K_HOP_GRAD = 4, DQ_K_HOP_PACKED = 5, DQ_K_FINALIZE = 6, DQ_K_MXFP8 = 7,
-    DQ_K_COUNT = 8
+    DQ_K_HOP_FINAL = 8,          /* dq_hop_finalize, either local kind */
+    DQ_K_COUNT = 9
 } dq_kernel_kind;
 
 typedef struct dq_timing {

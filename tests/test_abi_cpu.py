@@ -79,7 +79,8 @@ def test_options(lib):
     assert lib.dq_plan_set_u64(h, dq.OPT_ALLOC, 3) == dq.DQ_EINVAL
     assert lib.dq_plan_set_u64(h, dq.OPT_TIMING_KINDS, 1 << 4) == dq.DQ_OK
     assert lib.dq_plan_set_u64(h, dq.OPT_TIMING_KINDS, 0) == dq.DQ_EINVAL
-    assert lib.dq_plan_set_u64(h, dq.OPT_TIMING_KINDS, 1 << 8) == dq.DQ_EINVAL
+    assert lib.dq_plan_set_u64(h, dq.OPT_TIMING_KINDS, 1 << 8) == dq.DQ_OK
+    assert lib.dq_plan_set_u64(h, dq.OPT_TIMING_KINDS, 1 << len(dq.KERNEL_KINDS)) == dq.DQ_EINVAL
     assert lib.dq_plan_set_u64(h, 99, 0) == dq.DQ_EINVAL
     assert lib.dq_plan_set_u64(None, 0, 0) == dq.DQ_ENULL
     # level shape: (0, 1] and one level boundary per search bucket

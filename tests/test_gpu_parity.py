@@ -398,10 +398,12 @@ def test_timing_counts_coordinates():
     p.allreduce(grads)
     t = p.timing()
     J = p.J
-    assert t["hop_grad"]["launches"] == 8 * 7
-    assert t["hop_grad"]["coords"] == 7 * J * 256       # each ring step covers every SG once
+    assert t["hop_grad"]["launches"] == 8 * 6
+    assert t["hop_grad"]["coords"] == 6 * J * 256       # each ring step covers every SG once
     assert t["compress"]["coords"] == J * 256
     # the last ring step's hops also decode the final sum: no finalize launch
+    assert t["hop_final"]["launches"] == 8
+    assert t["hop_final"]["coords"] == J * 256
     assert t["finalize"]["launches"] == 0
     assert t["stats"]["coords"] == 8 * J * 256
     assert all(v["ms"] >= 0 for v in t.values())
