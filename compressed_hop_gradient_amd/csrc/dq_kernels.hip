@@ -50,9 +50,12 @@ __device__ __forceinline__ float dpp_mov(float x) {
                                                       0xF, 0xF, false));
 }
 
+// x from another lane of the row; 0 where no lane is read (never, for the
+// in-row permutations used here).  0 is the identity of an unsigned max, which
+// lets the compiler fold the move into the max as a DPP operand.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_mov_u(uint32_t x) {
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
 }
 
 // maximum over the 16 lanes of a DPP row (all lanes get the result).  The
@@ -140,7 +143,10 @@ __device__ __forceinline__ uint32_t search_levels(float v, const uint8_t *est_ta
     const uint32_t b = __float_as_uint(v);
     const uint32_t k = __builtin_elementwise_sub_sat((b >> 16) & 0x3FFFu, (uint32_t)kKeyBase);
     const uint32_t est = est_tab[(k << 1) | (b >> 31)];
-    const uint32_t r = est + (v >= cl[est + 1] ? 1u : 0u);
+    uint32_t r = est + (v >= cl[est + 1] ? 1u : 0u);
+    // keep r opaque: the code is then formed as r + (round up), one carry-add,
+    // rather than re-derived from est and both comparisons
+    asm("" : "+v"(r));
     const Pair p = lw[r];
     Lr = p.l;
     Wr = p.w;
@@ -150,7 +156,8 @@ __device__ __forceinline__ uint32_t search_levels(float v, const uint8_t *est_ta
 // 2-bit search: two compares against the inner levels c1 = L[1], c2 = L[2]
 __device__ __forceinline__ uint32_t search_levels2(float v, float c1, float c2, const Pair *lw,
                                                    float &Lr, float &Wr) {
-    const uint32_t r = (v >= c1 ? 1u : 0u) + (v >= c2 ? 1u : 0u);
+    uint32_t r = (v >= c1 ? 1u : 0u) + (v >= c2 ? 1u : 0u);
+    asm("" : "+v"(r));
     const Pair p = lw[r];
     Lr = p.l;
     Wr = p.w;
