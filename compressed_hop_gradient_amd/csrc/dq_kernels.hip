@@ -3,8 +3,9 @@
 // Everything here is HBM-streaming integer/fp32 work: no stage is a dense
 // contraction, so nothing uses MFMA.  Kernels are written for 64-lane
 // wavefronts:
-//   * stats: 32 lanes per super-group (SG), each lane one 128-bit load of 8
-//     bf16; the sum order is 8 sequential adds then an xor tree over 32 lanes;
+//   * stats: 16 lanes per super-group (SG), each lane two 128-bit loads of 8
+//     bf16 (partials l and l + 16); 8 sequential adds per partial, then the
+//     tree over the 32 partials (one in-lane step, four DPP row shifts);
 //   * codec (compress / hop / finalize): one 16-lane DPP row per SG, one lane
 //     per group of 16 coordinates, so group scales are per-lane scalars and the
 //     SG maximum is a 4-step DPP row reduction; 128-bit loads of codes and of
@@ -597,90 +598,128 @@ hipError_t launch_part_table(const unsigned long long *class_counts, int32_t n, 
 // statistics
 // ---------------------------------------------------------------------------
 
-// Tree step P_k <- P_k + P_{k+delta} for the lanes k < delta that matter; the
-// other lanes compute values nobody reads.  delta = 16 crosses DPP rows: a
-// ds_swizzle (xor 16 inside each 32-lane half); delta = 8, 4, 2, 1 are DPP row
-// shifts (lane i reads lane i + delta).
+// Lane l of a 16-lane DPP row holds the partials k = l and k = l + 16 of one
+// super-group (8 sequential adds each).  The tree step P_k <- P_k + P_{k+delta}
+// is then in-lane for delta = 16 and a DPP row shift (lane i reads lane i +
+// delta) for delta = 8, 4, 2, 1; lanes past the ones that matter compute values
+// nobody reads.  The result is in lane 0 of the row.
 template <int CTRL>
 __device__ __forceinline__ float dpp_shl(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
-__device__ __forceinline__ float tree32(float x) {
-    x = x + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));  // xor 16
+__device__ __forceinline__ float tree16(float x) {
     x = x + dpp_shl<0x108>(x);   // row_shl:8
     x = x + dpp_shl<0x104>(x);   // row_shl:4
     x = x + dpp_shl<0x102>(x);   // row_shl:2
     x = x + dpp_shl<0x101>(x);   // row_shl:1
-    return x;                    // valid in lane 0 of each 32-lane half
+    return x;
 }
 
-// Each wave handles kStatsPairs pairs of super-groups per iteration (32 lanes,
-// 8 values each, per super-group) so that several 128-bit loads per lane are
-// in flight before the reductions.
-constexpr int kStatsPairs = 4;
+// the raw bytes of partial k of super-group j (elements 8k .. 8k+7): one
+// 16-byte load of bf16, two of fp32; converted only when summed, so that the
+// loads of a whole iteration fit in registers
+template <int F32> struct Partial;
+template <> struct Partial<0> {
+    uint4 h;
+    __device__ __forceinline__ void load(const void *grad, int64_t j, int k) {
+        h = stream_load_u4(static_cast<const uint16_t *>(grad) + j * kSG + k * 8);
+    }
+    __device__ __forceinline__ void clear() { h = make_uint4(0u, 0u, 0u, 0u); }
+    __device__ __forceinline__ void values(float (&e)[8]) const {
+        e[0] = bf16_lo(h.x); e[1] = bf16_hi(h.x); e[2] = bf16_lo(h.y); e[3] = bf16_hi(h.y);
+        e[4] = bf16_lo(h.z); e[5] = bf16_hi(h.z); e[6] = bf16_lo(h.w); e[7] = bf16_hi(h.w);
+    }
+};
+template <> struct Partial<1> {
+    float4 f0, f1;
+    __device__ __forceinline__ void load(const void *grad, int64_t j, int k) {
+        const float *src = static_cast<const float *>(grad) + j * kSG + k * 8;
+        f0 = stream_load_f4(src);
+        f1 = stream_load_f4(src + 4);
+    }
+    __device__ __forceinline__ void clear() { f0 = f1 = make_float4(0.0f, 0.0f, 0.0f, 0.0f); }
+    __device__ __forceinline__ void values(float (&e)[8]) const {
+        e[0] = f0.x; e[1] = f0.y; e[2] = f0.z; e[3] = f0.w;
+        e[4] = f1.x; e[5] = f1.y; e[6] = f1.z; e[7] = f1.w;
+    }
+};
+
+template <int F32>
+__device__ __forceinline__ void partial_sums(const Partial<F32> &p, float &s, float &q) {
+    float e[8];
+    p.values(e);
+    s = e[0];
+    q = e[0] * e[0];
+#pragma unroll
+    for (int i = 1; i < 8; i++) {
+        s = s + e[i];
+        const float sq = e[i] * e[i];
+        q = q + sq;
+    }
+}
+
+// A wave takes 4 rows x kStatsIter super-groups per iteration.  The per-SG
+// results go through LDS to lanes 0..31, which fetch the earlier workers'
+// running sums and store the new ones with one coalesced access per array:
+// the sparse 4-byte accesses of one lane per row cost more than their bytes
+// (writes mixed into a read stream make the memory turn around).
+constexpr int kStatsIter = 8;
+constexpr int kStatsPerWave = 4 * kStatsIter;        // 32 super-groups
+constexpr int kStatsPerBlock = 4 * kStatsPerWave;    // 256-thread blocks
 
 template <int F32>
 __global__ __launch_bounds__(256) void k_stats(StatsArgs a) {
-    const int half = (threadIdx.x >> 5) & 1, wave = threadIdx.x >> 6, l = threadIdx.x & 31;
-    constexpr int per_block = 4 * 2 * kStatsPairs;
-    for (int64_t base = (int64_t)blockIdx.x * per_block; base < a.J;
-         base += (int64_t)gridDim.x * per_block) {
-        float e[kStatsPairs][8];
-        float prior_s[kStatsPairs], prior_q[kStatsPairs];
-        bool live[kStatsPairs];
+    const int row = (threadIdx.x >> 4) & 3, wave = threadIdx.x >> 6, l = threadIdx.x & 15;
+    const int lane = threadIdx.x & 63;
+    __shared__ float staged[4][2][kStatsPerWave];
+    for (int64_t base = (int64_t)blockIdx.x * kStatsPerBlock; base < a.J;
+         base += (int64_t)gridDim.x * kStatsPerBlock) {
+        const int64_t wbase = base + wave * kStatsPerWave;
+        Partial<F32> p0[kStatsIter], p1[kStatsIter];
 #pragma unroll
-        for (int u = 0; u < kStatsPairs; u++) {
-            const int64_t j = base + (wave * kStatsPairs + u) * 2 + half;
-            live[u] = j < a.J;
-            // the running sums of earlier workers are fetched with the data,
-            // so the read-modify-write costs no extra round trip
-            prior_s[u] = 0.0f;
-            prior_q[u] = 0.0f;
-            if (live[u] && l == 0 && !a.first) {
-                prior_s[u] = a.sum[j];
-                prior_q[u] = a.sumsq[j];
-            }
-            if (live[u]) {
-                if (F32) {
-                    const float *src = static_cast<const float *>(a.grad) + j * kSG + l * 8;
-                    const float4 f0 = stream_load_f4(src), f1 = stream_load_f4(src + 4);
-                    e[u][0] = f0.x; e[u][1] = f0.y; e[u][2] = f0.z; e[u][3] = f0.w;
-                    e[u][4] = f1.x; e[u][5] = f1.y; e[u][6] = f1.z; e[u][7] = f1.w;
-                } else {
-                    const uint4 h = stream_load_u4(static_cast<const uint16_t *>(a.grad) + j * kSG + l * 8);
-                    e[u][0] = bf16_lo(h.x); e[u][1] = bf16_hi(h.x); e[u][2] = bf16_lo(h.y); e[u][3] = bf16_hi(h.y);
-                    e[u][4] = bf16_lo(h.z); e[u][5] = bf16_hi(h.z); e[u][6] = bf16_lo(h.w); e[u][7] = bf16_hi(h.w);
-                }
+        for (int u = 0; u < kStatsIter; u++) {
+            const int64_t j = wbase + u * 4 + row;
+            if (j < a.J) {
+                p0[u].load(a.grad, j, l);
+                p1[u].load(a.grad, j, l + 16);
             } else {
-#pragma unroll
-                for (int i = 0; i < 8; i++) e[u][i] = 0.0f;
+                p0[u].clear();
+                p1[u].clear();
             }
         }
+        // lanes 0..31: the super-group wbase + lane, in the staged order
+        const int64_t jm = wbase + lane;
+        const bool mine = lane < kStatsPerWave && jm < a.J;
+        float prior_s = 0.0f, prior_q = 0.0f;
+        if (mine && !a.first) {
+            prior_s = a.sum[jm];
+            prior_q = a.sumsq[jm];
+        }
 #pragma unroll
-        for (int u = 0; u < kStatsPairs; u++) {
-            // 8 sequential adds per lane, then the tree over the 32 lanes
-            float s = e[u][0], q = e[u][0] * e[u][0];
-#pragma unroll
-            for (int i = 1; i < 8; i++) {
-                s = s + e[u][i];
-                const float sq = e[u][i] * e[u][i];
-                q = q + sq;
-            }
-            s = tree32(s);
-            q = tree32(q);
-            const int64_t j = base + (wave * kStatsPairs + u) * 2 + half;
-            if (live[u] && l == 0) {
-                float S = s, F = q;
-                if (!a.first) {
-                    S = prior_s[u] + s;
-                    F = prior_q[u] + q;
-                }
-                a.sum[j] = S;
-                a.sumsq[j] = F;
-                if (!(__builtin_isfinite(S) && __builtin_isfinite(F))) atomicOr(a.nonfinite, 1);
+        for (int u = 0; u < kStatsIter; u++) {
+            float sa, qa, sb, qb;
+            partial_sums(p0[u], sa, qa);
+            partial_sums(p1[u], sb, qb);
+            const float s = tree16(sa + sb), q = tree16(qa + qb);
+            if (l == 0) {
+                staged[wave][0][u * 4 + row] = s;
+                staged[wave][1][u * 4 + row] = q;
             }
         }
+        // the staging area belongs to this wave: a wavefront-scope fence orders
+        // the row leaders' writes before the reads of the other lanes
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        if (mine) {
+            const float s = staged[wave][0][lane], q = staged[wave][1][lane];
+            const float S = a.first ? s : prior_s + s, F = a.first ? q : prior_q + q;
+            __builtin_nontemporal_store(S, a.sum + jm);
+            __builtin_nontemporal_store(F, a.sumsq + jm);
+            if (!(__builtin_isfinite(S) && __builtin_isfinite(F))) atomicOr(a.nonfinite, 1);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
@@ -1200,7 +1239,7 @@ hipError_t launch_zero(uint32_t *p, int64_t n, hipStream_t s) {
 }
 
 hipError_t launch_stats(const StatsArgs &a, int f32, hipStream_t s) {
-    const dim3 grid(grid_for(a.J, 4 * 2 * kStatsPairs, kStreamGrid));
+    const dim3 grid(grid_for(a.J, kStatsPerBlock, 2 * kStreamGrid));
     if (f32) hipLaunchKernelGGL(k_stats<1>, grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL(k_stats<0>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
