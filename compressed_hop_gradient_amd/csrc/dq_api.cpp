@@ -653,6 +653,13 @@ dq_status dq_allreduce(dq_plan *p, const void *const *grads, int32_t kind, void 
 
 // ---- inspection --------------------------------------------------------------
 
+dq_status dq_check_reciprocal(uint32_t lo, uint32_t count, unsigned long long *d_mismatches, void *stream) {
+    if (!d_mismatches) return DQ_ENULL;
+    if ((uint64_t)lo + count > 0x100000000ull) return DQ_EINVAL;
+    if (count == 0) return DQ_OK;
+    return hip_status(launch_check_recip(lo, count, d_mismatches, static_cast<hipStream_t>(stream)));
+}
+
 dq_status dq_get_info(dq_plan *p, dq_info *out, void *stream) {
     if (!p || !out) return DQ_ENULL;
     if (!p->ws) return DQ_EWORKSPACE;

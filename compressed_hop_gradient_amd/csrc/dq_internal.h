@@ -142,5 +142,6 @@ int32_t part_table_index(int32_t n, int32_t topology, int64_t m, int64_t c);
 hipError_t launch_part_table(const unsigned long long *class_counts, int32_t n, int32_t topology,
                              PartInfo *table, hipStream_t s);
 hipError_t launch_mx(const MxArgs &a, int fmt, int local, hipStream_t s);
+hipError_t launch_check_recip(uint32_t lo, uint32_t n, unsigned long long *count, hipStream_t s);
 
 }  // namespace dq

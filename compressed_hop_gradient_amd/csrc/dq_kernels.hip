@@ -116,6 +116,23 @@ __device__ __forceinline__ float scale_unit(float A) {
     return s;
 }
 
+// fl(1/x), correctly rounded.  For x in [2^-126, 2^126) one Newton step on the
+// hardware reciprocal, e = fma(-x, r, 1) and fma(e, r, r), gives exactly the
+// IEEE quotient (checked on the hardware for every fp32 in the range by
+// dq_check_reciprocal); outside it, and only in the lanes that need it, the
+// IEEE division.
+__device__ __forceinline__ float recip_rn(float x) {
+    float y;
+    if (__builtin_expect(x >= 1.1754943508222875e-38f && x < 8.507059173023462e37f, 1)) {
+        const float r = __builtin_amdgcn_rcpf(x);
+        const float e = __builtin_fmaf(-x, r, 1.0f);
+        y = __builtin_fmaf(e, r, r);
+    } else {
+        y = 1.0f / x;
+    }
+    return y;
+}
+
 // Smallest c in [0, 255] with fl(c * s) >= a (exists because fl(255 s) >= A >= a).
 // For a normal s the estimate ceil(a * rcp(s)) (rcp within 1 ulp) is within one
 // of the answer, so one checked step down or up settles it; subnormal s (scale
@@ -360,7 +377,7 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po,
     const float s = scale_unit(A);
     const int c = group_code(amax, s);
     const float sigma = (float)c * s;
-    const float inv = sigma == 0.0f ? 0.0f : 1.0f / sigma;
+    const float inv = sigma == 0.0f ? 0.0f : recip_rn(sigma);
     float c1 = 0.0f, c2 = 0.0f;
     if constexpr (Q == 2) {
         c1 = T.dec2[1];
@@ -1020,6 +1037,19 @@ __global__ __launch_bounds__(256) void k_reorder_scatter(ReorderArgs a) {
 // report; one thread per 8 coordinates, a DPP quad per 32-element block.
 // ---------------------------------------------------------------------------
 
+// Compares recip_rn with the IEEE quotient 1/x for the fp32 bit patterns
+// [lo, lo + n); counts the mismatches.
+__global__ __launch_bounds__(256) void k_check_recip(uint32_t lo, uint32_t n, unsigned long long *count) {
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    bool bad = false;
+    if (i < n) {
+        const float x = __uint_as_float(lo + i);
+        bad = __float_as_uint(recip_rn(x)) != __float_as_uint(1.0f / x);
+    }
+    const unsigned long long m = __ballot(bad);
+    if ((threadIdx.x & 63) == 0 && m) atomicAdd(count, (unsigned long long)__popcll(m));
+}
+
 __device__ __forceinline__ int floor_log2(float a) {   // a > 0
     const uint32_t b = __float_as_uint(a);
     const int e = (int)(b >> 23);
@@ -1236,6 +1266,18 @@ constexpr int64_t kStreamGrid = 2048;  // 256 CUs x 8 blocks
 hipError_t launch_zero(uint32_t *p, int64_t n, hipStream_t s) {
     hipLaunchKernelGGL(k_zero_u32, dim3(grid_for(n, 256, 1024)), dim3(256), 0, s, p, n);
     return hipGetLastError();
+}
+
+hipError_t launch_check_recip(uint32_t lo, uint32_t n, unsigned long long *count, hipStream_t s) {
+    constexpr uint32_t kChunk = 1u << 28;   // bit patterns per launch
+    for (uint32_t done = 0; done < n;) {
+        const uint32_t k = n - done < kChunk ? n - done : kChunk;
+        hipLaunchKernelGGL(k_check_recip, dim3((k + 255) / 256), dim3(256), 0, s, lo + done, k, count);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        done += k;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_stats(const StatsArgs &a, int f32, hipStream_t s) {

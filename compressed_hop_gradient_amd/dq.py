@@ -83,6 +83,7 @@ _SIGS = {
     "dq_plan_set_f64": (C.c_int, [C.c_void_p, C.c_int32, C.c_double]),
     "dq_mx_allreduce": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
                                   C.c_void_p, C.c_void_p]),
+    "dq_check_reciprocal": (C.c_int, [C.c_uint32, C.c_uint32, C.c_void_p, C.c_void_p]),
     "dq_get_info": (C.c_int, [C.c_void_p, C.POINTER(dq_info), C.c_void_p]),
     "dq_timing_read": (C.c_int, [C.c_void_p, C.POINTER(dq_timing)]),
     "dq_status_string": (C.c_char_p, [C.c_int32]),
@@ -133,6 +134,16 @@ def _kind(t):
     if t.dtype == torch.uint8:
         return PACKED
     raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def check_reciprocal(lo_bits, count, device=None, stream=None):
+    """Mismatches between the codec's reciprocal and the IEEE quotient 1/x over
+    the fp32 bit patterns [lo_bits, lo_bits + count) (runs on the GPU)."""
+    dev = torch.device("cuda") if device is None else torch.device(device)
+    cnt = torch.zeros(1, dtype=torch.int64, device=dev)
+    _check(lib().dq_check_reciprocal(int(lo_bits), int(count), _ptr(cnt), _stream(stream)),
+           "dq_check_reciprocal")
+    return int(cnt.item())
 
 
 class Plan:

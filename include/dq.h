@@ -311,6 +311,16 @@ dq_status dq_get_info(dq_plan *plan, dq_info *out, void *stream);
  * the timed launches ran on.  Errors: DQ_ENULL, DQ_EHIP. */
 dq_status dq_timing_read(dq_plan *plan, dq_timing *out);
 
+/* Self-check of a hardware fact the codec kernels rely on: the reciprocal
+ * they use for v = y * fl(1/sigma) (one Newton step on the hardware
+ * approximation for sigma in [2^-126, 2^126)) must equal the IEEE quotient.
+ * Compares the two for the fp32 bit patterns [lo_bits, lo_bits + count) and
+ * ADDS the number of mismatches to *d_mismatches (device memory, one
+ * unsigned 64-bit counter, cleared by the caller).  Asynchronous on `stream`.
+ * Errors: DQ_ENULL, DQ_EINVAL (range past 0xFFFFFFFF), DQ_EHIP. */
+dq_status dq_check_reciprocal(uint32_t lo_bits, uint32_t count, unsigned long long *d_mismatches,
+                              void *stream);
+
 const char *dq_status_string(int32_t status);
 int32_t dq_version(void);
 

@@ -158,3 +158,10 @@ def test_package_has_no_cpu_fallback():
     src = open(os.path.join(ROOT, "compressed_hop_gradient_amd", "dq.py")).read()
     assert "oracle" not in src
     assert "raise RuntimeError" in src
+
+
+def test_check_reciprocal_argument_checks(lib):
+    fake = C.c_void_p(0x1000)
+    assert lib.dq_check_reciprocal(0, 16, None, None) == dq.DQ_ENULL
+    assert lib.dq_check_reciprocal(0xFFFFFFFF, 2, fake, None) == dq.DQ_EINVAL
+    assert lib.dq_check_reciprocal(0xFFFFFFF0, 0, fake, None) == dq.DQ_OK   # nothing to do, no launch
