@@ -970,6 +970,26 @@ def test_mx_quantiser_brute_force(fmt):
         assert np.array_equal(po.mxfp8_roundtrip(x), po.mx_roundtrip(fmt, x))
 
 
+def test_mx_e4m3_elements_match_torch_float8():
+    """E4M3 element rounding equals torch's float8_e4m3fn cast (an independent
+    round-to-nearest-even implementation) wherever the two are defined alike:
+    blocks whose maximum lies in [256, 448] have the scale 2^0, and no element
+    reaches 464, where torch's cast gives NaN instead of saturating."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(77)
+    nb = 2000
+    x = (np.where(rng.random(32 * nb) < 0.5, -1.0, 1.0) *
+         10.0 ** rng.uniform(-4.5, np.log10(448.0), 32 * nb)).astype(np.float32)
+    x[::32] = rng.uniform(256.0, 448.0, nb).astype(np.float32)
+    # midpoints between neighbouring E4M3 values (ties) in some blocks
+    vals = _mx_values(po.MX_E4M3)
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    for b in range(200):
+        x[32 * b + 1:32 * b + 32] = mids[rng.integers(0, len(mids), 31)] * np.where(rng.random(31) < 0.5, -1, 1)
+    theirs = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float32).numpy()
+    assert np.array_equal(po.mx_roundtrip(po.MX_E4M3, x), theirs)
+
+
 def test_mx_schedule_composition_fp4():
     rng = np.random.default_rng(18)
     J = 12
