@@ -133,6 +133,10 @@ def _run(name, budget, capsys, budgets_stage_only=()):
     positions = _sample_positions(C, n, topo, np.random.default_rng(7))
     say(f"{positions.size} sampled super-groups through the schedule")
     L = max(0, n.bit_length() - 1)
+    last = n - 1 if topo == dq.RING else L
+    # the schedule's last hops run fused with the finalize of their part, as a
+    # whole round does (dq_hop_finalize): they write the region and the output
+    out_g = torch.full((d,), float("nan"), dtype=torch.float32, device=DEV)
     g_prev, o_prev = {}, {}
     checked = 0
     for kind, _, step in _steps(n, topo):
@@ -152,7 +156,10 @@ def _run(name, budget, capsys, budgets_stage_only=()):
                 orc.compress(w, step, gnp[w], oout[0], filt=positions)
             elif topo == dq.RING:
                 src = (w - 1) % n
-                plan.hop(w, step, g_prev[src][0], grads[w], gout[0])
+                if step == last:
+                    plan.hop_finalize(w, step, g_prev[src][0], grads[w], gout[0], out_g)
+                else:
+                    plan.hop(w, step, g_prev[src][0], grads[w], gout[0])
                 orc.hop(w, step, o_prev[src][0], gnp[w], oout[0], filt=positions)
             else:
                 partner, keep = w ^ (n >> step), (w >> (L - step)) & 1
@@ -162,7 +169,10 @@ def _run(name, budget, capsys, budgets_stage_only=()):
                 else:
                     gi, oi = g_prev[partner][keep], o_prev[partner][keep]
                     gl, ol = g_prev[w][keep], o_prev[w][keep]
-                plan.hop(w, step, gi, gl, gout[0], gout[1] if len(gout) > 1 else None)
+                if step == last:
+                    plan.hop_finalize(w, step, gi, gl, gout[0], out_g)
+                else:
+                    plan.hop(w, step, gi, gl, gout[0], gout[1] if len(gout) > 1 else None)
                 orc.hop(w, step, oi, ol, oout[0], oout[1] if len(oout) > 1 else None, filt=positions)
             torch.cuda.synchronize()
             for (m, c), gb, ob in zip(parts, gout, oout):
@@ -174,17 +184,20 @@ def _run(name, budget, capsys, budgets_stage_only=()):
             g_cur[w], o_cur[w] = gout, oout
         g_prev, o_prev = g_cur, o_cur
         say(f"{kind} step {step} ok")
-    out_g = torch.full((d,), float("nan"), dtype=torch.float32, device=DEV)
     out_o = np.zeros(d, np.float32)
     for w in range(n):
-        part = plan.final_part(w)
-        plan.finalize(part, g_prev[w][0], out_g)
-        orc.finalize(part, o_prev[w][0], out_o, filt=positions)
+        orc.finalize(plan.final_part(w), o_prev[w][0], out_o, filt=positions)
     torch.cuda.synchronize()
-    assert not torch.isnan(out_g).any(), "finalize left a coordinate unwritten"
+    assert not torch.isnan(out_g).any(), "the fused last hops left a coordinate unwritten"
     cols = (perm_o[positions].astype(np.int64)[:, None] * 256 + np.arange(256)[None, :]).ravel()
     got = out_g[torch.from_numpy(cols).to(DEV)].cpu().numpy()
-    assert np.array_equal(_bits(got), _bits(out_o[cols])), "finalize: output"
+    assert np.array_equal(_bits(got), _bits(out_o[cols])), "fused finalize: output"
+    # the stand-alone finalize of the same final regions gives the same bytes everywhere
+    out_f = torch.full((d,), float("nan"), dtype=torch.float32, device=DEV)
+    for w in range(n):
+        plan.finalize(plan.final_part(w), g_prev[w][0], out_f)
+    torch.cuda.synchronize()
+    assert torch.equal(out_f.view(torch.int32), out_g.view(torch.int32)), "finalize vs fused last hop"
     say(f"{checked} sampled region records and {positions.size} output super-groups bit-exact")
 
     for b in budgets_stage_only:
