@@ -154,9 +154,14 @@ typedef struct dq_timing {
 /* ---- plan ---------------------------------------------------------------- */
 
 /* Host-only; allocates no device memory.  n_coords > 0 and a multiple of 256;
- * n_workers >= 1 (a power of two for DQ_BUTTERFLY).  avg_bits is the payload
- * budget in bits per coordinate (>= 2; > 8 means every width is 8).
- * Errors: DQ_ENULL, DQ_EINVAL, DQ_EBUDGET. */
+ * n_workers in 1..65536 (a power of two for DQ_BUTTERFLY).  avg_bits is the
+ * payload budget in bits per coordinate (>= 2; > 8 means every width is 8).
+ * The kernels address a region with 32-bit offsets, so the largest region
+ * the schedule writes (a part of m = n for a ring, m = 2 for a butterfly,
+ * the whole vector for n = 1), sized at 276 bytes per super-group, must stay
+ * below 4 GB: at most about 1.5e7 super-groups (3.98e9 coordinates) per part.
+ * Errors: DQ_ENULL, DQ_EINVAL (sizes, counts, topology, the region limit),
+ * DQ_EBUDGET. */
 dq_status dq_plan_create(int64_t n_coords, int32_t n_workers, int32_t topology,
                          float avg_bits, dq_plan **out);
 void dq_plan_destroy(dq_plan *plan);

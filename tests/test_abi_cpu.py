@@ -165,3 +165,15 @@ def test_check_reciprocal_argument_checks(lib):
     assert lib.dq_check_reciprocal(0, 16, None, None) == dq.DQ_ENULL
     assert lib.dq_check_reciprocal(0xFFFFFFFF, 2, fake, None) == dq.DQ_EINVAL
     assert lib.dq_check_reciprocal(0xFFFFFFF0, 0, fake, None) == dq.DQ_OK   # nothing to do, no launch
+
+
+def test_region_limit(lib):
+    """The largest region a schedule writes must stay below 4 GB (32-bit
+    offsets in the kernels): 276 bytes per super-group at worst."""
+    J = 16_000_000                                    # 4.1e9 coordinates
+    assert _create(lib, d=256 * J, n=1)[0] == dq.DQ_EINVAL        # the whole vector in one region
+    for n, topo in ((2, dq.RING), (2, dq.BUTTERFLY), (8, dq.RING)):
+        rc, h = _create(lib, d=256 * J, n=n, topo=topo)            # halves and eighths fit
+        assert rc == dq.DQ_OK
+        lib.dq_plan_destroy(h)
+    assert _create(lib, d=256 * 2 * J, n=2, topo=dq.BUTTERFLY)[0] == dq.DQ_EINVAL
