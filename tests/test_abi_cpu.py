@@ -177,3 +177,20 @@ def test_region_limit(lib):
         assert rc == dq.DQ_OK
         lib.dq_plan_destroy(h)
     assert _create(lib, d=256 * 2 * J, n=2, topo=dq.BUTTERFLY)[0] == dq.DQ_EINVAL
+
+
+def test_header_compiles_as_c_and_host_calls_work(lib, tmp_path):
+    """include/dq.h is a C header (C11, pedantic, warnings as errors), and a
+    plain C program linked against the library gets the documented results
+    from the host-only calls (tests/native/abi_c_check.c)."""
+    import shutil
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = os.path.join(ROOT, "tests", "native", "abi_c_check.c")
+    libdir = os.path.dirname(dq.LIB_PATH)
+    exe = str(tmp_path / "abi_c_check")
+    subprocess.run([cc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+                    src, "-L", libdir, "-ldq", "-Wl,-rpath," + libdir, "-o", exe], check=True)
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0 and out.stdout.strip() == "ok", out.stdout
