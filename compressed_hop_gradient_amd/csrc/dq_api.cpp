@@ -54,6 +54,10 @@ struct dq_plan {
 
     std::vector<Launch> launches;
     std::vector<hipEvent_t> pool;
+    // DQ_OPT_STREAMS = 2: dq_allreduce's second stream and its fork/join events
+    int32_t streams = 1;
+    hipStream_t aux = nullptr;
+    hipEvent_t fork_ev = nullptr, join_ev = nullptr;
     dq_timing acc{};
     int64_t host_counts[3] = {0, 0, 0};
 };
@@ -302,6 +306,9 @@ void dq_plan_destroy(dq_plan *p) {
         if (L.e1) (void)hipEventDestroy(L.e1);
     }
     for (auto e : p->pool) (void)hipEventDestroy(e);
+    if (p->fork_ev) (void)hipEventDestroy(p->fork_ev);
+    if (p->join_ev) (void)hipEventDestroy(p->join_ev);
+    if (p->aux) (void)hipStreamDestroy(p->aux);
     delete p;
 }
 
@@ -333,6 +340,17 @@ dq_status dq_plan_set_u64(dq_plan *p, int32_t option, uint64_t v) {
             if (v != DQ_ALLOC_THRESHOLD && v != DQ_ALLOC_MEAN_CORRECTED && v != DQ_ALLOC_UNIFORM)
                 return DQ_EINVAL;
             p->alloc = (int32_t)v;
+            return DQ_OK;
+        case DQ_OPT_STREAMS:
+            if (v != 1 && v != 2) return DQ_EINVAL;
+            if (v == 2 && !p->aux) {
+                // default priority, non-blocking with respect to the null stream
+                if (hipStreamCreateWithFlags(&p->aux, hipStreamNonBlocking) != hipSuccess) return DQ_EHIP;
+                if (hipEventCreateWithFlags(&p->fork_ev, hipEventDisableTiming) != hipSuccess ||
+                    hipEventCreateWithFlags(&p->join_ev, hipEventDisableTiming) != hipSuccess)
+                    return DQ_EHIP;
+            }
+            p->streams = (int32_t)v;
             return DQ_OK;
         default: return DQ_EINVAL;
     }
@@ -616,37 +634,63 @@ dq_status dq_allreduce(dq_plan *p, const void *const *grads, int32_t kind, void 
         if ((st = dq_compress(p, 0, 0, grads[0], kind, A + ap.off[0], stream)) != DQ_OK) return st;
         return dq_finalize(p, 0, A + ap.off[0], out, stream);
     }
+    // Within one schedule step the workers' launches are independent.  With two
+    // streams the odd workers' launches go to the plan's second stream, forked
+    // from and joined back into the caller's stream around every step, so one
+    // launch's tail overlaps the next launch's start.
+    hipStream_t main_s = static_cast<hipStream_t>(stream);
+    const bool two = p->streams == 2;
+    auto fork = [&]() -> dq_status {
+        if (!two) return DQ_OK;
+        if (hipEventRecord(p->fork_ev, main_s) != hipSuccess) return DQ_EHIP;
+        return hipStreamWaitEvent(p->aux, p->fork_ev, 0) == hipSuccess ? DQ_OK : DQ_EHIP;
+    };
+    auto join = [&]() -> dq_status {
+        if (!two) return DQ_OK;
+        if (hipEventRecord(p->join_ev, p->aux) != hipSuccess) return DQ_EHIP;
+        return hipStreamWaitEvent(main_s, p->join_ev, 0) == hipSuccess ? DQ_OK : DQ_EHIP;
+    };
+    auto sw = [&](int w) -> void * { return two && (w & 1) ? static_cast<void *>(p->aux) : stream; };
     if (p->topo == DQ_RING) {
         auto slot = [&](int w, int t) { return A + ap.off[(size_t)(t & 1) * n + w]; };
+        if ((st = fork()) != DQ_OK) return st;
         for (int w = 0; w < n; w++)
-            if ((st = dq_compress(p, w, 0, grads[w], kind, slot(w, 0), stream)) != DQ_OK) return st;
+            if ((st = dq_compress(p, w, 0, grads[w], kind, slot(w, 0), sw(w))) != DQ_OK) return st;
+        if ((st = join()) != DQ_OK) return st;
         // the last step's hops also write the decoded sum (no separate finalize)
-        for (int t = 1; t < n; t++)
+        for (int t = 1; t < n; t++) {
+            if ((st = fork()) != DQ_OK) return st;
             for (int w = 0; w < n; w++) {
                 const void *in = slot((w - 1 + n) % n, t - 1);
-                st = t < n - 1 ? dq_hop(p, w, t, in, grads[w], kind, slot(w, t), nullptr, stream)
-                               : dq_hop_finalize(p, w, t, in, grads[w], kind, slot(w, t), out, stream);
+                st = t < n - 1 ? dq_hop(p, w, t, in, grads[w], kind, slot(w, t), nullptr, sw(w))
+                               : dq_hop_finalize(p, w, t, in, grads[w], kind, slot(w, t), out, sw(w));
                 if (st != DQ_OK) return st;
             }
+            if ((st = join()) != DQ_OK) return st;
+        }
         return DQ_OK;
     }
     const int L = p->L;
     const size_t per_w = 1 + (size_t)(2 * (L - 1) + 1);
     auto cmp = [&](int w) { return A + ap.off[w * per_w]; };
     auto lvl = [&](int w, int s, int h) { return A + ap.off[w * per_w + 1 + 2 * (s - 1) + h]; };
+    if ((st = fork()) != DQ_OK) return st;
     for (int w = 0; w < n; w++)
-        if ((st = dq_compress(p, w, 1, grads[w], kind, cmp(w), stream)) != DQ_OK) return st;
+        if ((st = dq_compress(p, w, 1, grads[w], kind, cmp(w), sw(w))) != DQ_OK) return st;
+    if ((st = join()) != DQ_OK) return st;
     for (int s = 1; s <= L; s++) {
+        if ((st = fork()) != DQ_OK) return st;
         for (int w = 0; w < n; w++) {
             const int partner = w ^ (n >> s);
             const int keep = (w >> (L - s)) & 1;
             const void *in = s == 1 ? (const void *)cmp(partner) : (const void *)lvl(partner, s - 1, keep);
             const void *local = s == 1 ? grads[w] : (const void *)lvl(w, s - 1, keep);
             const int32_t lk = s == 1 ? kind : (p->own == DQ_OWN_F32 ? DQ_F32_PARTIAL : DQ_PACKED);
-            st = s < L ? dq_hop(p, w, s, in, local, lk, lvl(w, s, 0), lvl(w, s, 1), stream)
-                       : dq_hop_finalize(p, w, s, in, local, lk, lvl(w, s, 0), out, stream);
+            st = s < L ? dq_hop(p, w, s, in, local, lk, lvl(w, s, 0), lvl(w, s, 1), sw(w))
+                       : dq_hop_finalize(p, w, s, in, local, lk, lvl(w, s, 0), out, sw(w));
             if (st != DQ_OK) return st;
         }
+        if ((st = join()) != DQ_OK) return st;
     }
     return DQ_OK;
 }

@@ -20,6 +20,7 @@ BF16, F32, PACKED, F32_PARTIAL = 0, 1, 2, 3
 OWN_PACKED, OWN_F32 = 0, 1
 CORRELATED, INDEPENDENT = 0, 1
 OPT_SEED, OPT_ROUND, OPT_ROUNDING, OPT_TIMING, OPT_ALLOC, OPT_TIMING_KINDS, OPT_OWN = 0, 1, 2, 3, 4, 5, 6
+OPT_STREAMS = 7
 ALLOC_THRESHOLD, ALLOC_MEAN_CORRECTED, ALLOC_UNIFORM = 0, 1, 2
 MX_FP8_E4M3, MX_FP6_E3M2, MX_FP6_E2M3, MX_FP4_E2M1 = 0, 1, 2, 3
 OPT_EPS = 0   # dq_option_f64
@@ -155,7 +156,7 @@ class Plan:
 
     def __init__(self, n_coords, n_workers, topology=RING, avg_bits=5.0, seed=1, rnd=0,
                  rounding=CORRELATED, device="cuda", timing=False, alloc=ALLOC_THRESHOLD, eps=None,
-                 own=OWN_PACKED):
+                 own=OWN_PACKED, streams=1):
         self.d = int(n_coords)
         self.n = int(n_workers)
         self.J = self.d // 256
@@ -173,6 +174,9 @@ class Plan:
         self.set(OPT_OWN, own)
         if eps is not None:
             _check(lib().dq_plan_set_f64(self.h, OPT_EPS, float(eps)), "dq_plan_set_f64")
+        if streams != 1:
+            with torch.cuda.device(torch.device(device)):   # the second stream lives on this device
+                self.set(OPT_STREAMS, streams)
         nbytes = lib().dq_workspace_bytes(self.h)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _check(lib().dq_plan_bind(self.h, _ptr(self.workspace), nbytes), "dq_plan_bind")

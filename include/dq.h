@@ -107,7 +107,9 @@ typedef enum dq_option {
                               next dq_allocate */
     DQ_OPT_TIMING_KINDS = 5, /* bit mask of dq_kernel_kind: which launches DQ_OPT_TIMING
                                 times (default all); fewer events, less overhead */
-    DQ_OPT_OWN = 6           /* dq_own (default DQ_OWN_PACKED); set between rounds */
+    DQ_OPT_OWN = 6,          /* dq_own (default DQ_OWN_PACKED); set between rounds */
+    DQ_OPT_STREAMS = 7       /* 1 (default) or 2: dq_allreduce runs the independent launches
+                                of each schedule step on two streams (see dq_allreduce) */
 } dq_option;
 
 typedef struct dq_plan dq_plan;
@@ -168,6 +170,10 @@ void dq_plan_destroy(dq_plan *plan);
 
 /* Set a dq_option.  Errors: DQ_ENULL, DQ_EINVAL (unknown option or value). */
 dq_status dq_plan_set_u64(dq_plan *plan, int32_t option, uint64_t value);
+/* DQ_OPT_STREAMS = 2 creates the plan's second stream and two events on the
+ * current device (host resources, released by dq_plan_destroy); set it with
+ * the device the plan runs on current and outside stream capture.  Errors
+ * for it: DQ_EINVAL (not 1 or 2), DQ_EHIP. */
 
 /* Real-valued options. */
 typedef enum dq_option_f64 {
@@ -270,9 +276,14 @@ size_t dq_arena_bytes(const dq_plan *plan);
 
 /* One full simulated round: dq_stats for every worker, dq_allocate,
  * dq_reorder, the schedule's compress and hop calls with region hand-offs,
- * and dq_finalize of every part into d_out (float[n_coords]).
- * h_grads is a HOST array of n device pointers of the same kind.
- * Errors: as the stages, DQ_EWORKSPACE if the arena is too small. */
+ * the last hops fused with the finalize of their part (dq_hop_finalize; n = 1:
+ * compress then dq_finalize) into d_out (float[n_coords]).
+ * h_grads is a HOST array of n device pointers of the same kind.  All work is
+ * ordered on `stream`; with DQ_OPT_STREAMS = 2 the odd workers' launches of
+ * each step run on the plan's second stream, forked from `stream` before the
+ * step and joined back after it (capturable in a HIP graph; the round then
+ * holds the second stream's launches too).  Each plan owns its second stream.
+ * Errors: as the stages, DQ_EWORKSPACE if the arena is too small, DQ_EHIP. */
 dq_status dq_allreduce(dq_plan *plan, const void *const *h_grads, int32_t kind,
                        void *d_arena, size_t arena_bytes, float *d_out, void *stream);
 

@@ -194,3 +194,12 @@ def test_header_compiles_as_c_and_host_calls_work(lib, tmp_path):
                     src, "-L", libdir, "-ldq", "-Wl,-rpath," + libdir, "-o", exe], check=True)
     out = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert out.returncode == 0 and out.stdout.strip() == "ok", out.stdout
+
+
+def test_streams_option(lib):
+    rc, h = _create(lib)
+    assert rc == dq.DQ_OK
+    assert lib.dq_plan_set_u64(h, dq.OPT_STREAMS, 1) == dq.DQ_OK
+    assert lib.dq_plan_set_u64(h, dq.OPT_STREAMS, 0) == dq.DQ_EINVAL
+    assert lib.dq_plan_set_u64(h, dq.OPT_STREAMS, 3) == dq.DQ_EINVAL
+    lib.dq_plan_destroy(h)

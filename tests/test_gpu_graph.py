@@ -11,14 +11,15 @@ from compressed_hop_gradient_amd import dq, synth
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("topo,name", [(dq.RING, "bert"), (dq.BUTTERFLY, "gemma")])
-def test_round_in_graph_replays(topo, name):
+@pytest.mark.parametrize("topo,name,streams", [(dq.RING, "bert", 1), (dq.BUTTERFLY, "gemma", 1),
+                                               (dq.RING, "bert", 2), (dq.BUTTERFLY, "gemma", 2)])
+def test_round_in_graph_replays(topo, name, streams):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     J, n = 1031, 8
     grads = synth.generate(name, d=256 * J, device="cuda", workers=range(n))
     bufs = [g.clone() for g in grads]                    # the inputs the graph reads
-    plan = dq.Plan(256 * J, n, topo, 5.0)
+    plan = dq.Plan(256 * J, n, topo, 5.0, streams=streams)   # two streams: fork/join inside the graph
     arena = torch.empty(plan.arena_bytes(), dtype=torch.uint8, device="cuda")
     out = torch.empty(256 * J, dtype=torch.float32, device="cuda")
     ref = dq.Plan(256 * J, n, topo, 5.0)

@@ -210,6 +210,29 @@ def test_tiny_workload_bit_exact():
     assert np.array_equal(_bits(out2.cpu().numpy()), _bits(out))
 
 
+@pytest.mark.parametrize("name,n,topo,own", [("bert", 8, dq.RING, dq.OWN_PACKED),
+                                             ("llama", 3, dq.RING, dq.OWN_PACKED),
+                                             ("gemma", 8, dq.BUTTERFLY, dq.OWN_PACKED),
+                                             ("gemma", 16, dq.BUTTERFLY, dq.OWN_F32)])
+def test_two_stream_round_bit_exact(name, n, topo, own):
+    """DQ_OPT_STREAMS = 2 (odd workers' launches on a second stream, fork/join
+    around every step) gives the oracle's bytes, on the caller's stream's
+    timeline: the output is read after synchronising only that stream."""
+    _need_gpu()
+    J = 1537
+    grads = _scaled(name, J, workers=range(n))
+    p = dq.Plan(256 * J, n, topo, 5.0, own=own, streams=2)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out = p.allreduce(grads, stream=s)
+    s.synchronize()
+    o = po.Oracle(256 * J, n, po.BUTTERFLY if topo == dq.BUTTERFLY else po.RING, 5.0,
+                  own=po.OWN_F32 if own == dq.OWN_F32 else po.OWN_PACKED)
+    ref = o.allreduce(_grads_np(grads))
+    assert np.array_equal(_bits(out.cpu().numpy()), _bits(ref))
+
+
 @pytest.mark.parametrize("name,J,topo", [
     ("bert", 3001, dq.RING),          # 8 workers, ragged parts
     ("gemma", 4099, dq.BUTTERFLY),    # 8 workers, 3 levels, two-child outputs
