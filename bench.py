@@ -107,6 +107,22 @@ def cpu_baseline(args, wl_name, budget, device):
     dt = time.perf_counter() - t0
     dar = dar_coords_per_round(wl.n, wl.topology, 256 * J)
     cores = po.get_threads()
+    # the front-end stages alone, on a second oracle over the same sample; the
+    # encoding stages (compress, hops, finalize) take the rest of the round
+    of = po.Oracle(256 * J, wl.n, topo, budget, seed=wl.rounding_seed)
+    ts = time.perf_counter()
+    for w in range(wl.n):
+        of.stats(w, grads[w])
+    ta = time.perf_counter()
+    of.allocate()
+    tr = time.perf_counter()
+    of.reorder()
+    te = time.perf_counter()
+    stages = {"stats": {"seconds": ta - ts, "coords_per_s": wl.n * 256 * J / (ta - ts)},
+              "allocate": {"seconds": tr - ta},
+              "reorder": {"seconds": te - tr},
+              "compress_hops_finalize": {"seconds": max(dt - (te - ts), 0.0),
+                                         "dar_coords_per_s": dar / max(dt - (te - ts), 1e-9)}}
     # the same oracle on one host thread, on a 16x smaller sample
     J1 = max(1, J // 16)
     o1 = po.Oracle(256 * J1, wl.n, topo, budget, seed=wl.rounding_seed)
@@ -121,7 +137,7 @@ def cpu_baseline(args, wl_name, budget, device):
     return {"value": dar / dt, "unit": "coords/s", "cores": cores, "kind": "oracle",
             "sample": f"whole round of the {wl_name} workload scaled to {J} super-groups "
                       f"({256 * J} coords x {wl.n} workers), same recipe and schedule; "
-                      f"{dt:.2f} s", "seconds": dt, "single_thread": one}
+                      f"{dt:.2f} s", "seconds": dt, "stages": stages, "single_thread": one}
 
 
 def dar_coords_per_round(n, topology, d):
