@@ -26,6 +26,12 @@
  * Threading: OpenMP over super-groups; every per-super-group computation is
  * independent and every reduction is sequential or integer, so results do not
  * depend on the thread count.
+ *
+ * Pins: tests/test_oracle_pins.py checks every function here against
+ * something other than itself: exact rationals and hand-derived fixtures
+ * (tests/golden/), closed forms, brute force on small inputs, Monte Carlo
+ * unbiasedness, and independent implementations (rocRAND's Philox4x32-10,
+ * torch's float8_e4m3fn rounding).  No function is left unpinned.
  */
 #ifndef DQ_ORACLE_H
 #define DQ_ORACLE_H
