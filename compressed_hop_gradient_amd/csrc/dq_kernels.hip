@@ -299,18 +299,31 @@ __device__ __forceinline__ void decode_group(const RegionBase &R, uint32_t t, ui
 // Q = bits per code of the super-group's class, K = the class index.
 // Po = output part, Pi = input part (the same part or its parent); In / Own /
 // Out are their regions.  t is the part-local index in the output part.
+// Whether a kernel fetches its rows' next super-group's j and mean one
+// iteration ahead, so that the gather of the local gradient at j waits for an
+// LDS read instead of a global load.  The value is parked in LDS rather than
+// carried in a register: vector-memory completions count in issue order, and
+// a loop-carried load would make every iteration wait for the previous one's
+// stores.  Measured: compress 6% faster; the hop kernels no faster (their
+// incoming-region loads cover the latency) and some of them would spill.
+template <int MODE, int LOCAL>
+constexpr bool codec_ahead() { return LOCAL == kLocalBF16 && MODE == kCompress; }
+
 template <int Q, int MODE, int LOCAL>
 __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po, const PartInfo &Pi,
                                          const RegionBase &In, const RegionBase &Own,
-                                         const RegionBase &Out, uint32_t t, int g,
+                                         const RegionBase &Out, uint32_t t, uint32_t j, float mu,
+                                         uint32_t pos_next, uint32_t *slot_j, float *slot_mu, int g,
                                          const SharedTables &T, float *stage_row) {
     constexpr int K = Q == 2 ? 0 : (Q == 4 ? 1 : 2);
     const uint32_t idx = t - (uint32_t)Po.pre[K];        // index in the class, output part
     const uint32_t pos = (uint32_t)Po.lo[K] + idx;       // stream position
-    const uint32_t j = (uint32_t)a.perm[pos];            // original super-group
     const uint32_t idx_in = pos - (uint32_t)Pi.lo[K];    // index in the class, input part
     const uint32_t t_in = (uint32_t)Pi.pre[K] + idx_in;
-    const float mu = a.mu_stream[pos];
+    if constexpr (!codec_ahead<MODE, LOCAL>()) {
+        j = (uint32_t)a.perm[pos];                       // original super-group
+        mu = a.mu_stream[pos];
+    }
     float y[16];
 
     if constexpr (MODE != kCompress) decode_group<Q, K>(In, t_in, idx_in, g, T, y);
@@ -361,11 +374,28 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po,
         }
     }
 
+    // the next iteration's original index and mean, issued after this
+    // super-group's loads and parked in LDS at the end
+    uint32_t j_next = 0u;
+    float mu_next = 0.0f;
+    const bool ahead = codec_ahead<MODE, LOCAL>() && pos_next != 0xFFFFFFFFu;
+    if (ahead) {
+        j_next = (uint32_t)a.perm[pos_next];
+        mu_next = a.mu_stream[pos_next];
+    }
+    auto park = [&]() {
+        if (ahead && g == 0) {
+            *slot_j = j_next;
+            *slot_mu = mu_next;
+        }
+    };
+
     if constexpr (MODE == kPartial) {
         // the kept child of the own-fp32 variant: store y, no quantisation
         float4 *dst = reinterpret_cast<float4 *>(a.partial_out + ((uint64_t)t * kSG + (uint32_t)g * kGroup));
 #pragma unroll
         for (int v = 0; v < 4; v++) dst[v] = make_float4(y[4 * v], y[4 * v + 1], y[4 * v + 2], y[4 * v + 3]);
+        park();
         return;
     } else {
 
@@ -458,6 +488,7 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po,
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
     }
+    park();
     }   // MODE != kPartial
 }
 
@@ -495,12 +526,46 @@ __global__ __launch_bounds__(kCodecThreads) __attribute__((amdgpu_waves_per_eu(6
     constexpr int kStageRows = MODE == kHopFinal ? kCodecThreads / 16 : 1;
     __shared__ __align__(16) float stage[kStageRows][kSG];
     float *stage_row = stage[MODE == kHopFinal ? threadIdx.x / 16 : 0];
-    for (uint32_t base = blockIdx.x * kCodecSGPerBlock; base < N; base += gridDim.x * kCodecSGPerBlock) {
+    // per row: the original index and mean of the row's next super-group,
+    // fetched during the current one (see codec_sg)
+    __shared__ uint32_t next_j[kCodecThreads / 16];
+    __shared__ float next_mu[kCodecThreads / 16];
+    uint32_t *slot_j = &next_j[threadIdx.x / 16];
+    float *slot_mu = &next_mu[threadIdx.x / 16];
+    // (selects, not an index into Po's arrays: a runtime index would put the
+    // part layout in scratch memory)
+    const uint32_t lo0 = (uint32_t)Po.lo[0], lo1 = (uint32_t)Po.lo[1], lo2 = (uint32_t)Po.lo[2];
+    auto pos_of = [&](uint32_t tt) -> uint32_t {
+        return tt < pre1 ? lo0 + tt : (tt < pre2 ? lo1 + (tt - pre1) : lo2 + (tt - pre2));
+    };
+    const uint32_t stride = gridDim.x * kCodecSGPerBlock;
+    constexpr bool kAhead = codec_ahead<MODE, LOCAL>();
+    if (kAhead) {
+        const uint32_t t0 = blockIdx.x * kCodecSGPerBlock + wave * 4 + row;
+        if (t0 < N && g == 0) {
+            const uint32_t p0 = pos_of(t0);
+            *slot_j = (uint32_t)a.perm[p0];
+            *slot_mu = a.mu_stream[p0];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    }
+    for (uint32_t base = blockIdx.x * kCodecSGPerBlock; base < N; base += stride) {
         const uint32_t t = base + wave * 4 + row;
         if (t >= N) continue;
-        if (t < pre1) codec_sg<2, MODE, LOCAL>(a, Po, Pi, In, Own, Out, t, g, T, stage_row);
-        else if (t < pre2) codec_sg<4, MODE, LOCAL>(a, Po, Pi, In, Own, Out, t, g, T, stage_row);
-        else codec_sg<8, MODE, LOCAL>(a, Po, Pi, In, Own, Out, t, g, T, stage_row);
+        uint32_t j = 0u;
+        float mu = 0.0f;
+        uint32_t pn = 0xFFFFFFFFu;
+        if (kAhead) {
+            // written by this row at the end of its previous super-group (or
+            // before the loop): same wave, same address, program order
+            j = *slot_j;
+            mu = *slot_mu;
+            if (t + stride < N) pn = pos_of(t + stride);
+        }
+        if (t < pre1) codec_sg<2, MODE, LOCAL>(a, Po, Pi, In, Own, Out, t, j, mu, pn, slot_j, slot_mu, g, T, stage_row);
+        else if (t < pre2) codec_sg<4, MODE, LOCAL>(a, Po, Pi, In, Own, Out, t, j, mu, pn, slot_j, slot_mu, g, T, stage_row);
+        else codec_sg<8, MODE, LOCAL>(a, Po, Pi, In, Own, Out, t, j, mu, pn, slot_j, slot_mu, g, T, stage_row);
     }
 }
 
