@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-sgs", type=int, default=1 << 20)
     ap.add_argument("--no-quality", action="store_true")
+    ap.add_argument("--two-stream", action="store_true",
+                    help="also time the rounds with DQ_OPT_STREAMS=2 (after the timed region)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed region, copy this many MiB once with a plain copy kernel "
                          "(reference for HBM byte counters)")
@@ -217,19 +219,22 @@ def main():
     torch.cuda.synchronize()
     graph_ms = 1e3 * (time.perf_counter() - tg) / args.steps
     del graph
-    # the same rounds with the odd workers' launches on a second stream
-    # (DQ_OPT_STREAMS = 2): overlaps each launch's tail with the next launch;
-    # reported beside the single-stream figures, whose per-launch durations
-    # the roofline needs undisturbed
-    plan.set(dq.OPT_STREAMS, 2)
-    plan.allreduce(grads, out=out, arena=arena, stream=stream)
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for _ in range(args.steps):
+    # --two-stream: the same rounds with the odd workers' launches on a second
+    # stream (DQ_OPT_STREAMS = 2), overlapping each launch's tail with the
+    # next launch.  Off by default: overlapping launches stretch each other's
+    # durations, and a profile of the default command must show the
+    # single-stream launches the roofline is taken from.
+    two_stream_ms = None
+    if args.two_stream:
+        plan.set(dq.OPT_STREAMS, 2)
         plan.allreduce(grads, out=out, arena=arena, stream=stream)
-    torch.cuda.synchronize()
-    two_stream_ms = 1e3 * (time.perf_counter() - t2) / args.steps
-    plan.set(dq.OPT_STREAMS, 1)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for _ in range(args.steps):
+            plan.allreduce(grads, out=out, arena=arena, stream=stream)
+        torch.cuda.synchronize()
+        two_stream_ms = 1e3 * (time.perf_counter() - t2) / args.steps
+        plan.set(dq.OPT_STREAMS, 1)
     plan.set(dq.OPT_TIMING, 1)
     secs = t1 - t0
     ms_per_step = 1e3 * secs / args.steps
@@ -380,9 +385,9 @@ def main():
         "dar_kernel_coords_per_s": (hg["coords"] / (hg["ms"] * 1e-3)) if hg["ms"] > 0 else None,
         "kernels": kernels,
         "graph_replay_ms_per_step": graph_ms,
-        "two_stream": {"ms_per_step": two_stream_ms,
-                       "value": dar_coords / args.steps / (two_stream_ms * 1e-3),
-                       "note": "DQ_OPT_STREAMS=2, measured after the timed region"},
+        "two_stream": None if two_stream_ms is None else {
+            "ms_per_step": two_stream_ms, "value": dar_coords / args.steps / (two_stream_ms * 1e-3),
+            "note": "DQ_OPT_STREAMS=2, measured after the timed region"},
         "quality": quality,
         "copy_calibration": copy_cal,
     }
