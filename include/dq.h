@@ -20,6 +20,17 @@
  *                notes, "Key idea and contribution": the fused kernel)
  *   dq_finalize  decode, add back the mean, restore the original order
  *                (scribe notes, main all-reduce phase)
+ *   dq_hop_finalize  the schedule's last hop and the finalize of its part in
+ *                one pass
+ *
+ * A ring round, step by step (dq_allreduce does all of it in one call):
+ *   dq_plan_create, dq_plan_bind(workspace of dq_workspace_bytes);
+ *   dq_stats(w) for w = 0..n-1 (rank order); dq_allocate; dq_reorder;
+ *   dq_compress(w, 0) into region R[0][w];
+ *   for t = 1..n-2: dq_hop(w, t, R[t-1][w-1], grad[w]) into R[t][w];
+ *   dq_hop_finalize(w, n-1, R[n-2][w-1], grad[w]) into R[n-1][w] and out.
+ * The region R[t][w] is the message worker w sends at step t; a butterfly
+ * round differs in the parts and partners of each level (dq_hop).
  *
  * Numerics and layouts the pages leave open are fixed by one stated reading
  * each (fp32 with round-to-nearest-even and no contraction, the level set,
@@ -31,7 +42,8 @@
  *     throws across the ABI.  Argument checks are synchronous; a device fault
  *     surfaces at the caller's next synchronisation of the stream.
  *   - The caller owns every device buffer: gradients, regions, outputs and the
- *     plan workspace.  The plan owns only host state and borrows the bound
+ *     plan workspace.  The plan owns only host state (and, with
+ *     DQ_OPT_STREAMS = 2, one stream and two events) and borrows the bound
  *     workspace.  No stage allocates device memory.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *     device work of a call is enqueued on it; no call synchronises except
