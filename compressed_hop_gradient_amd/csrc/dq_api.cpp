@@ -343,12 +343,21 @@ dq_status dq_plan_set_u64(dq_plan *p, int32_t option, uint64_t v) {
             return DQ_OK;
         case DQ_OPT_STREAMS:
             if (v != 1 && v != 2) return DQ_EINVAL;
-            if (v == 2 && !p->aux) {
-                // default priority, non-blocking with respect to the null stream
-                if (hipStreamCreateWithFlags(&p->aux, hipStreamNonBlocking) != hipSuccess) return DQ_EHIP;
-                if (hipEventCreateWithFlags(&p->fork_ev, hipEventDisableTiming) != hipSuccess ||
-                    hipEventCreateWithFlags(&p->join_ev, hipEventDisableTiming) != hipSuccess)
+            if (v == 2) {
+                // each resource once, so that a retry after a failure completes the set;
+                // the stream has the default priority and does not sync with the null stream
+                if (!p->aux && hipStreamCreateWithFlags(&p->aux, hipStreamNonBlocking) != hipSuccess) {
+                    p->aux = nullptr;
                     return DQ_EHIP;
+                }
+                if (!p->fork_ev && hipEventCreateWithFlags(&p->fork_ev, hipEventDisableTiming) != hipSuccess) {
+                    p->fork_ev = nullptr;
+                    return DQ_EHIP;
+                }
+                if (!p->join_ev && hipEventCreateWithFlags(&p->join_ev, hipEventDisableTiming) != hipSuccess) {
+                    p->join_ev = nullptr;
+                    return DQ_EHIP;
+                }
             }
             p->streams = (int32_t)v;
             return DQ_OK;
