@@ -36,6 +36,7 @@ __device__ __forceinline__ float4 stream_load_f4(const void *p) {
 }
 
 static int grid_for(int64_t items, int64_t per_block, int64_t cap);
+static int64_t device_cus();
 
 
 // ---------------------------------------------------------------------------
@@ -741,67 +742,62 @@ __device__ __forceinline__ void partial_sums(const Partial<F32> &p, float &s, fl
     }
 }
 
-// A wave takes 4 rows x kStatsIter super-groups per iteration.  The per-SG
-// results go through LDS to lanes 0..31, which fetch the earlier workers'
-// running sums and store the new ones with one coalesced access per array:
-// the sparse 4-byte accesses of one lane per row cost more than their bytes
-// (writes mixed into a read stream make the memory turn around).
-constexpr int kStatsIter = 8;
-constexpr int kStatsPerWave = 4 * kStatsIter;        // 32 super-groups
-constexpr int kStatsPerBlock = 4 * kStatsPerWave;    // 256-thread blocks
+// One resident 1024-thread block per CU owns a contiguous range of at most
+// kStatsChunk super-groups.  A wave takes 4 rows x iterations super-groups per
+// step (all their loads in flight before any arithmetic); each row's leader
+// parks its sums in LDS.  Only when the whole range has been read does the
+// block read the earlier workers' running sums, add, and store the new ones,
+// in one coalesced burst: writes interleaved with the read stream make the
+// memory turn around and cost far more than their bytes.
+constexpr int kStatsThreads = 1024;
+constexpr int kStatsChunk = 15360;                   // 120 KB of LDS per block
+template <int F32>
+constexpr int stats_iters() { return F32 ? 4 : 8; }  // fp32 partials take twice the registers
 
 template <int F32>
-__global__ __launch_bounds__(256) void k_stats(StatsArgs a) {
+__global__ __launch_bounds__(kStatsThreads) void k_stats(StatsArgs a, int64_t chunk) {
+    constexpr int kIter = stats_iters<F32>();
+    constexpr int kPerWave = 4 * kIter, kPerBlock = (kStatsThreads / 64) * kPerWave;
     const int row = (threadIdx.x >> 4) & 3, wave = threadIdx.x >> 6, l = threadIdx.x & 15;
-    const int lane = threadIdx.x & 63;
-    __shared__ float staged[4][2][kStatsPerWave];
-    for (int64_t base = (int64_t)blockIdx.x * kStatsPerBlock; base < a.J;
-         base += (int64_t)gridDim.x * kStatsPerBlock) {
-        const int64_t wbase = base + wave * kStatsPerWave;
-        Partial<F32> p0[kStatsIter], p1[kStatsIter];
+    __shared__ float park[2][kStatsChunk];
+    for (int64_t c0 = (int64_t)blockIdx.x * chunk; c0 < a.J; c0 += (int64_t)gridDim.x * chunk) {
+        const int64_t c1 = c0 + chunk < a.J ? c0 + chunk : a.J;
+        for (int64_t base = c0; base < c1; base += kPerBlock) {
+            const int64_t wbase = base + wave * kPerWave;
+            Partial<F32> p0[kIter], p1[kIter];
 #pragma unroll
-        for (int u = 0; u < kStatsIter; u++) {
-            const int64_t j = wbase + u * 4 + row;
-            if (j < a.J) {
-                p0[u].load(a.grad, j, l);
-                p1[u].load(a.grad, j, l + 16);
-            } else {
-                p0[u].clear();
-                p1[u].clear();
+            for (int u = 0; u < kIter; u++) {
+                const int64_t j = wbase + u * 4 + row;
+                if (j < c1) {
+                    p0[u].load(a.grad, j, l);
+                    p1[u].load(a.grad, j, l + 16);
+                } else {
+                    p0[u].clear();
+                    p1[u].clear();
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kIter; u++) {
+                float sa, qa, sb, qb;
+                partial_sums(p0[u], sa, qa);
+                partial_sums(p1[u], sb, qb);
+                const float s = tree16(sa + sb), q = tree16(qa + qb);
+                const int64_t j = wbase + u * 4 + row;
+                if (l == 0 && j < c1) {
+                    park[0][j - c0] = s;
+                    park[1][j - c0] = q;
+                }
             }
         }
-        // lanes 0..31: the super-group wbase + lane, in the staged order
-        const int64_t jm = wbase + lane;
-        const bool mine = lane < kStatsPerWave && jm < a.J;
-        float prior_s = 0.0f, prior_q = 0.0f;
-        if (mine && !a.first) {
-            prior_s = a.sum[jm];
-            prior_q = a.sumsq[jm];
-        }
-#pragma unroll
-        for (int u = 0; u < kStatsIter; u++) {
-            float sa, qa, sb, qb;
-            partial_sums(p0[u], sa, qa);
-            partial_sums(p1[u], sb, qb);
-            const float s = tree16(sa + sb), q = tree16(qa + qb);
-            if (l == 0) {
-                staged[wave][0][u * 4 + row] = s;
-                staged[wave][1][u * 4 + row] = q;
-            }
-        }
-        // the staging area belongs to this wave: a wavefront-scope fence orders
-        // the row leaders' writes before the reads of the other lanes
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        if (mine) {
-            const float s = staged[wave][0][lane], q = staged[wave][1][lane];
-            const float S = a.first ? s : prior_s + s, F = a.first ? q : prior_q + q;
-            __builtin_nontemporal_store(S, a.sum + jm);
-            __builtin_nontemporal_store(F, a.sumsq + jm);
+        __syncthreads();
+        for (int64_t j = c0 + threadIdx.x; j < c1; j += kStatsThreads) {
+            const float s = park[0][j - c0], q = park[1][j - c0];
+            const float S = a.first ? s : a.sum[j] + s, F = a.first ? q : a.sumsq[j] + q;
+            __builtin_nontemporal_store(S, a.sum + j);
+            __builtin_nontemporal_store(F, a.sumsq + j);
             if (!(__builtin_isfinite(S) && __builtin_isfinite(F))) atomicOr(a.nonfinite, 1);
         }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
+        __syncthreads();
     }
 }
 
@@ -1346,9 +1342,15 @@ hipError_t launch_check_recip(uint32_t lo, uint32_t n, unsigned long long *count
 }
 
 hipError_t launch_stats(const StatsArgs &a, int f32, hipStream_t s) {
-    const dim3 grid(grid_for(a.J, kStatsPerBlock, 2 * kStreamGrid));
-    if (f32) hipLaunchKernelGGL(k_stats<1>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(k_stats<0>, grid, dim3(256), 0, s, a);
+    // one block per CU, each owning an even share of the super-groups (at most
+    // kStatsChunk; larger inputs take several shares per block)
+    const int64_t cus = device_cus();
+    int64_t chunk = (a.J + cus - 1) / cus;
+    if (chunk > kStatsChunk) chunk = kStatsChunk;
+    if (chunk < 1) chunk = 1;
+    const dim3 grid(grid_for(a.J, chunk, cus));
+    if (f32) hipLaunchKernelGGL(k_stats<1>, grid, dim3(kStatsThreads), 0, s, a, chunk);
+    else hipLaunchKernelGGL(k_stats<0>, grid, dim3(kStatsThreads), 0, s, a, chunk);
     return hipGetLastError();
 }
 
