@@ -1342,11 +1342,12 @@ hipError_t launch_check_recip(uint32_t lo, uint32_t n, unsigned long long *count
 }
 
 hipError_t launch_stats(const StatsArgs &a, int f32, hipStream_t s) {
-    // one block per CU, each owning an even share of the super-groups (at most
-    // kStatsChunk; larger inputs take several shares per block)
+    // one block per CU; the super-groups are cut into rounds x CUs even shares
+    // of at most kStatsChunk, with the fewest rounds that allows, so that every
+    // block does the same number of equal shares
     const int64_t cus = device_cus();
-    int64_t chunk = (a.J + cus - 1) / cus;
-    if (chunk > kStatsChunk) chunk = kStatsChunk;
+    const int64_t rounds = (a.J + cus * kStatsChunk - 1) / (cus * kStatsChunk);
+    int64_t chunk = (a.J + rounds * cus - 1) / (rounds * cus);
     if (chunk < 1) chunk = 1;
     const dim3 grid(grid_for(a.J, chunk, cus));
     if (f32) hipLaunchKernelGGL(k_stats<1>, grid, dim3(kStatsThreads), 0, s, a, chunk);
