@@ -214,18 +214,6 @@ __device__ __forceinline__ void part_info(const unsigned long long *C, int64_t m
     p.bytes = off;
 }
 
-struct SharedTables {
-    float dec2[4];
-    Pair lw2[3];
-    float dec4[16];
-    float dec8[256];
-    float cl4[16];
-    float cl8[256];
-    Pair lw4[15];
-    Pair lw8[255];
-    uint8_t b4[2 * kKeys];
-    uint8_t b8[2 * kKeys];
-};
 
 template <int B>
 __device__ __forceinline__ float level_of(const SharedTables &T, uint32_t code) {
@@ -496,24 +484,13 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po,
 template <int MODE, int LOCAL>
 // three 512-thread blocks per CU: six waves per SIMD, at most 80 VGPRs
 __global__ __launch_bounds__(kCodecThreads) __attribute__((amdgpu_waves_per_eu(6))) void k_codec(CodecArgs a) {
-    __shared__ __align__(16) SharedTables T;
-    const LevelTables &lev = a.tab->lev;
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) {
-        T.dec8[i] = lev.L8[i];
-        T.cl8[i] = lev.CL8[i];
+    __shared__ SharedTables T;
+    {
+        // the block's copy of the tables: the workspace keeps their LDS image
+        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(&a.tab->lds);
+        u32x4_t *dst = reinterpret_cast<u32x4_t *>(&T);
+        for (int i = threadIdx.x; i < (int)(sizeof(SharedTables) / 16); i += blockDim.x) dst[i] = src[i];
     }
-    for (int i = threadIdx.x; i < 255; i += blockDim.x) T.lw8[i] = lev.LW8[i];
-    for (int i = threadIdx.x; i < 2 * kKeys; i += blockDim.x) {
-        T.b8[i] = a.tab->b8.est[i];
-        T.b4[i] = a.tab->b4.est[i];
-    }
-    if (threadIdx.x < 16) {
-        T.dec4[threadIdx.x] = lev.L4[threadIdx.x];
-        T.cl4[threadIdx.x] = lev.CL4[threadIdx.x];
-    }
-    if (threadIdx.x < 15) T.lw4[threadIdx.x] = lev.LW4[threadIdx.x];
-    if (threadIdx.x < 4) T.dec2[threadIdx.x] = lev.L2[threadIdx.x];
-    if (threadIdx.x < 3) T.lw2[threadIdx.x] = Pair{lev.L2[threadIdx.x], lev.W2[threadIdx.x]};
     __syncthreads();
     // part layouts: uniform loads from the per-round part table
     const PartInfo Po = *a.part_out, Pi = *a.part_in;
@@ -1297,6 +1274,26 @@ __global__ __launch_bounds__(256) void k_build_tables(DeviceTables *t, double ep
         t->b8.est[2 * k + 1] = (unsigned char)est_of<256>(nh, eps);
         t->b4.est[2 * k] = (unsigned char)est_of<16>(lo, eps);
         t->b4.est[2 * k + 1] = (unsigned char)est_of<16>(nh, eps);
+    }
+    // the LDS image, from the tables just written (visible to the whole block
+    // after the barrier)
+    __syncthreads();
+    SharedTables &S = t->lds;
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) {
+        S.dec8[i] = v.L8[i];
+        S.cl8[i] = v.CL8[i];
+        if (i < 255) S.lw8[i] = v.LW8[i];
+        if (i < 16) {
+            S.dec4[i] = v.L4[i];
+            S.cl4[i] = v.CL4[i];
+        }
+        if (i < 15) S.lw4[i] = v.LW4[i];
+        if (i < 4) S.dec2[i] = v.L2[i];
+        if (i < 3) S.lw2[i] = Pair{v.L2[i], v.W2[i]};
+    }
+    for (int i = threadIdx.x; i < 2 * kKeys; i += blockDim.x) {
+        S.b8[i] = t->b8.est[i];
+        S.b4[i] = t->b4.est[i];
     }
 }
 

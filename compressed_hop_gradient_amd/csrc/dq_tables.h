@@ -141,10 +141,28 @@ constexpr bool buckets_hold_one_boundary(double eps) {
 
 // Everything the codec kernels read from their tables; one copy per plan in
 // the workspace (built on the host for the plan's level shape).
+// The tables as a codec block holds them in LDS: decode levels, compare
+// levels, (L, W) pairs and bucket entries of each class.  The workspace keeps
+// a byte image of it so that a block loads its copy with 16-byte reads.
+struct alignas(16) SharedTables {
+    float dec2[4];
+    Pair lw2[3];
+    float dec4[16];
+    float dec8[256];
+    float cl4[16];
+    float cl8[256];
+    Pair lw4[15];
+    Pair lw8[255];
+    unsigned char b4[2 * kKeys];
+    unsigned char b8[2 * kKeys];
+};
+static_assert(sizeof(SharedTables) % 16 == 0, "the image is copied in 16-byte pieces");
+
 struct DeviceTables {
     LevelTables lev;
     BucketTable<256> b8;
     BucketTable<16> b4;
+    SharedTables lds;      // the same tables in the LDS layout (filled by the device)
 };
 
 constexpr bool level_shape_ok(double eps) {
@@ -153,7 +171,7 @@ constexpr bool level_shape_ok(double eps) {
 }
 
 constexpr DeviceTables make_device_tables(double eps) {
-    return DeviceTables{make_tables(eps), make_buckets<256>(eps), make_buckets<16>(eps)};
+    return DeviceTables{make_tables(eps), make_buckets<256>(eps), make_buckets<16>(eps), SharedTables{}};
 }
 
 static_assert(level_shape_ok(kDefaultEps), "default level shape: one boundary per bucket");  // needs -fconstexpr-steps
