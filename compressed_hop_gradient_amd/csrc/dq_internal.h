@@ -11,8 +11,6 @@ constexpr int kSG = 256;          // coordinates per super-group
 constexpr int kGroup = 16;        // coordinates per group (one lane owns one group)
 constexpr int kGroupsPerSG = 16;
 constexpr int kSGPerBlock = 16;   // finalize: 4 waves x 4 super-groups
-constexpr int kCodecThreads = 512;                 // codec kernels: 8 waves
-constexpr int kCodecSGPerBlock = kCodecThreads / 16;   // one super-group per 16-lane row
 constexpr int kReorderSGPerBlock = 1024;  // allocation/reorder: 256 threads x 4
 // The scalar rho is found by an exact radix search on its fp32 bit pattern:
 // pass p fixes the bits above kRadixShift[p] by testing up to 256 candidates.

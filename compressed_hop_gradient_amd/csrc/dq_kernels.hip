@@ -481,9 +481,26 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po,
     }   // MODE != kPartial
 }
 
+// Block layout of each codec kernel, one super-group per 16-lane row.  The
+// kernels with a bf16 local run 256-thread blocks (compress 8 per CU, the hop 7,
+// the fused last hop 5 as its output staging allows); the others 512-thread
+// blocks, 3 per CU.  Measured per kernel: with the packed local the larger
+// blocks are 4.6% faster, with the bf16 local the smaller ones 1-4%.
 template <int MODE, int LOCAL>
-// three 512-thread blocks per CU: six waves per SIMD, at most 80 VGPRs
-__global__ __launch_bounds__(kCodecThreads) __attribute__((amdgpu_waves_per_eu(6))) void k_codec(CodecArgs a) {
+struct CodecShape {
+    static constexpr bool kSmall = LOCAL == kLocalBF16 && MODE != kPartial;
+    static constexpr int threads = kSmall ? 256 : 512;
+    static constexpr int sg_per_block = threads / 16;
+    static constexpr int blocks_per_cu = kSmall ? (MODE == kCompress ? 8 : (MODE == kHopFinal ? 5 : 7)) : 3;
+    static constexpr int waves_per_simd = blocks_per_cu * threads / 256;   // 4 SIMDs per CU
+};
+
+template <int MODE, int LOCAL>
+__global__ __launch_bounds__((CodecShape<MODE, LOCAL>::threads))
+__attribute__((amdgpu_waves_per_eu(CodecShape<MODE, LOCAL>::waves_per_simd)))
+void k_codec(CodecArgs a) {
+    using Shape = CodecShape<MODE, LOCAL>;
+    constexpr int kThreads = Shape::threads, kSGPerBlock = Shape::sg_per_block;
     __shared__ SharedTables T;
     {
         // the block's copy of the tables: the workspace keeps their LDS image
@@ -501,13 +518,13 @@ __global__ __launch_bounds__(kCodecThreads) __attribute__((amdgpu_waves_per_eu(6
     const int g = lane & 15, row = lane >> 4;
     const uint32_t N = (uint32_t)Po.N, pre1 = (uint32_t)Po.pre[1], pre2 = (uint32_t)Po.pre[2];
     // the fused final hop stages each row's decoded super-group here
-    constexpr int kStageRows = MODE == kHopFinal ? kCodecThreads / 16 : 1;
+    constexpr int kStageRows = MODE == kHopFinal ? kThreads / 16 : 1;
     __shared__ __align__(16) float stage[kStageRows][kSG];
     float *stage_row = stage[MODE == kHopFinal ? threadIdx.x / 16 : 0];
     // per row: the original index and mean of the row's next super-group,
     // fetched during the current one (see codec_sg)
-    __shared__ uint32_t next_j[kCodecThreads / 16];
-    __shared__ float next_mu[kCodecThreads / 16];
+    __shared__ uint32_t next_j[kThreads / 16];
+    __shared__ float next_mu[kThreads / 16];
     uint32_t *slot_j = &next_j[threadIdx.x / 16];
     float *slot_mu = &next_mu[threadIdx.x / 16];
     // (selects, not an index into Po's arrays: a runtime index would put the
@@ -516,10 +533,10 @@ __global__ __launch_bounds__(kCodecThreads) __attribute__((amdgpu_waves_per_eu(6
     auto pos_of = [&](uint32_t tt) -> uint32_t {
         return tt < pre1 ? lo0 + tt : (tt < pre2 ? lo1 + (tt - pre1) : lo2 + (tt - pre2));
     };
-    const uint32_t stride = gridDim.x * kCodecSGPerBlock;
+    const uint32_t stride = gridDim.x * kSGPerBlock;
     constexpr bool kAhead = codec_ahead<MODE, LOCAL>();
     if (kAhead) {
-        const uint32_t t0 = blockIdx.x * kCodecSGPerBlock + wave * 4 + row;
+        const uint32_t t0 = blockIdx.x * kSGPerBlock + wave * 4 + row;
         if (t0 < N && g == 0) {
             const uint32_t p0 = pos_of(t0);
             *slot_j = (uint32_t)a.perm[p0];
@@ -528,7 +545,7 @@ __global__ __launch_bounds__(kCodecThreads) __attribute__((amdgpu_waves_per_eu(6
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
     }
-    for (uint32_t base = blockIdx.x * kCodecSGPerBlock; base < N; base += stride) {
+    for (uint32_t base = blockIdx.x * kSGPerBlock; base < N; base += stride) {
         const uint32_t t = base + wave * 4 + row;
         if (t >= N) continue;
         uint32_t j = 0u;
@@ -1390,25 +1407,24 @@ static int64_t device_cus() {
     return cus;
 }
 
-// Grid of a codec launch over n super-groups: whole "waves" of 3 blocks of 8
-// waves per CU (the hop kernels' occupancy, 6 waves per SIMD; a partial last
-// wave leaves CUs idle at the end): one wave while that gives each block
-// fewer than about 18 grid-stride iterations, else two.  Measured on launches
-// of 1.6e5 to 2e6 super-groups (BERT-, LLaMA- and Gemma-shaped parts): one
-// wave up to 3e5, two from 4.9e5 on, 3-9% faster than a fixed grid at the
-// small end; the compress kernel, which could hold more, is also fastest this
-// way.  512-thread blocks beat 256 (half the per-block table copies) by 1-3%.
-constexpr int64_t kCodecBlocksPerCU = 3;
-static dim3 codec_grid(int64_t n) {
-    const int64_t wave = device_cus() * kCodecBlocksPerCU;
-    int64_t waves = (n + wave * kCodecSGPerBlock * 6) / (wave * kCodecSGPerBlock * 12);
+// Grid of a codec launch over n super-groups: whole "waves" of the kernel's
+// resident blocks (a partial last wave leaves CUs idle at the end): one wave
+// while that gives each block fewer than about 18 grid-stride iterations, else
+// two.  Measured on launches of 1.6e5 to 2e6 super-groups (BERT-, LLaMA- and
+// Gemma-shaped parts): one wave up to 3e5, two from 4.9e5 on, 3-9% faster
+// than a fixed grid at the small end.
+static dim3 codec_grid(int64_t n, int64_t blocks_per_cu, int64_t sg_per_block) {
+    const int64_t wave = device_cus() * blocks_per_cu;
+    int64_t waves = (n + wave * sg_per_block * 6) / (wave * sg_per_block * 12);
     waves = waves < 1 ? 1 : (waves > 2 ? 2 : waves);
-    return dim3(grid_for(n, kCodecSGPerBlock, wave * waves));
+    return dim3(grid_for(n, sg_per_block, wave * waves));
 }
 
 template <int MODE, int LOCAL>
 static hipError_t launch_codec_t(const CodecArgs &a, int64_t max_sg, hipStream_t s) {
-    hipLaunchKernelGGL((k_codec<MODE, LOCAL>), codec_grid(max_sg), dim3(kCodecThreads), 0, s, a);
+    using Shape = CodecShape<MODE, LOCAL>;
+    hipLaunchKernelGGL((k_codec<MODE, LOCAL>), codec_grid(max_sg, Shape::blocks_per_cu, Shape::sg_per_block),
+                       dim3(Shape::threads), 0, s, a);
     return hipGetLastError();
 }
 
