@@ -17,6 +17,7 @@ Printed as one JSON line:
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -56,10 +57,16 @@ def dar_bytes_per_coord(achieved_bits):
 
 
 def kernel_source_hash():
+    """Identity of the kernel code behind a profile: the kernel sources with
+    comments and blank space removed, so that editing a comment keeps the
+    committed counters valid and any change to the code does not."""
     h = hashlib.sha256()
     for f in ("dq_kernels.hip", "dq_tables.h", "dq_internal.h"):
-        with open(os.path.join(ROOT, "compressed_hop_gradient_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "compressed_hop_gradient_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)       # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                     # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

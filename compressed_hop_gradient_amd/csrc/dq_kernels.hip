@@ -5,13 +5,16 @@
 // wavefronts:
 //   * stats: 16 lanes per super-group (SG), each lane two 128-bit loads of 8
 //     bf16 (partials l and l + 16); 8 sequential adds per partial, then the
-//     tree over the 32 partials (one in-lane step, four DPP row shifts);
-//   * codec (compress / hop / finalize): one 16-lane DPP row per SG, one lane
-//     per group of 16 coordinates, so group scales are per-lane scalars and the
-//     SG maximum is a 4-step DPP row reduction; 128-bit loads of codes and of
-//     the local bf16 gradient; level tables staged in LDS once per block;
-//   * allocation: integer counts only (order-free), bisection on the fp32 bit
-//     pattern of the scalar with no host round trip;
+//     tree over the 32 partials (one in-lane step, four DPP row shifts); one
+//     resident block per CU parks its results in LDS and writes the running
+//     sums in one burst after its share has been read;
+//   * codec (compress / hop / fused last hop / finalize): one 16-lane DPP row
+//     per SG, one lane per group of 16 coordinates, so group scales are
+//     per-lane scalars and the SG maximum is a 4-step DPP row reduction;
+//     128-bit loads of codes and of the local bf16 gradient; level tables
+//     copied into LDS once per block from an image kept in the workspace;
+//   * allocation: integer counts only (order-free), a 4-pass radix search on
+//     the fp32 bit pattern of the scalar with no host round trip;
 //   * reorder: per-block counts, one scan block, stable per-block scatter.
 //
 // Numerics follow the readings shared with the CPU oracle: fp32, round to
