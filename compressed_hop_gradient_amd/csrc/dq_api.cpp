@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <cstddef>
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -292,7 +293,9 @@ dq_status dq_plan_create(int64_t n_coords, int32_t n_workers, int32_t topology, 
     p->topo = topology;
     p->L = L;
     p->budget = avg_bits;
-    p->budget_bits = (long long)std::floor((double)avg_bits * (double)p->J);
+    // floor(B J); the widths sum to at most 8 J, so any B >= 8 (including
+    // +inf) is the budget 8 J and the product stays in range
+    p->budget_bits = (long long)std::floor(std::min((double)avg_bits, 8.0) * (double)p->J);
     p->nblk = (p->J + kReorderSGPerBlock - 1) / kReorderSGPerBlock;
     compute_layout(p);
     *out = p;

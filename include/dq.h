@@ -132,7 +132,7 @@ typedef struct dq_info {
     float rho;
     float t12, t24, t48;       /* fl(85 rho), fl(544 rho), fl(16384 rho) */
     int64_t class_counts[3];   /* super-groups at 2, 4, 8 bits */
-    int64_t budget_bits;       /* floor(avg_bits * J) */
+    int64_t budget_bits;       /* floor(min(avg_bits, 8) * J) */
     int64_t used_bits;         /* sum of widths over super-groups */
     double achieved_bits;      /* used_bits / J (payload bits per coordinate) */
     int32_t nonfinite;         /* 1 if a gradient value or square was not finite */
@@ -169,7 +169,8 @@ typedef struct dq_timing {
 
 /* Host-only; allocates no device memory.  n_coords > 0 and a multiple of 256;
  * n_workers in 1..65536 (a power of two for DQ_BUTTERFLY).  avg_bits is the
- * payload budget in bits per coordinate (>= 2; > 8 means every width is 8).
+ * payload budget in bits per coordinate (>= 2; 8 or more, +inf included,
+ * means every width is 8).
  * The kernels address a region with 32-bit offsets, so the largest region
  * the schedule writes (a part of m = n for a ring, m = 2 for a butterfly,
  * the whole vector for n = 1), sized at 276 bytes per super-group, must stay

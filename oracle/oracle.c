@@ -232,7 +232,10 @@ int or_stats(or_ctx *c, int32_t worker, const void *grad, int32_t dtype) {
 /* ------------------------------------------------------------------ */
 
 int64_t or_budget_bits(const or_ctx *c) {
-    return (int64_t)floor((double)c->budget * (double)c->J);
+    /* sum_j q_j never exceeds 8 J, so every budget of 8 bits or more is the */
+    /* same constraint; capping it keeps the product finite (B may be +inf) */
+    const double b = c->budget < 8.0f ? (double)c->budget : 8.0;
+    return (int64_t)floor(b * (double)c->J);
 }
 
 static int width_of(float F, float t4, float t8) {

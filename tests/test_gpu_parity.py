@@ -353,12 +353,13 @@ def test_tiny_and_empty_parts(J, n, topo):
     full_round(_scaled("bert", J, workers=range(n)), topo)
 
 
-@pytest.mark.parametrize("budget", [2.0, 8.0, 100.0, 2.0001, 7.999])
+@pytest.mark.parametrize("budget", [2.0, 8.0, 100.0, 2.0001, 7.999, float("inf")])
 def test_budget_extremes(budget):
     _need_gpu()
     r, info, out = full_round(_scaled("llama", 517, workers=range(4)), dq.RING, budget=budget)
     if budget >= 8:
         assert info["class_counts"] == [0, 0, 517] and info["rho_bits"] == 0
+        assert info["budget_bits"] == 8 * 517
     if budget == 2.0:
         assert info["class_counts"] == [517, 0, 0]
 

@@ -872,6 +872,18 @@ def test_uniform_allocation(budget, q):
     assert 40 * q <= o.budget_bits()
 
 
+@pytest.mark.parametrize("budget", [8.0, 9.5, 1e30, float("inf")])
+def test_budgets_of_eight_bits_or_more_give_all_eight(budget):
+    """The widths sum to at most 8 J, so any budget of 8 bits or more is met
+    at rho = 0 with every super-group 8-bit; the bit budget is then 8 J even
+    for a budget whose product with J leaves the integer range."""
+    rng = np.random.default_rng(29)
+    gs = [rng.standard_normal(256 * 40).astype(np.float32) for _ in range(3)]
+    o = _variant_round(gs, budget, po.ALLOC_THRESHOLD)
+    assert o.budget_bits() == 8 * 40
+    assert o.rho_bits() == 0 and (o.widths() == 8).all()
+
+
 def test_variable_widths_beat_uniform_unless_shuffled():
     """Table 6 direction: at 4 bits per coordinate, variable widths give a
     lower vNMSE than uniform 4-bit codes on gradients with skewed, spatially
