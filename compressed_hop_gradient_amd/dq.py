@@ -137,6 +137,25 @@ def _kind(t):
     raise TypeError(f"unsupported tensor dtype {t.dtype}")
 
 
+def _tensor(t, what, device, numel=None, min_bytes=None, dtype=None):
+    """Reject what the kernels cannot address safely: tensors on the host or on
+    another device, non-contiguous views and buffers shorter than the call
+    writes or reads (the C ABI takes bare pointers and cannot check sizes)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.device != device:
+        raise ValueError(f"{what}: tensor on {t.device}, the plan works on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: tensor must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what}: dtype {t.dtype}, expected {dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{what}: {t.numel()} elements, expected {numel}")
+    if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
+        raise ValueError(f"{what}: {t.numel() * t.element_size()} bytes, the call needs {min_bytes}")
+    return t
+
+
 def check_reciprocal(lo_bits, count, device=None, stream=None):
     """Mismatches between the codec's reciprocal and the IEEE quotient 1/x over
     the fp32 bit patterns [lo_bits, lo_bits + count) (runs on the GPU)."""
@@ -162,6 +181,9 @@ class Plan:
         self.J = self.d // 256
         self.topology = int(topology)
         self.log2n = max(0, (self.n - 1).bit_length())
+        self.own = int(own)
+        if torch.device(device).type != "cuda":
+            raise ValueError(f"the plan's workspace must be GPU memory, not {device}")
         h = C.c_void_p()
         _check(lib().dq_plan_create(self.d, self.n, self.topology, float(avg_bits), C.byref(h)),
                "dq_plan_create")
@@ -179,6 +201,7 @@ class Plan:
                 self.set(OPT_STREAMS, streams)
         nbytes = lib().dq_workspace_bytes(self.h)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.device = self.workspace.device
         _check(lib().dq_plan_bind(self.h, _ptr(self.workspace), nbytes), "dq_plan_bind")
         lay = dq_layout()
         _check(lib().dq_workspace_layout(self.h, C.byref(lay)), "dq_workspace_layout")
@@ -193,8 +216,61 @@ class Plan:
     def set(self, option, value):
         _check(lib().dq_plan_set_u64(self.h, int(option), int(value)), "dq_plan_set_u64")
 
+    # ---- buffer sizes the schedule implies (for the argument checks) ---------
+    def _m_compress(self):
+        """m of the part a compress writes: the whole vector for one worker,
+        a ring part (m = n), or a butterfly level-1 half (m = 2)."""
+        return 1 if self.n == 1 else (self.n if self.topology == RING else 2)
+
+    def _m_hop(self, step):
+        """(m of the part a hop reads, m of each region it writes), or None
+        for a step outside the schedule (the library rejects those)."""
+        if self.n == 1:
+            return None
+        if self.topology == RING:
+            return (self.n, self.n) if 1 <= step < self.n else None
+        if not 1 <= step <= self.log2n:
+            return None
+        m = 1 << step
+        return (m, 2 * m if step < self.log2n else m)
+
+    def _check_hop(self, worker, step, region_in, local, kind, outs):
+        ms = self._m_hop(int(step))
+        dev = self.device
+        _tensor(region_in, "region_in", dev)
+        _tensor(local, "local", dev)
+        for i, o in enumerate(outs):
+            if o is not None:
+                _tensor(o, f"out{i}", dev)
+        if ms is None:
+            return
+        m_in, m_out = ms
+        _tensor(region_in, "region_in", dev, min_bytes=self.region_bytes_max(m_in))
+        if kind in (BF16, F32):
+            _tensor(local, "local", dev, numel=self.d)
+        elif kind == PACKED:
+            _tensor(local, "local", dev, min_bytes=self.region_bytes_max(m_in))
+        elif kind == F32_PARTIAL:
+            _tensor(local, "local", dev, min_bytes=self.partial_bytes_max(m_in))
+        two = self.topology == BUTTERFLY and step < self.log2n
+        # own-fp32: the child this worker keeps is written as fp32 partial sums
+        keep = (int(worker) >> (self.log2n - int(step) - 1)) & 1 if two and self.own == OWN_F32 else -1
+        for h, o in enumerate(outs):
+            if o is not None:
+                need = self.partial_bytes_max(m_out) if h == keep else self.region_bytes_max(m_out)
+                _tensor(o, f"out{h}", dev, min_bytes=need)
+
+    def _check_grads(self, grads):
+        if len(grads) != self.n:
+            raise ValueError(f"{len(grads)} gradients for {self.n} workers")
+        kind = _kind(grads[0])
+        for w, g in enumerate(grads):
+            _tensor(g, f"grads[{w}]", self.device, numel=self.d, dtype=grads[0].dtype)
+        return kind
+
     # ---- stages --------------------------------------------------------
     def stats(self, worker, grad, stream=None):
+        _tensor(grad, "grad", self.device, numel=self.d)
         _check(lib().dq_stats(self.h, int(worker), _ptr(grad), _kind(grad), _stream(stream)),
                "dq_stats")
 
@@ -205,6 +281,8 @@ class Plan:
         _check(lib().dq_reorder(self.h, _stream(stream)), "dq_reorder")
 
     def compress(self, worker, step, grad, region_out, stream=None):
+        _tensor(grad, "grad", self.device, numel=self.d)
+        _tensor(region_out, "region_out", self.device, min_bytes=self.region_bytes_max(self._m_compress()))
         _check(lib().dq_compress(self.h, int(worker), int(step), _ptr(grad), _kind(grad),
                                  _ptr(region_out), _stream(stream)), "dq_compress")
 
@@ -212,16 +290,21 @@ class Plan:
         """local_kind: F32_PARTIAL for the own fp32 partial sums (OWN_F32);
         otherwise taken from the tensor's dtype."""
         kind = _kind(local) if local_kind is None else int(local_kind)
+        self._check_hop(worker, step, region_in, local, kind, (out0, out1))
         _check(lib().dq_hop(self.h, int(worker), int(step), _ptr(region_in), _ptr(local),
                             kind, _ptr(out0), None if out1 is None else _ptr(out1),
                             _stream(stream)), "dq_hop")
 
     def hop_finalize(self, worker, step, region_in, local, region_out, out, stream=None, local_kind=None):
         kind = _kind(local) if local_kind is None else int(local_kind)
+        self._check_hop(worker, step, region_in, local, kind, (region_out,))
+        _tensor(out, "out", self.device, min_bytes=4 * self.d, dtype=torch.float32)
         _check(lib().dq_hop_finalize(self.h, int(worker), int(step), _ptr(region_in), _ptr(local), kind,
                                      _ptr(region_out), _ptr(out), _stream(stream)), "dq_hop_finalize")
 
     def finalize(self, part, region, out, stream=None):
+        _tensor(region, "region", self.device, min_bytes=self.region_bytes_max(self.n))
+        _tensor(out, "out", self.device, min_bytes=4 * self.d, dtype=torch.float32)
         _check(lib().dq_finalize(self.h, int(part), _ptr(region), _ptr(out), _stream(stream)),
                "dq_finalize")
 
@@ -241,42 +324,34 @@ class Plan:
     def arena_bytes(self):
         return int(lib().dq_arena_bytes(self.h))
 
-    def allreduce(self, grads, out=None, arena=None, stream=None):
-        assert len(grads) == self.n
-        kind = _kind(grads[0])
-        dev = grads[0].device
+    def _round_buffers(self, grads, out, arena, arena_bytes):
+        kind = self._check_grads(grads)
         if arena is None:
-            arena = torch.empty(self.arena_bytes(), dtype=torch.uint8, device=dev)
+            arena = torch.empty(max(1, arena_bytes), dtype=torch.uint8, device=self.device)
         if out is None:
-            out = torch.empty(self.d, dtype=torch.float32, device=dev)
+            out = torch.empty(self.d, dtype=torch.float32, device=self.device)
+        _tensor(arena, "arena", self.device)
+        _tensor(out, "out", self.device, min_bytes=4 * self.d, dtype=torch.float32)
         ptrs = (C.c_void_p * self.n)(*[g.data_ptr() for g in grads])
-        _check(lib().dq_allreduce(self.h, ptrs, kind, _ptr(arena), arena.numel(), _ptr(out),
+        return kind, out, arena, arena.numel() * arena.element_size(), ptrs
+
+    def allreduce(self, grads, out=None, arena=None, stream=None):
+        kind, out, arena, nbytes, ptrs = self._round_buffers(grads, out, arena, self.arena_bytes())
+        _check(lib().dq_allreduce(self.h, ptrs, kind, _ptr(arena), nbytes, _ptr(out),
                                   _stream(stream)), "dq_allreduce")
         return out
 
     def mxfp8_allreduce(self, grads, out=None, arena=None, stream=None):
-        kind = _kind(grads[0])
-        dev = grads[0].device
-        if arena is None:
-            arena = torch.empty(max(1, int(lib().dq_mxfp8_arena_bytes(self.h))), dtype=torch.uint8,
-                                device=dev)
-        if out is None:
-            out = torch.empty(self.d, dtype=torch.float32, device=dev)
-        ptrs = (C.c_void_p * self.n)(*[g.data_ptr() for g in grads])
-        _check(lib().dq_mxfp8_allreduce(self.h, ptrs, kind, _ptr(arena), arena.numel(), _ptr(out),
+        kind, out, arena, nbytes, ptrs = self._round_buffers(
+            grads, out, arena, int(lib().dq_mxfp8_arena_bytes(self.h)))
+        _check(lib().dq_mxfp8_allreduce(self.h, ptrs, kind, _ptr(arena), nbytes, _ptr(out),
                                         _stream(stream)), "dq_mxfp8_allreduce")
         return out
 
     def mx_allreduce(self, fmt, grads, out=None, arena=None, stream=None):
-        kind = _kind(grads[0])
-        dev = grads[0].device
-        if arena is None:
-            arena = torch.empty(max(1, int(lib().dq_mx_arena_bytes(self.h))), dtype=torch.uint8,
-                                device=dev)
-        if out is None:
-            out = torch.empty(self.d, dtype=torch.float32, device=dev)
-        ptrs = (C.c_void_p * self.n)(*[g.data_ptr() for g in grads])
-        _check(lib().dq_mx_allreduce(self.h, int(fmt), ptrs, kind, _ptr(arena), arena.numel(), _ptr(out),
+        kind, out, arena, nbytes, ptrs = self._round_buffers(
+            grads, out, arena, int(lib().dq_mx_arena_bytes(self.h)))
+        _check(lib().dq_mx_allreduce(self.h, int(fmt), ptrs, kind, _ptr(arena), nbytes, _ptr(out),
                                      _stream(stream)), "dq_mx_allreduce")
         return out
 
