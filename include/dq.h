@@ -194,9 +194,9 @@ typedef enum dq_option_f64 {
      * review's ledger names the level set Q = {f(eps, r)} and notes that the
      * paper never states eps).  Default 1/2; 1 is the uniform grid.  Accepted
      * for eps in (0, 1] when every bucket of the kernels' interval search holds
-     * at most one level boundary (true at least for eps >= 0.01).  Rebuilds the
-     * plan's tables; if a workspace is bound they are copied into it at once
-     * (synchronous).  Set it between rounds, not inside one. */
+     * at most one level boundary (true at least for eps >= 0.01).  The first
+     * dq_stats of the next round rebuilds the tables in the workspace on the
+     * device.  Set it between rounds, not inside one. */
     DQ_OPT_EPS = 0
 } dq_option_f64;
 dq_status dq_plan_set_f64(dq_plan *plan, int32_t option, double value);
@@ -205,9 +205,10 @@ dq_status dq_plan_set_f64(dq_plan *plan, int32_t option, double value);
 size_t dq_workspace_bytes(const dq_plan *plan);
 
 /* Bind caller-owned device memory (>= dq_workspace_bytes, 256-byte aligned).
- * Copies the plan's level and bucket tables into it (a synchronous
- * host-to-device copy, the only one the library makes).
- * Errors: DQ_ENULL, DQ_EWORKSPACE, DQ_EHIP. */
+ * Nothing is copied: the first dq_stats of the next round writes the plan's
+ * level and bucket tables into the workspace on the device, ahead of every
+ * codec launch on that stream.  A bind starts a new round.
+ * Errors: DQ_ENULL, DQ_EWORKSPACE. */
 dq_status dq_plan_bind(dq_plan *plan, void *d_workspace, size_t bytes);
 
 dq_status dq_workspace_layout(const dq_plan *plan, dq_layout *out);
