@@ -47,13 +47,33 @@ def parse():
     return ap.parse_args()
 
 
-def dar_bytes_per_coord(achieved_bits):
-    """Algorithmic HBM bytes per coordinate of the DAR hop with a bf16 local:
-    read the incoming region ((b + 0.625)/8 B: codes + fp32 scale unit + 16
-    UINT8 group codes per 256), read the local bf16 (2 B), read perm and mean
-    (8 B per 256), write the outgoing region ((b + 0.625)/8 B)."""
+def dar_bytes_per_coord(achieved_bits, in_bytes=2.0):
+    """Algorithmic HBM bytes per coordinate of the DAR hop with a gradient
+    local: read the incoming region ((b + 0.625)/8 B: codes + fp32 scale unit +
+    16 UINT8 group codes per 256), read the local gradient (2 B bf16, 4 B
+    fp32), read perm and mean (8 B per 256), write the outgoing region
+    ((b + 0.625)/8 B)."""
     region = (achieved_bits + 0.625) / 8.0
-    return 2.0 * region + 2.0 + 8.0 / 256.0
+    return 2.0 * region + in_bytes + 8.0 / 256.0
+
+
+def stage_bytes_per_coord(kind, achieved_bits, in_bytes, n_workers):
+    """Algorithmic HBM bytes per coordinate of each streaming stage, with
+    P = (b + 0.625)/8 the region bytes per coordinate at b achieved bits and
+    in_bytes the gradient element size.  Stats: the gradient, plus the running
+    sums (8 B per 256 written by worker 0, read and written by the others).
+    Codec stages read perm and the mean (8 B per 256).  None for the small
+    allocate / reorder passes and the MX reference."""
+    P = (achieved_bits + 0.625) / 8.0
+    meta = 8.0 / 256.0
+    return {
+        "stats": in_bytes + (8.0 + 16.0 * (n_workers - 1)) / n_workers / 256.0,
+        "compress": in_bytes + meta + P,
+        "hop_grad": dar_bytes_per_coord(achieved_bits, in_bytes),
+        "hop_packed": 3.0 * P + meta,
+        "hop_final": 3.0 * P + meta + 4.0,
+        "finalize": P + meta + 4.0,
+    }.get(kind)
 
 
 def kernel_source_hash():
@@ -70,26 +90,35 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel, src_hash):
-    """HBM bytes per launch from rocprofv3 PMC runs, if taken on this kernel source."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def _profile_record(name, workload):
+    """A committed counter summary, if it was taken on this workload:
+    {"name", "avg_bits"} as bench.py runs it."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
+    return rec if rec.get("workload") == workload else None
+
+
+def measured_traffic(kernel, src_hash, workload):
+    """HBM bytes per launch from rocprofv3 PMC runs, if taken on this kernel
+    source and workload."""
+    rec = _profile_record("traffic.json", workload)
+    if rec is None:
+        return None
     e = rec.get(kernel)
     if not e or e.get("kernel_source") != src_hash:
         return None
     return e.get("bytes_per_launch")
 
 
-def measured_valu(kernel, src_hash):
-    """VALU issue rate of a kernel from a rocprofv3 SQ counter run, if taken on this kernel source."""
-    path = os.path.join(ROOT, "profiles", "valu.json")
-    if not os.path.exists(path):
+def measured_valu(kernel, src_hash, workload):
+    """VALU issue rate of a kernel from a rocprofv3 SQ counter run, if taken on
+    this kernel source and workload."""
+    rec = _profile_record("valu.json", workload)
+    if rec is None:
         return None
-    with open(path) as f:
-        rec = json.load(f)
     e = rec.get(kernel)
     if not e or e.get("kernel_source") != src_hash:
         return None
@@ -249,20 +278,27 @@ def main():
     value = dar_coords / secs
 
     b = info["achieved_bits"]
-    bpc = dar_bytes_per_coord(b)
+    in_bytes = 2.0 if grads[0].dtype == torch.bfloat16 else 4.0
+    bpc = dar_bytes_per_coord(b, in_bytes)
     hg = tim_hop["hop_grad"]
     launches = max(1, hg["launches"])
     bytes_per_launch = hg["coords"] / launches * bpc
     avg_ms = hg["ms"] / launches
     achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
     src_hash = kernel_source_hash()
-    traffic = measured_traffic("hop_grad", src_hash)
+    prof_wl = {"name": args.workload, "avg_bits": float(budget)}
+    traffic = measured_traffic("hop_grad", src_hash, prof_wl)
 
     kernels = {}
     for k, v in tim.items():        # one fully timed round
         if v["launches"]:
-            kernels[k] = {"ms_per_step": v["ms"], "launches_per_step": v["launches"],
-                          "coords_per_s": (v["coords"] / (v["ms"] * 1e-3)) if v["ms"] > 0 else None}
+            cps = (v["coords"] / (v["ms"] * 1e-3)) if v["ms"] > 0 else None
+            kernels[k] = {"ms_per_step": v["ms"], "launches_per_step": v["launches"], "coords_per_s": cps}
+            bpc_k = stage_bytes_per_coord(k, b, in_bytes, wl.n)
+            if bpc_k is not None and cps is not None:
+                gbs = cps * bpc_k / 1e9
+                kernels[k].update({"bytes_per_coord": bpc_k, "GBs": gbs,
+                                   "frac_of_hbm_peak": gbs / HBM_PEAK_GBS})
 
     quality = None
     if not args.no_quality:
@@ -383,12 +419,13 @@ def main():
                    "input_dtype": wl.dtype},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "DAR hop, bf16 local (k_codec<hop,bf16>)",
+                     "kernel": ("DAR hop, bf16 local (k_codec<hop,bf16>)" if in_bytes == 2.0
+                                else "DAR hop, fp32 local (k_codec<hop,f32>)"),
                      "algorithmic_bytes_per_launch": bytes_per_launch,
                      "bytes_per_coord": bpc, "avg_launch_ms": avg_ms, "launches": hg["launches"],
                      "kernel_source": src_hash,
                      "achievable_copy_GBs": copy_gbs, "frac_of_copy": achieved / copy_gbs,
-                     "valu_issue": measured_valu("hop_grad", src_hash)},
+                     "valu_issue": measured_valu("hop_grad", src_hash, prof_wl)},
         "dar_kernel_coords_per_s": (hg["coords"] / (hg["ms"] * 1e-3)) if hg["ms"] > 0 else None,
         "kernels": kernels,
         "graph_replay_ms_per_step": graph_ms,
