@@ -57,12 +57,15 @@ def dar_bytes_per_coord(achieved_bits, in_bytes=2.0):
     return 2.0 * region + in_bytes + 8.0 / 256.0
 
 
-def stage_bytes_per_coord(kind, achieved_bits, in_bytes, n_workers):
+def stage_bytes_per_coord(kind, achieved_bits, in_bytes, n_workers, packed_last):
     """Algorithmic HBM bytes per coordinate of each streaming stage, with
     P = (b + 0.625)/8 the region bytes per coordinate at b achieved bits and
     in_bytes the gradient element size.  Stats: the gradient, plus the running
     sums (8 B per 256 written by worker 0, read and written by the others).
-    Codec stages read perm and the mean (8 B per 256).  None for the small
+    Codec stages read perm and the mean (8 B per 256).  The fused last hop
+    reads the incoming region and its local operand -- the worker's own packed
+    region at a butterfly level >= 2 (packed_last), the gradient otherwise --
+    and writes its region and 4 B of fp32 output.  None for the small
     allocate / reorder passes and the MX reference."""
     P = (achieved_bits + 0.625) / 8.0
     meta = 8.0 / 256.0
@@ -71,7 +74,7 @@ def stage_bytes_per_coord(kind, achieved_bits, in_bytes, n_workers):
         "compress": in_bytes + meta + P,
         "hop_grad": dar_bytes_per_coord(achieved_bits, in_bytes),
         "hop_packed": 3.0 * P + meta,
-        "hop_final": 3.0 * P + meta + 4.0,
+        "hop_final": 2.0 * P + (P if packed_last else in_bytes) + meta + 4.0,
         "finalize": P + meta + 4.0,
     }.get(kind)
 
@@ -294,7 +297,7 @@ def main():
         if v["launches"]:
             cps = (v["coords"] / (v["ms"] * 1e-3)) if v["ms"] > 0 else None
             kernels[k] = {"ms_per_step": v["ms"], "launches_per_step": v["launches"], "coords_per_s": cps}
-            bpc_k = stage_bytes_per_coord(k, b, in_bytes, wl.n)
+            bpc_k = stage_bytes_per_coord(k, b, in_bytes, wl.n, topo == dq.BUTTERFLY and wl.n >= 4)
             if bpc_k is not None and cps is not None:
                 gbs = cps * bpc_k / 1e9
                 kernels[k].update({"bytes_per_coord": bpc_k, "GBs": gbs,
