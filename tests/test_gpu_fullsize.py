@@ -87,19 +87,22 @@ def _steps(n, topo):
             yield ("hop", None, s)
 
 
-def _run(name, budget, capsys, budgets_stage_only=()):
+def _run(name, budget, capsys, budgets_stage_only=(), d=None, n=None):
+    """The workload's recipe and schedule; d and n override its size."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     wl = synth.WORKLOADS[name]
     topo = dq.BUTTERFLY if wl.topology == "butterfly" else dq.RING
-    n, d = wl.n, wl.d
+    n = wl.n if n is None else n
+    d = wl.d if d is None else d
+    label = name if (n, d) == (wl.n, wl.d) else f"{name} recipe, {d} coords x {n}"
 
     def say(msg):
         with capsys.disabled():
-            print(f"[fullsize {name}] {msg}", flush=True)
+            print(f"[fullsize {label}] {msg}", flush=True)
 
     say("generating")
-    grads = synth.generate(name, device=DEV)
+    grads = synth.generate(name, device=DEV, d=d, workers=range(n))
     torch.cuda.synchronize()
     say("host copy")
     gnp = [_host(g) for g in grads]
@@ -235,3 +238,20 @@ def test_llama_full(capsys):
 @pytest.mark.timeout(900)
 def test_large_full(capsys):
     _run("large", 5.0, capsys)
+
+
+# the largest part a plan admits: (J/m + 3) * 276 + 256 bytes must stay below
+# 2^32 (32-bit offsets inside a region), so J/m <= 15,561,471
+MAX_PART_SG = 15_561_471
+
+
+@pytest.mark.timeout(900)
+def test_largest_region_full(capsys):
+    """Two workers on a ring at the largest size a plan admits (J/2 at the
+    limit, 7.97e9 coordinates) and a budget of 8 bits, so that every
+    super-group is 8-bit and each part's region is 4,294,966,012 bytes: code,
+    scale and group-code offsets run past 2^31 to within 1,284 bytes of
+    2^32.  The Large-share recipe; the oracle follows sampled super-groups at
+    the part ends as everywhere else."""
+    assert (MAX_PART_SG + 3) * 276 + 256 < 2 ** 32 <= (MAX_PART_SG + 4) * 276 + 256
+    _run("large", 8.0, capsys, d=256 * 2 * MAX_PART_SG, n=2)
