@@ -332,7 +332,8 @@ def test_device_tables_match_the_definition(eps):
 
 
 @pytest.mark.parametrize("n,topo", [(1, dq.RING), (1, dq.BUTTERFLY), (2, dq.RING), (2, dq.BUTTERFLY),
-                                    (4, dq.BUTTERFLY), (16, dq.BUTTERFLY), (3, dq.RING), (5, dq.RING)])
+                                    (4, dq.BUTTERFLY), (16, dq.BUTTERFLY), (32, dq.BUTTERFLY),
+                                    (64, dq.BUTTERFLY), (3, dq.RING), (5, dq.RING), (13, dq.RING)])
 def test_worker_counts(n, topo):
     _need_gpu()
     grads = _scaled("bert", 733, workers=range(n))
