@@ -716,6 +716,20 @@ dq_status dq_check_reciprocal(uint32_t lo, uint32_t count, unsigned long long *d
     return hip_status(launch_check_recip(lo, count, d_mismatches, static_cast<hipStream_t>(stream)));
 }
 
+dq_status dq_probe_stream(const void *src, size_t src_bytes, void *dst, size_t dst_bytes,
+                          int32_t reads_per_write, void *stream) {
+    if (!src || !dst) return DQ_ENULL;
+    const int32_t R = reads_per_write;
+    if (R != 0 && R != 1 && R != 2 && R != 4 && R != 8) return DQ_EINVAL;
+    const size_t tile = 1024 * (size_t)(R == 0 ? 1 : R);
+    if (src_bytes == 0 || src_bytes % tile != 0 || !aligned(src, 16) || !aligned(dst, 16))
+        return DQ_EINVAL;
+    const size_t need = R == 0 ? (size_t)probe_stream_sink_bytes() : src_bytes / (size_t)R;
+    if (dst_bytes < need) return DQ_EINVAL;
+    return hip_status(launch_probe_stream(src, (int64_t)(src_bytes / tile), R, dst,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 dq_status dq_get_info(dq_plan *p, dq_info *out, void *stream) {
     if (!p || !out) return DQ_ENULL;
     if (!p->ws) return DQ_EWORKSPACE;

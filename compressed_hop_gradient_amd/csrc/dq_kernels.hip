@@ -105,9 +105,9 @@ __device__ __forceinline__ void philox4x32_10(uint32_t &x0, uint32_t &x1, uint32
 }
 
 // Scale unit of a super-group: fl(A/255), raised to the next float while
-// fl(255 s) < A.  One raise always suffices (the first product is within one
-// part in 2^24 of A, and one ulp of s adds 255 ulps to it); the second guard
-// keeps the definition's loop semantics without a loop.
+// fl(255 s) < A.  One raise always suffices: over every non-negative finite
+// fp32 A, fl(255 s) < A after one raise never happens (exhaustive CPU check),
+// so the loop of the definition is a single guarded step.
 __device__ __forceinline__ float scale_unit(float A) {
     // fl(A / 255) by a product and two FMAs: equal to the correctly rounded
     // quotient for every non-negative finite A (exhaustive CPU check)
@@ -115,7 +115,6 @@ __device__ __forceinline__ float scale_unit(float A) {
     const float y = A * R;
     const float rem = __builtin_fmaf(-y, 255.0f, A);
     float s = __builtin_fmaf(rem, R, y);
-    if (255.0f * s < A) s = __uint_as_float(__float_as_uint(s) + 1u);
     if (255.0f * s < A) s = __uint_as_float(__float_as_uint(s) + 1u);
     return s;
 }
@@ -225,6 +224,33 @@ __device__ __forceinline__ float level_of(const SharedTables &T, uint32_t code) 
     else return T.dec8[code];
 }
 
+// x[i] = fl(sigma * L[code i]) for the 16 codes of one group.  2- and 4-bit
+// codes are looked up a byte at a time (four or two levels per LDS read).
+template <int B>
+__device__ __forceinline__ void decode_codes(const uint32_t (&w)[B / 2], float sigma, const SharedTables &T,
+                                             float (&x)[16]) {
+    if constexpr (B == 2) {
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const f32x4_t l = *reinterpret_cast<const f32x4_t *>(T.quad2[(w[0] >> (8 * k)) & 0xFFu]);
+            x[4 * k] = sigma * l.x;
+            x[4 * k + 1] = sigma * l.y;
+            x[4 * k + 2] = sigma * l.z;
+            x[4 * k + 3] = sigma * l.w;
+        }
+    } else if constexpr (B == 4) {
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            const float2 l = *reinterpret_cast<const float2 *>(T.pair4[(w[k >> 2] >> (8 * (k & 3))) & 0xFFu]);
+            x[2 * k] = sigma * l.x;
+            x[2 * k + 1] = sigma * l.y;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; i++) x[i] = sigma * T.dec8[(w[i >> 2] >> (8 * (i & 3))) & 0xFFu];
+    }
+}
+
 // load / store the 2B bytes of one group's codes (B = bits per code)
 template <int B>
 __device__ __forceinline__ void load_codes(const uint8_t *p, uint32_t (&w)[B / 2]) {
@@ -248,6 +274,24 @@ __device__ __forceinline__ void store_codes(uint8_t *p, const uint32_t (&w)[B / 
     } else {
         *reinterpret_cast<uint32_t *>(p) = w[0];
     }
+}
+
+// The stream positions and part-local offsets of a part's classes as 32-bit
+// values (a part holds fewer than 2^31 super-groups), so that a launch keeps
+// a dozen scalar registers of layout instead of the whole 64-bit PartInfo.
+struct PartU32 {
+    uint32_t lo[3];    // first stream position of each class
+    uint32_t pre[3];   // part-local index of each class's first super-group
+};
+
+__device__ __forceinline__ PartU32 part_u32(const PartInfo &P) {
+    PartU32 q;
+#pragma unroll
+    for (int k = 0; k < 3; k++) {
+        q.lo[k] = (uint32_t)P.lo[k];
+        q.pre[k] = (uint32_t)P.pre[k];
+    }
+    return q;
 }
 
 // Region pointers of one part, split by class (uniform over a launch).  Offsets
@@ -276,11 +320,7 @@ __device__ __forceinline__ void decode_group(const RegionBase &R, uint32_t t, ui
     const float s = *reinterpret_cast<const float *>(R.s + 4u * t);
     const uint32_t c = R.g[16u * t + (uint32_t)g];
     const float sigma = (float)c * s;
-#pragma unroll
-    for (int i = 0; i < 16; i++) {
-        const uint32_t code = (w[(i * B) / 32] >> ((i * B) % 32)) & ((1u << B) - 1u);
-        x[i] = sigma * level_of<B>(T, code);
-    }
+    decode_codes<B>(w, sigma, T, x);
 }
 
 // ---------------------------------------------------------------------------
@@ -302,7 +342,7 @@ template <int MODE, int LOCAL>
 constexpr bool codec_ahead() { return LOCAL == kLocalBF16 && MODE == kCompress; }
 
 template <int Q, int MODE, int LOCAL>
-__device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po, const PartInfo &Pi,
+__device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartU32 &Po, const PartU32 &Pi,
                                          const RegionBase &In, const RegionBase &Own,
                                          const RegionBase &Out, uint32_t t, uint32_t j, float mu,
                                          uint32_t pos_next, uint32_t *slot_j, float *slot_mu, int g,
@@ -486,15 +526,15 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartInfo &Po,
 
 // Block layout of each codec kernel, one super-group per 16-lane row.  The
 // kernels with a bf16 local run 256-thread blocks (compress 8 per CU, the hop 7,
-// the fused last hop 5 as its output staging allows); the others 512-thread
-// blocks, 3 per CU.  Measured per kernel: with the packed local the larger
+// the fused last hop 4 as its output staging and the tables allow: 33.5 KB of
+// LDS per block); the others 512-thread blocks, 3 per CU.  Measured per kernel: with the packed local the larger
 // blocks are 4.6% faster, with the bf16 local the smaller ones 1-4%.
 template <int MODE, int LOCAL>
 struct CodecShape {
     static constexpr bool kSmall = LOCAL == kLocalBF16 && MODE != kPartial;
     static constexpr int threads = kSmall ? 256 : 512;
     static constexpr int sg_per_block = threads / 16;
-    static constexpr int blocks_per_cu = kSmall ? (MODE == kCompress ? 8 : (MODE == kHopFinal ? 5 : 7)) : 3;
+    static constexpr int blocks_per_cu = kSmall ? (MODE == kCompress ? 8 : (MODE == kHopFinal ? 4 : 7)) : 3;
     static constexpr int waves_per_simd = blocks_per_cu * threads / 256;   // 4 SIMDs per CU
 };
 
@@ -516,6 +556,7 @@ void k_codec(CodecArgs a) {
     const PartInfo Po = *a.part_out, Pi = *a.part_in;
     const RegionBase In = region_base(a.region_in, Pi), Own = region_base(a.region_own, Pi);
     const RegionBase Out = region_base(a.out, Po);
+    const PartU32 po = part_u32(Po), pi = part_u32(Pi);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane & 15, row = lane >> 4;
@@ -561,9 +602,9 @@ void k_codec(CodecArgs a) {
             mu = *slot_mu;
             if (t + stride < N) pn = pos_of(t + stride);
         }
-        if (t < pre1) codec_sg<2, MODE, LOCAL>(a, Po, Pi, In, Own, Out, t, j, mu, pn, slot_j, slot_mu, g, T, stage_row);
-        else if (t < pre2) codec_sg<4, MODE, LOCAL>(a, Po, Pi, In, Own, Out, t, j, mu, pn, slot_j, slot_mu, g, T, stage_row);
-        else codec_sg<8, MODE, LOCAL>(a, Po, Pi, In, Own, Out, t, j, mu, pn, slot_j, slot_mu, g, T, stage_row);
+        if (t < pre1) codec_sg<2, MODE, LOCAL>(a, po, pi, In, Own, Out, t, j, mu, pn, slot_j, slot_mu, g, T, stage_row);
+        else if (t < pre2) codec_sg<4, MODE, LOCAL>(a, po, pi, In, Own, Out, t, j, mu, pn, slot_j, slot_mu, g, T, stage_row);
+        else codec_sg<8, MODE, LOCAL>(a, po, pi, In, Own, Out, t, j, mu, pn, slot_j, slot_mu, g, T, stage_row);
     }
 }
 
@@ -1252,6 +1293,57 @@ hipError_t launch_mx(const MxArgs &a, int fmt, int local, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// streaming probe: the HBM rate a kernel with a given read:write mix reaches.
+// A wave moves tiles of R x 64 sixteen-byte words: load k of a tile reads
+// words k*64 .. k*64 + 63 (one contiguous kilobyte per instruction), and the
+// xor of the R words a lane read is stored as one 16-byte word of the tile's
+// contiguous kilobyte of output.  R = 0 reads only: every lane folds all it
+// read and stores one word at the end of the grid-stride loop, so no write
+// is interleaved with the read stream.  Plain loads and stores, as in the
+// codec kernels.
+// ---------------------------------------------------------------------------
+
+constexpr int kProbeBlocks = 2048;     // 256 CUs x 8 resident blocks of 256 threads
+
+template <int R>
+__global__ __launch_bounds__(256) void k_probe_stream(const uint4 *src, int64_t tiles, uint4 *dst) {
+    constexpr int kR = R == 0 ? 1 : R;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t waves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    uint4 acc = make_uint4(0u, 0u, 0u, 0u);
+    for (int64_t t = wave; t < tiles; t += waves) {
+        const uint4 *p = src + t * (64 * kR) + lane;
+        uint4 v[kR];
+#pragma unroll
+        for (int k = 0; k < kR; k++) v[k] = p[64 * k];
+        uint4 x = v[0];
+#pragma unroll
+        for (int k = 1; k < kR; k++) x = make_uint4(x.x ^ v[k].x, x.y ^ v[k].y, x.z ^ v[k].z, x.w ^ v[k].w);
+        if constexpr (R == 0) acc = make_uint4(acc.x ^ x.x, acc.y ^ x.y, acc.z ^ x.z, acc.w ^ x.w);
+        else dst[t * 64 + lane] = x;
+    }
+    if constexpr (R == 0) dst[wave * 64 + lane] = acc;
+}
+
+int64_t probe_stream_sink_bytes() { return (int64_t)kProbeBlocks * 256 * 16; }
+
+hipError_t launch_probe_stream(const void *src, int64_t tiles, int reads_per_write, void *dst, hipStream_t s) {
+    const dim3 grid(kProbeBlocks), block(256);
+    const uint4 *in = static_cast<const uint4 *>(src);
+    uint4 *out = static_cast<uint4 *>(dst);
+    switch (reads_per_write) {
+        case 0: hipLaunchKernelGGL(k_probe_stream<0>, grid, block, 0, s, in, tiles, out); break;
+        case 1: hipLaunchKernelGGL(k_probe_stream<1>, grid, block, 0, s, in, tiles, out); break;
+        case 2: hipLaunchKernelGGL(k_probe_stream<2>, grid, block, 0, s, in, tiles, out); break;
+        case 4: hipLaunchKernelGGL(k_probe_stream<4>, grid, block, 0, s, in, tiles, out); break;
+        case 8: hipLaunchKernelGGL(k_probe_stream<8>, grid, block, 0, s, in, tiles, out); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // utility
 // ---------------------------------------------------------------------------
 
@@ -1314,6 +1406,12 @@ __global__ __launch_bounds__(256) void k_build_tables(DeviceTables *t, double ep
     for (int i = threadIdx.x; i < 2 * kKeys; i += blockDim.x) {
         S.b8[i] = t->b8.est[i];
         S.b4[i] = t->b4.est[i];
+    }
+    for (int b = threadIdx.x; b < 256; b += blockDim.x) {
+#pragma unroll
+        for (int k = 0; k < 4; k++) S.quad2[b][k] = v.L2[(b >> (2 * k)) & 3];
+        S.pair4[b][0] = v.L4[b & 15];
+        S.pair4[b][1] = v.L4[b >> 4];
     }
 }
 

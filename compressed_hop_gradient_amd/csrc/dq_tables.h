@@ -145,6 +145,10 @@ constexpr bool buckets_hold_one_boundary(double eps) {
 // levels, (L, W) pairs and bucket entries of each class.  The workspace keeps
 // a byte image of it so that a block loads its copy with 16-byte reads.
 struct alignas(16) SharedTables {
+    // decode of a whole code byte: four 2-bit codes, two 4-bit codes
+    // (code k of the byte sits at bits q k, LSB first)
+    float quad2[256][4];
+    float pair4[256][2];
     float dec2[4];
     Pair lw2[3];
     float dec4[16];

@@ -85,6 +85,8 @@ _SIGS = {
     "dq_mx_allreduce": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
                                   C.c_void_p, C.c_void_p]),
     "dq_check_reciprocal": (C.c_int, [C.c_uint32, C.c_uint32, C.c_void_p, C.c_void_p]),
+    "dq_probe_stream": (C.c_int, [C.c_void_p, C.c_size_t, C.c_void_p, C.c_size_t, C.c_int32,
+                                  C.c_void_p]),
     "dq_get_info": (C.c_int, [C.c_void_p, C.POINTER(dq_info), C.c_void_p]),
     "dq_timing_read": (C.c_int, [C.c_void_p, C.POINTER(dq_timing)]),
     "dq_status_string": (C.c_char_p, [C.c_int32]),
@@ -164,6 +166,17 @@ def check_reciprocal(lo_bits, count, device=None, stream=None):
     _check(lib().dq_check_reciprocal(int(lo_bits), int(count), _ptr(cnt), _stream(stream)),
            "dq_check_reciprocal")
     return int(cnt.item())
+
+
+def probe_stream(src, dst, reads_per_write, stream=None):
+    """Run the streaming probe over the bytes of ``src`` (device tensor) with
+    the given read:write mix, writing into ``dst``."""
+    dev = src.device
+    _tensor(src, "src", dev)
+    _tensor(dst, "dst", dev)
+    _check(lib().dq_probe_stream(_ptr(src), src.numel() * src.element_size(), _ptr(dst),
+                                 dst.numel() * dst.element_size(), int(reads_per_write),
+                                 _stream(stream)), "dq_probe_stream")
 
 
 class Plan:

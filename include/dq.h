@@ -351,6 +351,22 @@ dq_status dq_timing_read(dq_plan *plan, dq_timing *out);
 dq_status dq_check_reciprocal(uint32_t lo_bits, uint32_t count, unsigned long long *d_mismatches,
                               void *stream);
 
+/* Measurement probe: a plain coalesced streaming kernel with a fixed
+ * read:write mix, for the HBM rate such a mix reaches on the device (the
+ * ceiling against which a codec kernel's bandwidth is read; the hop with a
+ * bf16 local reads about four bytes for every one it writes).  It reads all
+ * src_bytes of d_src in tiles of reads_per_write kilobytes and writes, per
+ * tile, one kilobyte to d_dst (the xor of the words read): reads_per_write
+ * = 1 is a copy, 2, 4 or 8 read that many bytes per byte written.
+ * reads_per_write = 0 only reads; each thread then stores one 16-byte word
+ * after its last load (8 MiB in all), so no write interleaves the reads.
+ * src_bytes: a positive multiple of 1024 * max(reads_per_write, 1);
+ * d_dst holds src_bytes / reads_per_write bytes (8 MiB for 0); both 16-byte
+ * aligned device pointers owned by the caller.  Asynchronous on `stream`.
+ * Errors: DQ_ENULL, DQ_EINVAL (mix, sizes, alignment), DQ_EHIP. */
+dq_status dq_probe_stream(const void *d_src, size_t src_bytes, void *d_dst, size_t dst_bytes,
+                          int32_t reads_per_write, void *stream);
+
 const char *dq_status_string(int32_t status);
 int32_t dq_version(void);
 

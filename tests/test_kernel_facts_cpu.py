@@ -92,6 +92,8 @@ def test_scale_unit_division_by_255_with_two_fmas(tmp_path):
         subprocess.run([cc, "-O2", "-ffp-contract=off", "-o", exe, src, "-lm"], check=True)
     ranges = ["0", "254"]
     out = subprocess.run([exe] + ranges, check=True, capture_output=True, text=True).stdout.split()
-    checked, bad = int(out[0]), int(out[1])
+    checked, bad, second = int(out[0]), int(out[1]), int(out[2])
     assert checked == 255 * (1 << 23)
     assert bad == 0
+    # the scale unit's raise loop stops after at most one step
+    assert second == 0
