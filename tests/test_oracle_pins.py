@@ -1078,3 +1078,77 @@ def test_own_fp32_partial_is_the_exact_partial_sum():
         assert np.array_equal(kept[t].view(np.uint32), y.view(np.uint32))
     # and the sent child is a packed region of part (4, 1)
     assert R.region_bytes(C, 4, 1) > 0 and sent[:R.region_bytes(C, 4, 1)].any()
+
+
+# ---------------------------------------------------------------------------
+# MX all-reduce schedule beyond two workers (ring n = 3, 4, 5; butterfly n = 4,
+# 8): exact sums and an independent part-by-part composition
+# (tests/mx_schedule_checks.py), and copies of the oracle with a planted
+# schedule mistake that these checks must catch
+# ---------------------------------------------------------------------------
+
+def test_mx_schedule_exact_sums_and_composition():
+    from tests import mx_schedule_checks as M
+    res = M.run_checks()
+    assert len(res) == 2 * 4 * len(M.CASES)
+    failed = [k for k, ok in res.items() if not ok]
+    assert not failed, failed
+
+
+def test_mx_exact_sum_inputs_are_exact():
+    """The exact-sum inputs really keep every partial sum exact: one
+    quantisation of any partial sum of the workers returns it unchanged."""
+    from tests import mx_schedule_checks as M
+    rng = np.random.default_rng(3)
+    for fmt in (po.MX_E4M3, po.MX_E3M2, po.MX_E2M3, po.MX_E2M1):
+        g, v = M.exact_sum_inputs(fmt, 5, 16, seed=fmt)
+        assert np.array_equal(np.sum(g, axis=0, dtype=np.float32), v)
+        for _ in range(20):
+            sub = rng.random(5) < 0.5
+            part = np.sum([g[w] for w in range(5) if sub[w]] or [np.zeros_like(v)], axis=0, dtype=np.float32)
+            assert np.array_equal(po.mx_roundtrip(fmt, part), part)
+
+
+# each mutation: (what it plants, text in or_mx_allreduce, replacement)
+_MX_MUTATIONS = [
+    ("ring hop reads worker w+1's region",
+     "const int src = (w - 1 + n) % n;", "const int src = (w + 1) % n;"),
+    ("ring hop works on part (w + t) mod n",
+     "mx_part(c, n, ((int64_t)w - t % n + n) % n, &lo, &hi);", "mx_part(c, n, ((int64_t)w + t) % n, &lo, &hi);"),
+    ("butterfly levels >= 2 read another worker's partial than the partner's",
+     "const float in = (s == 1) ? nxt[partner][i] : cur[partner][i];",
+     "const float in = (s == 1) ? nxt[partner][i] : cur[w ^ 1][i];"),
+    ("butterfly level 1 takes the partner's raw gradient",
+     "const float in = (s == 1) ? nxt[partner][i] : cur[partner][i];",
+     "const float in = (s == 1) ? load_elem(grads[partner], dtype, i) : cur[partner][i];"),
+]
+
+
+@pytest.mark.parametrize("what,old,new", _MX_MUTATIONS, ids=[m[0] for m in _MX_MUTATIONS])
+def test_mx_schedule_checks_catch_planted_mistakes(tmp_path, what, old, new):
+    """A copy of the oracle with one schedule mistake planted in its MX
+    all-reduce, built here and run in a child process, fails the checks."""
+    import shutil
+    import subprocess
+    import sys
+    from oracle import build as ob
+    cc = shutil.which("gcc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = open(os.path.join(os.path.dirname(ob.__file__), "oracle.c")).read()
+    start = src.index("int or_mx_allreduce(")
+    end = src.index("int or_mxfp8_allreduce(")
+    body = src[start:end]
+    assert body.count(old) == 1, what
+    mutated = src[:start] + body.replace(old, new) + src[end:]
+    c_path = tmp_path / "oracle_mutant.c"
+    c_path.write_text(mutated)
+    so = tmp_path / "liboracle_mutant.so"
+    subprocess.run([cc] + ob.FLAGS + ["-I", os.path.dirname(ob.__file__), str(c_path), "-o", str(so), "-lm"],
+                   check=True)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, DQ_ORACLE_LIB=str(so), PYTHONPATH=root, OMP_NUM_THREADS="4")
+    out = subprocess.run([sys.executable, "-m", "tests.mx_schedule_checks"], cwd=root, env=env,
+                         check=True, capture_output=True, text=True).stdout
+    r = json.loads(out.strip().splitlines()[-1])
+    assert r["passed"] < r["total"], f"planted mistake not caught: {what}"
