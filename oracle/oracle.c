@@ -283,12 +283,74 @@ int64_t or_count_bits(const or_ctx *c, uint32_t rho_bits) {
     return count_bits_on(c->F, c->J, rho_bits);
 }
 
+/* ------------------------------------------------------------------ */
+/* Exact allocation (pith.science review, referee major 1 and "What would  */
+/* settle it": compare the threshold rule with an exhaustive search over   */
+/* all allocations of the same bit budget).  The error model of "What      */
+/* carries the argument" charges a super-group F_j 4^-q_j; the exact       */
+/* allocation minimises sum_j F_j 4^-q_j over q_j in {2,4,8} subject to    */
+/* sum_j q_j <= budget_bits.  Dynamic programme over super-groups and the  */
+/* bits spent above 2 per super-group, in units of 2 bits (a super-group   */
+/* takes 0, 1 or 3 units), costs in fp64; ties go to fewer units.  Work    */
+/* and memory grow with J times the budget: J is limited to 4096.          */
+/* Returns the minimal cost, or -1 if J is out of range.                   */
+/* ------------------------------------------------------------------ */
+
+double or_alloc_exact(const float *F, int64_t J, int64_t budget_bits, uint8_t *widths) {
+    if (J < 1 || J > 4096 || budget_bits < 2 * J) return -1.0;
+    int64_t U = (budget_bits - 2 * J) / 2;
+    if (U > 3 * J) U = 3 * J;
+    const int units[3] = {0, 1, 3};
+    const double inv4q[3] = {1.0 / 16.0, 1.0 / 256.0, 1.0 / 65536.0};
+    double *best = (double *)malloc((size_t)(U + 1) * sizeof(double));
+    double *next = (double *)malloc((size_t)(U + 1) * sizeof(double));
+    uint8_t *choice = (uint8_t *)malloc((size_t)J * (size_t)(U + 1));
+    /* best[u]: least cost of the super-groups so far spending exactly u units */
+    for (int64_t u = 0; u <= U; u++) best[u] = u == 0 ? 0.0 : INFINITY;
+    for (int64_t j = 0; j < J; j++) {
+        for (int64_t u = 0; u <= U; u++) {
+            double b = INFINITY;
+            uint8_t ch = 0;
+            for (int k = 0; k < 3; k++) {
+                if (units[k] > u) break;
+                const double v = best[u - units[k]] + (double)F[j] * inv4q[k];
+                if (v < b) { b = v; ch = (uint8_t)k; }
+            }
+            next[u] = b;
+            choice[(size_t)j * (size_t)(U + 1) + (size_t)u] = ch;
+        }
+        double *t = best; best = next; next = t;
+    }
+    int64_t us = 0;
+    for (int64_t u = 1; u <= U; u++)
+        if (best[u] < best[us]) us = u;
+    const double cost = best[us];
+    for (int64_t j = J - 1; j >= 0; j--) {
+        const int k = choice[(size_t)j * (size_t)(U + 1) + (size_t)us];
+        widths[j] = (uint8_t)Q_OF_CLASS[k];
+        us -= units[k];
+    }
+    free(best);
+    free(next);
+    free(choice);
+    return cost;
+}
+
 int or_allocate(or_ctx *c) {
     if (c->stats_done != c->n) return -3;
     const float denom = (float)(256 * c->n);
     for (int64_t j = 0; j < c->J; j++) c->mu[j] = c->sum[j] / denom;
     const int64_t budget = or_budget_bits(c);
     c->C[0] = c->C[1] = c->C[2] = 0;
+    if (c->alloc == OR_ALLOC_EXACT) {
+        /* the exact minimiser of the error model under the budget; no scalar */
+        if (or_alloc_exact(c->F, c->J, budget, c->width) < 0.0) return -1;
+        for (int64_t j = 0; j < c->J; j++) c->C[c->width[j] == 2 ? 0 : (c->width[j] == 4 ? 1 : 2)]++;
+        c->rho_bits = 0x7FC00000u;
+        c->allocated = 1;
+        c->reordered = 0;
+        return 0;
+    }
     if (c->alloc == OR_ALLOC_UNIFORM) {
         /* widest q in {2,4,8} with q <= B, i.e. q J <= floor(B J) */
         const int q = c->budget >= 8.0f ? 8 : (c->budget >= 4.0f ? 4 : 2);

@@ -59,7 +59,10 @@ enum { OR_CORRELATED = 0, OR_INDEPENDENT = 1 };
  *   OR_ALLOC_MEAN_CORRECTED thresholds on G_j = max(F_j - fl(256 n) mu_j^2, 0)
  *   OR_ALLOC_UNIFORM        every super-group at the widest q in {2,4,8}
  *                           with q <= B (rho reported as NaN) */
-enum { OR_ALLOC_THRESHOLD = 0, OR_ALLOC_MEAN_CORRECTED = 1, OR_ALLOC_UNIFORM = 2 };
+enum { OR_ALLOC_THRESHOLD = 0, OR_ALLOC_MEAN_CORRECTED = 1, OR_ALLOC_UNIFORM = 2, OR_ALLOC_EXACT = 3 };
+/* OR_ALLOC_EXACT: the minimiser of sum_j F_j 4^-q_j under the same budget
+ * (exhaustive in effect: a dynamic programme; J <= 4096), the comparison the
+ * review's referee asks for; rho is reported as NaN. */
 
 typedef struct or_ctx or_ctx;
 
@@ -104,6 +107,10 @@ void or_get_perm(const or_ctx *c, int32_t *perm, int32_t *inv);
 void or_get_class_counts(const or_ctx *c, int64_t counts[3]);
 int64_t or_budget_bits(const or_ctx *c);
 int64_t or_count_bits(const or_ctx *c, uint32_t rho_bits);
+/* Widths q_j in {2,4,8} minimising sum_j F_j 4^-q_j subject to
+ * sum_j q_j <= budget_bits (J <= 4096, budget_bits >= 2 J); returns that
+ * minimum (fp64), or -1 on bad arguments. */
+double or_alloc_exact(const float *F, int64_t J, int64_t budget_bits, uint8_t *widths);
 /* T12, T24, T48 for the scalar with bit pattern rho_bits. */
 void or_thresholds(uint32_t rho_bits, float out[3]);
 

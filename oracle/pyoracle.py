@@ -13,7 +13,7 @@ from . import build as _build
 RING, BUTTERFLY = 0, 1
 BF16, F32, PACKED, PARTIAL = 0, 1, 2, 3
 CORRELATED, INDEPENDENT = 0, 1
-ALLOC_THRESHOLD, ALLOC_MEAN_CORRECTED, ALLOC_UNIFORM = 0, 1, 2
+ALLOC_THRESHOLD, ALLOC_MEAN_CORRECTED, ALLOC_UNIFORM, ALLOC_EXACT = 0, 1, 2, 3
 OWN_PACKED, OWN_F32 = 0, 1
 Q_OF_CLASS = (2, 4, 8)
 
@@ -56,6 +56,7 @@ def lib():
             "or_budget_bits": (i64, [vp]),
             "or_count_bits": (i64, [vp, u32]),
             "or_thresholds": (None, [u32, vp]),
+            "or_alloc_exact": (f64, [vp, i64, i64, vp]),
             "or_region_bytes": (i64, [vp, i64, i64, vp]),
             "or_compress": (C.c_int, [vp, i32, i32, vp, i32, vp, vp, i64]),
             "or_hop": (C.c_int, [vp, i32, i32, vp, vp, i32, vp, vp, vp, i64]),
@@ -109,6 +110,17 @@ def levels(q, eps=0.5):
     lib().or_levels(int(q), float(eps), _p(L), _p(W))
     Q = 1 << q
     return L[:Q].copy(), W[:Q - 1].copy()
+
+
+def alloc_exact(F, budget_bits):
+    """(widths, cost): the widths in {2,4,8} minimising sum F 4^-q under
+    sum q <= budget_bits, and that minimum."""
+    F = np.ascontiguousarray(F, dtype=np.float32)
+    w = np.zeros(F.size, np.uint8)
+    cost = lib().or_alloc_exact(_p(F), F.size, int(budget_bits), _p(w))
+    if cost < 0:
+        raise ValueError("or_alloc_exact: J out of range or budget below 2 bits")
+    return w, cost
 
 
 def thresholds(rho_bits):

@@ -2,11 +2,19 @@
 benchmark uses (the same library calls on the same buffer sizes).
 
 The oracle computes every statistic, the allocation and the reorder itself from
-a host copy of the inputs, and these are compared over every super-group.  It
-then follows a sample of super-groups (class and part boundaries plus random
-ones) through every compress and hop of the schedule: after each step the
-sampled super-groups' region bytes are compared, and at the end their decoded
-output.  Inputs come from the shared seeded generator (drawn on the GPU).
+a host copy of the inputs, and these are compared over every super-group.
+
+Whole rounds (BERT-, Gemma- and LLaMA-shaped workloads): the oracle then runs
+every compress and hop of the schedule over every super-group, and after each
+step every byte of every region the GPU wrote is compared with the oracle's,
+and at the end every coordinate of the fp32 output.
+
+Sampled rounds (the Large share, whose eight 8.6 GB gradients and 3e10
+coordinates of oracle work per round are too heavy for a test, and the
+largest-region case): the oracle follows a sample of super-groups (class and
+part boundaries plus random ones) through the schedule and their region bytes
+and decoded output are compared.  Inputs come from the shared seeded
+generator (drawn on the GPU).
 """
 import numpy as np
 import pytest
@@ -87,8 +95,24 @@ def _steps(n, topo):
             yield ("hop", None, s)
 
 
-def _run(name, budget, capsys, budgets_stage_only=(), d=None, n=None):
-    """The workload's recipe and schedule; d and n override its size."""
+def _region_diff(got, exp, C, m, c):
+    """Where two region byte arrays first differ: (section, super-group)."""
+    bad = int(np.flatnonzero(got != exp)[0])
+    lay = R.layout([cnt for _, cnt in R.part_ranges(C, m, c)])
+    for k in range(3):
+        a = lay["codes"][k]
+        n_k = R.part_ranges(C, m, c)[k][1]
+        if a <= bad < a + n_k * 32 * R.QS[k]:
+            return f"codes of class {R.QS[k]}, super-group {(bad - a) // (32 * R.QS[k])} of the class"
+    if lay["s"] <= bad < lay["c"]:
+        return f"scale unit of part-local super-group {(bad - lay['s']) // 4}"
+    return f"group codes of part-local super-group {(bad - lay['c']) // 16}"
+
+
+def _run(name, budget, capsys, budgets_stage_only=(), d=None, n=None, whole=False):
+    """The workload's recipe and schedule; d and n override its size.  whole:
+    the oracle runs every super-group and every region byte and output
+    coordinate is compared; otherwise a sample of super-groups."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     wl = synth.WORKLOADS[name]
@@ -133,8 +157,14 @@ def _run(name, budget, capsys, budgets_stage_only=(), d=None, n=None):
     assert np.array_equal(perm_g, perm_o) and np.array_equal(inv_g, inv_o), "reorder"
     assert np.array_equal(_bits(plan.mu_stream().cpu().numpy()), _bits(mu_o[perm_o])), "reorder: mean"
 
-    positions = _sample_positions(C, n, topo, np.random.default_rng(7))
-    say(f"{positions.size} sampled super-groups through the schedule")
+    J = d // 256
+    if whole:
+        positions = None
+        say(f"all {J} super-groups through the schedule")
+    else:
+        positions = _sample_positions(C, n, topo, np.random.default_rng(7))
+        say(f"{positions.size} sampled super-groups through the schedule")
+    region_bytes_checked = 0
     L = max(0, n.bit_length() - 1)
     last = n - 1 if topo == dq.RING else L
     # the schedule's last hops run fused with the finalize of their part, as a
@@ -179,6 +209,15 @@ def _run(name, budget, capsys, budgets_stage_only=(), d=None, n=None):
                 orc.hop(w, step, oi, ol, oout[0], oout[1] if len(oout) > 1 else None, filt=positions)
             torch.cuda.synchronize()
             for (m, c), gb, ob in zip(parts, gout, oout):
+                if whole:
+                    nb = R.region_bytes(C, m, c)
+                    gbb = gb[:nb].cpu().numpy()
+                    if not np.array_equal(gbb, ob[:nb]):
+                        where = _region_diff(gbb, ob[:nb], C, m, c)
+                        raise AssertionError(f"{kind} worker {w} step {step}, part {c} of {m}: {where} differs")
+                    region_bytes_checked += nb
+                    checked += sum(cnt for _, cnt in R.part_ranges(C, m, c))
+                    continue
                 keep_pos, gbytes = _gather(gb, C, m, c, positions)
                 for p, gbb in zip(keep_pos, gbytes):
                     obb = _oracle_bytes(ob, C, m, c, p)
@@ -192,16 +231,27 @@ def _run(name, budget, capsys, budgets_stage_only=(), d=None, n=None):
         orc.finalize(plan.final_part(w), o_prev[w][0], out_o, filt=positions)
     torch.cuda.synchronize()
     assert not torch.isnan(out_g).any(), "the fused last hops left a coordinate unwritten"
-    cols = (perm_o[positions].astype(np.int64)[:, None] * 256 + np.arange(256)[None, :]).ravel()
-    got = out_g[torch.from_numpy(cols).to(DEV)].cpu().numpy()
-    assert np.array_equal(_bits(got), _bits(out_o[cols])), "fused finalize: output"
+    if whole:
+        got = out_g.cpu().numpy()
+        if not np.array_equal(_bits(got), _bits(out_o)):
+            bad = np.flatnonzero(_bits(got) != _bits(out_o))
+            raise AssertionError(f"fused finalize: {bad.size} output coordinates differ, first {bad[0]} "
+                                 f"(super-group {bad[0] // 256})")
+    else:
+        cols = (perm_o[positions].astype(np.int64)[:, None] * 256 + np.arange(256)[None, :]).ravel()
+        got = out_g[torch.from_numpy(cols).to(DEV)].cpu().numpy()
+        assert np.array_equal(_bits(got), _bits(out_o[cols])), "fused finalize: output"
     # the stand-alone finalize of the same final regions gives the same bytes everywhere
     out_f = torch.full((d,), float("nan"), dtype=torch.float32, device=DEV)
     for w in range(n):
         plan.finalize(plan.final_part(w), g_prev[w][0], out_f)
     torch.cuda.synchronize()
     assert torch.equal(out_f.view(torch.int32), out_g.view(torch.int32)), "finalize vs fused last hop"
-    say(f"{checked} sampled region records and {positions.size} output super-groups bit-exact")
+    if whole:
+        say(f"all {region_bytes_checked} region bytes ({checked} super-group records) of every step and "
+            f"all {J} output super-groups ({d} coordinates) bit-exact")
+    else:
+        say(f"{checked} sampled region records and {positions.size} output super-groups bit-exact")
 
     for b in budgets_stage_only:
         p2 = dq.Plan(d, n, topo, b, seed=wl.rounding_seed)
@@ -222,17 +272,17 @@ def _run(name, budget, capsys, budgets_stage_only=(), d=None, n=None):
 
 @pytest.mark.timeout(600)
 def test_bert_full(capsys):
-    _run("bert", 5.0, capsys)
-
-
-@pytest.mark.timeout(600)
-def test_gemma_full(capsys):
-    _run("gemma", 5.0, capsys)
+    _run("bert", 5.0, capsys, whole=True)
 
 
 @pytest.mark.timeout(900)
+def test_gemma_full(capsys):
+    _run("gemma", 5.0, capsys, whole=True)
+
+
+@pytest.mark.timeout(1200)
 def test_llama_full(capsys):
-    _run("llama", 5.0, capsys, budgets_stage_only=(3.0, 4.0, 6.0))
+    _run("llama", 5.0, capsys, budgets_stage_only=(3.0, 4.0, 6.0), whole=True)
 
 
 @pytest.mark.timeout(900)

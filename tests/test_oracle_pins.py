@@ -1152,3 +1152,85 @@ def test_mx_schedule_checks_catch_planted_mistakes(tmp_path, what, old, new):
                          check=True, capture_output=True, text=True).stdout
     r = json.loads(out.strip().splitlines()[-1])
     assert r["passed"] < r["total"], f"planted mistake not caught: {what}"
+
+
+# ---------------------------------------------------------------------------
+# exact allocation under the same budget (pith.science review, referee major
+# 1 and "What would settle it"): the minimiser of sum_j F_j 4^-q_j, against
+# brute force and against the threshold rule
+# ---------------------------------------------------------------------------
+
+def _model_cost(F, q):
+    return float(np.sum(F.astype(np.float64) * 4.0 ** (-q.astype(np.float64))))
+
+
+def test_exact_allocation_brute_force_8_super_groups():
+    """The dynamic programme returns the least cost over all 3^8 width
+    assignments that keep the budget, on skewed random norms and every budget
+    from 2 to 8 bits in steps of 1/8 bit per coordinate."""
+    rng = np.random.default_rng(21)
+    allq = np.array(list(itertools.product((2, 4, 8), repeat=8)), dtype=np.int64)
+    for trial in range(60):
+        F = (10.0 ** rng.uniform(-8, 0, 8) * rng.uniform(0.5, 2, 8)).astype(np.float32)
+        costs = (F.astype(np.float64)[None, :] * 4.0 ** (-allq.astype(np.float64))).sum(1)
+        bits = allq.sum(1)
+        for b8 in range(16, 65, 3 if trial % 2 else 1):
+            budget = b8                     # floor(B * 8) with B = b8 / 8
+            w, cost = po.alloc_exact(F, budget)
+            assert int(w.astype(np.int64).sum()) <= budget
+            assert set(np.unique(w)) <= {2, 4, 8}
+            best = costs[bits <= budget].min()
+            assert abs(cost - best) <= 1e-12 * best
+            assert abs(_model_cost(F, w) - cost) <= 1e-12 * cost
+
+
+def test_exact_allocation_never_worse_than_threshold_rule():
+    """The threshold allocation keeps the budget, so the exact minimum is at
+    most its cost; on skewed inputs the threshold rule already comes within a
+    small fraction of it."""
+    rng = np.random.default_rng(22)
+    worse = 0
+    for trial in range(40):
+        J = 64
+        scale = np.repeat(10.0 ** rng.uniform(-5, -1, J), 256)
+        gs = [(scale * rng.standard_normal(256 * J)).astype(np.float32) for _ in range(4)]
+        for budget in (3.0, 4.0, 5.0, 6.0):
+            o = po.Oracle(256 * J, 4, po.RING, budget)
+            for w in range(4):
+                o.stats(w, gs[w])
+            o.allocate()
+            _, F, _ = o.stats_arrays()
+            q_thr = o.widths().astype(np.int64)
+            w_ex, cost = po.alloc_exact(F, o.budget_bits())
+            c_thr = _model_cost(F, q_thr)
+            assert cost <= c_thr * (1 + 1e-12)
+            if cost < c_thr * (1 - 1e-9):
+                worse += 1
+            assert c_thr <= 1.5 * cost
+    # the discrete 4 -> 8 step leaves the threshold rule short of the optimum
+    # in some instances (its allocation is optimal only for its own bit count)
+    assert worse > 0
+
+
+def test_exact_allocation_special_budgets_and_pipeline():
+    rng = np.random.default_rng(23)
+    F = (10.0 ** rng.uniform(-6, 0, 100)).astype(np.float32)
+    assert np.all(po.alloc_exact(F, 200)[0] == 2)          # 2 bits per super-group
+    assert np.all(po.alloc_exact(F, 800)[0] == 8)          # 8 bits
+    assert np.all(po.alloc_exact(F, 10 ** 6)[0] == 8)      # more than 8 bits
+    with pytest.raises(ValueError):
+        po.alloc_exact(F, 199)                             # below 2 bits per super-group
+    with pytest.raises(ValueError):
+        po.alloc_exact(np.ones(4097, np.float32), 8 * 4097)
+    # the allocation mode runs the whole round: widths as the programme gives
+    # them, no scalar (NaN), and the round is exact on constant super-groups
+    J, n = 32, 4
+    gs = [(np.repeat(10.0 ** rng.uniform(-4, 0, J), 256) * rng.standard_normal(256 * J)).astype(np.float32)
+          for _ in range(n)]
+    o = po.Oracle(256 * J, n, po.RING, 5.0, alloc=po.ALLOC_EXACT)
+    out = o.allreduce(gs)
+    _, F, _ = o.stats_arrays()
+    assert np.array_equal(o.widths(), po.alloc_exact(F, o.budget_bits())[0])
+    assert np.isnan(o.rho())
+    exact = np.sum([g.astype(np.float64) for g in gs], axis=0)
+    assert np.sum((out - exact) ** 2) / np.sum(exact ** 2) < 1e-2
