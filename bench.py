@@ -176,9 +176,22 @@ def cpu_baseline(args, wl_name, budget, device):
     one = {"value": dar_coords_per_round(wl.n, wl.topology, 256 * J1) / dt1, "unit": "coords/s",
            "cores": 1, "sample": f"{J1} super-groups x {wl.n} workers; {dt1:.2f} s"}
     return {"value": dar / dt, "unit": "coords/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"whole round of the {wl_name} workload scaled to {J} super-groups "
                       f"({256 * J} coords x {wl.n} workers), same recipe and schedule; "
                       f"{dt:.2f} s", "seconds": dt, "stages": stages, "single_thread": one}
+
+
+def cpu_model():
+    """The host CPU's model name (what lscpu reports), from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def dar_coords_per_round(n, topology, d):
@@ -314,11 +327,14 @@ def main():
         def vnmse(o):
             return ((o.double() - exact) ** 2).sum().item() / norm
 
-        v_corr = vnmse(out)
-        p_ind = dq.Plan(wl.d, wl.n, topo, budget, seed=wl.rounding_seed, rounding=dq.INDEPENDENT,
-                        device=dev)
-        v_ind = vnmse(p_ind.allreduce(grads, out=torch.empty_like(out), arena=arena))
-        del p_ind
+        # the timed rounds use the default, level-stratified rounding
+        v_strat = vnmse(out)
+        v_mode = {}
+        for mode in (dq.INDEPENDENT, dq.CORRELATED):
+            p_m = dq.Plan(wl.d, wl.n, topo, budget, seed=wl.rounding_seed, rounding=mode, device=dev)
+            v_mode[mode] = vnmse(p_m.allreduce(grads, out=torch.empty_like(out), arena=arena))
+            del p_m
+        v_ind, v_rank = v_mode[dq.INDEPENDENT], v_mode[dq.CORRELATED]
         mx_arena = torch.empty(int(dq.lib().dq_mxfp8_arena_bytes(plan.h)), dtype=torch.uint8, device=dev)
         v_mx = vnmse(plan.mxfp8_allreduce(grads, out=torch.empty_like(out), arena=mx_arena))
         v_mx6a = vnmse(plan.mx_allreduce(dq.MX_FP6_E3M2, grads, out=torch.empty_like(out), arena=mx_arena))
@@ -367,8 +383,9 @@ def main():
         v_var4_s = variant(shuffled, 4.0, dq.ALLOC_THRESHOLD, exact_s) if shuffled else None
         v_uni4_s = variant(shuffled, 4.0, dq.ALLOC_UNIFORM, exact_s) if shuffled else None
         del shuffled, exact_s
-        quality = {"vnmse_correlated": v_corr, "vnmse_independent": v_ind, "vnmse_mxfp8": v_mx,
-                   "mxfp8_over_dynamiq": v_mx / v_corr, "achieved_bits": b,
+        quality = {"vnmse_stratified": v_strat, "vnmse_independent": v_ind,
+                   "vnmse_rank_correlated": v_rank, "vnmse_mxfp8": v_mx,
+                   "mxfp8_over_dynamiq": v_mx / v_strat, "achieved_bits": b,
                    "wire_bits_per_coord": b + 0.625, "mxfp8_wire_bits_per_coord": 8.25,
                    "stats_traffic_ratio": 8.0 / (256 * 2), "class_counts": info["class_counts"],
                    "vnmse_mxfp6_e3m2": v_mx6a, "vnmse_mxfp6_e2m3": v_mx6b, "vnmse_mxfp4_e2m1": v_mx4,
@@ -378,8 +395,11 @@ def main():
                    "vnmse_4bit_variable_shuffled": v_var4_s, "vnmse_4bit_uniform_shuffled": v_uni4_s}
         del exact
 
-    # achievable HBM rate on this machine: a plain 1 GiB device-to-device copy
-    # (read + write), 10 repetitions, HIP events on the current stream
+    # achievable HBM rates on this machine, measured in the same run: a plain
+    # 1 GiB device-to-device copy, and the library's streaming probe over
+    # 4 GiB read-only, as a copy and with the hop's mix (four bytes read per
+    # byte written; the DAR hop with a bf16 local reads 2.73 and writes 0.70
+    # per coordinate); 10 repetitions each, HIP events on the current stream
     src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -391,6 +411,22 @@ def main():
     torch.cuda.synchronize()
     copy_gbs = 2 * (1 << 30) / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
     del src, dst
+    probe = {}
+    psrc = torch.ones(1 << 30, dtype=torch.int32, device=dev)
+    pdst = torch.empty(1 << 30, dtype=torch.int32, device=dev)
+    pbytes = psrc.numel() * 4
+    for name, R in (("read_only", 0), ("copy", 1), ("read4_write1", 4)):
+        dq.probe_stream(psrc, pdst, R)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            dq.probe_stream(psrc, pdst, R)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        probe[name] = (pbytes + (pbytes // R if R else 0)) / (ms * 1e-3) / 1e9
+    del psrc, pdst
+    torch.cuda.empty_cache()
 
     copy_cal = None
     if args.copy_calibration_mib > 0:
@@ -402,6 +438,13 @@ def main():
         torch.cuda.synchronize()
         copy_cal = {"bytes_read": nb, "bytes_written": nb}
         del src, dst
+
+    # which resource the DAR kernel runs closest to: VALU issue (committed
+    # counters of this kernel source and workload) or the HBM rate its
+    # read:write mix reaches (measured above)
+    valu = measured_valu("hop_grad", src_hash, prof_wl)
+    mix_frac = achieved / probe["read4_write1"]
+    limiter = None if valu is None else ("valu_issue" if valu["frac"] > mix_frac else "hbm_mix")
 
     res = {
         "metric": METRIC,
@@ -428,7 +471,11 @@ def main():
                      "bytes_per_coord": bpc, "avg_launch_ms": avg_ms, "launches": hg["launches"],
                      "kernel_source": src_hash,
                      "achievable_copy_GBs": copy_gbs, "frac_of_copy": achieved / copy_gbs,
-                     "valu_issue": measured_valu("hop_grad", src_hash, prof_wl)},
+                     "stream_probe_GBs": probe,
+                     "frac_of_read4_write1": achieved / probe["read4_write1"],
+                     "frac_of_read_only": achieved / probe["read_only"],
+                     "valu_issue": valu,
+                     "limiter": limiter},
         "dar_kernel_coords_per_s": (hg["coords"] / (hg["ms"] * 1e-3)) if hg["ms"] > 0 else None,
         "kernels": kernels,
         "graph_replay_ms_per_step": graph_ms,

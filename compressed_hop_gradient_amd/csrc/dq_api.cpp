@@ -37,7 +37,7 @@ struct dq_plan {
     long long budget_bits = 0;
     uint64_t seed = 1;
     uint32_t round = 0;
-    int32_t rounding = DQ_ROUND_CORRELATED;
+    int32_t rounding = DQ_ROUND_STRATIFIED;
     int32_t alloc = DQ_ALLOC_THRESHOLD;
     int32_t own = DQ_OWN_PACKED;           // butterfly own operand at levels >= 2
     bool timing = false;
@@ -170,11 +170,36 @@ int32_t event_of(const dq_plan *p, int32_t w, int32_t step) {
     return w;
 }
 
-void fill_rng(const dq_plan *p, int32_t w, int32_t step, CodecArgs &a) {
+// Philox tag and 16-bit stagger of the quantisations a launch makes:
+//   correlated:  tag 0 for every event, staggered by the worker's rank of n;
+//   independent: tag 1 + event, no stagger;
+//   stratified:  a fresh tag per schedule level and a stagger among the
+//                workers that quantise the same coordinates at that level --
+//                ring step t: tag 1 + t, no stagger (one worker per part and
+//                step); butterfly compress: tag 1, k = w mod n/2 of n/2;
+//                butterfly hop of level s: tag 1 + s, k = w mod 2^(L-s) of
+//                2^(L-s); n = 1: tag 1.  Stagger floor(k 65536 / P).
+void fill_rng(const dq_plan *p, int32_t w, int32_t step, bool is_compress, CodecArgs &a) {
     a.key0 = (uint32_t)(p->seed & 0xFFFFFFFFu);
     a.key1 = (uint32_t)(p->seed >> 32);
     a.round = p->round;
-    if (p->rounding == DQ_ROUND_CORRELATED) {
+    if (p->rounding == DQ_ROUND_STRATIFIED) {
+        uint32_t P = 1u, k = 0u;
+        if (p->n == 1) {
+            a.tag = 1u;
+        } else if (p->topo == DQ_RING) {
+            a.tag = 1u + (uint32_t)step;
+        } else if (is_compress) {
+            a.tag = 1u;
+            P = (uint32_t)(p->n / 2);
+            k = (uint32_t)w % P;
+        } else {
+            a.tag = 1u + (uint32_t)step;
+            P = 1u << (p->L - step);
+            k = (uint32_t)w % P;
+        }
+        a.stagger = (uint32_t)(((uint64_t)k * 65536u) / P);
+    } else if (p->rounding == DQ_ROUND_CORRELATED) {
         a.tag = 0u;
         a.stagger = (uint32_t)(((uint64_t)w * 65536u) / (uint64_t)p->n);
     } else {
@@ -324,7 +349,8 @@ dq_status dq_plan_set_u64(dq_plan *p, int32_t option, uint64_t v) {
             p->round = (uint32_t)v;
             return DQ_OK;
         case DQ_OPT_ROUNDING:
-            if (v != DQ_ROUND_CORRELATED && v != DQ_ROUND_INDEPENDENT) return DQ_EINVAL;
+            if (v != DQ_ROUND_CORRELATED && v != DQ_ROUND_INDEPENDENT && v != DQ_ROUND_STRATIFIED)
+                return DQ_EINVAL;
             p->rounding = (int32_t)v;
             return DQ_OK;
         case DQ_OPT_TIMING:
@@ -524,7 +550,7 @@ dq_status dq_compress(dq_plan *p, int32_t w, int32_t step, const void *grad, int
     hipStream_t s = static_cast<hipStream_t>(stream);
     CodecArgs a;
     fill_common(p, a);
-    fill_rng(p, w, step, a);
+    fill_rng(p, w, step, true, a);
     a.part_out = a.part_in = part_entry(p, sp.m, sp.part);
     a.grad = grad;
     a.out = static_cast<uint8_t *>(out);
@@ -563,7 +589,7 @@ dq_status hop_impl(dq_plan *p, int32_t w, int32_t step, const void *in, const vo
     hipStream_t s = static_cast<hipStream_t>(stream);
     CodecArgs a;
     fill_common(p, a);
-    fill_rng(p, w, step, a);
+    fill_rng(p, w, step, false, a);
     a.part_in = part_entry(p, sp.m, sp.part);
     a.region_in = static_cast<const uint8_t *>(in);
     if (local_kind == DQ_PACKED) a.region_own = static_cast<const uint8_t *>(local);

@@ -18,7 +18,7 @@ DQ_OK, DQ_EINVAL, DQ_EBUDGET, DQ_ESTATE, DQ_EWORKSPACE, DQ_ENULL, DQ_EHIP, DQ_EN
 RING, BUTTERFLY = 0, 1
 BF16, F32, PACKED, F32_PARTIAL = 0, 1, 2, 3
 OWN_PACKED, OWN_F32 = 0, 1
-CORRELATED, INDEPENDENT = 0, 1
+CORRELATED, INDEPENDENT, STRATIFIED = 0, 1, 2
 OPT_SEED, OPT_ROUND, OPT_ROUNDING, OPT_TIMING, OPT_ALLOC, OPT_TIMING_KINDS, OPT_OWN = 0, 1, 2, 3, 4, 5, 6
 OPT_STREAMS = 7
 ALLOC_THRESHOLD, ALLOC_MEAN_CORRECTED, ALLOC_UNIFORM = 0, 1, 2
@@ -187,7 +187,7 @@ class Plan:
     """
 
     def __init__(self, n_coords, n_workers, topology=RING, avg_bits=5.0, seed=1, rnd=0,
-                 rounding=CORRELATED, device="cuda", timing=False, alloc=ALLOC_THRESHOLD, eps=None,
+                 rounding=STRATIFIED, device="cuda", timing=False, alloc=ALLOC_THRESHOLD, eps=None,
                  own=OWN_PACKED, streams=1):
         self.d = int(n_coords)
         self.n = int(n_workers)

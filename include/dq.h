@@ -90,9 +90,30 @@ typedef enum dq_kind {
  * (b + 0.625)/8.  A variant for measurement, off by default. */
 typedef enum dq_own { DQ_OWN_PACKED = 0, DQ_OWN_F32 = 1 } dq_own;
 
+/* Rounding modes.  The scribe notes ("Key idea and contribution") describe
+ * correlated rounding, randomness shared across workers; the pith.science
+ * review ("Core claim") states that every hop is unbiased.  A quantisation
+ * stays unbiased given its input only if its dither is independent of that
+ * input, i.e. of every earlier rounding the input went through.
+ *   DQ_ROUND_STRATIFIED (default): a fresh uniform per schedule level, shared
+ *     by the workers that quantise the same coordinate at that level (their
+ *     inputs do not depend on each other's roundings) and staggered by their
+ *     index among them: ring step t takes Philox tag 1 + t with no stagger
+ *     (each part is quantised by one worker per step); the butterfly's
+ *     compress takes tag 1 with the n/2 senders of a half at strata
+ *     w mod (n/2); its hop of level s takes tag 1 + s with the 2^(L-s)
+ *     workers on a part at strata w mod 2^(L-s).  Unbiased at every hop.
+ *   DQ_ROUND_CORRELATED: one shared uniform for every quantisation of a
+ *     coordinate (tag 0), staggered by the quantising worker's rank of n;
+ *     later hops reuse randomness their inputs already depend on, so the
+ *     round is biased (kept for measurement).
+ *   DQ_ROUND_INDEPENDENT: a fresh uniform per quantisation event
+ *     (tag 1 + event: the worker on a ring, (level - 1) n + w on a butterfly).
+ * Stratum k of P workers adds floor(k 65536 / P) to the 16-bit dither. */
 typedef enum dq_rounding {
-    DQ_ROUND_CORRELATED = 0,   /* one shared dither per coordinate, staggered by worker rank */
-    DQ_ROUND_INDEPENDENT = 1   /* an independent dither per quantisation event */
+    DQ_ROUND_CORRELATED = 0,
+    DQ_ROUND_INDEPENDENT = 1,
+    DQ_ROUND_STRATIFIED = 2
 } dq_rounding;
 
 /* Allocation variants.  The method thresholds F_j, the squared norm before
@@ -113,7 +134,7 @@ typedef enum dq_alloc {
 typedef enum dq_option {
     DQ_OPT_SEED = 0,       /* 64-bit Philox key (default 1) */
     DQ_OPT_ROUND = 1,      /* round index, 32-bit, part of every Philox counter (default 0) */
-    DQ_OPT_ROUNDING = 2,   /* dq_rounding (default DQ_ROUND_CORRELATED) */
+    DQ_OPT_ROUNDING = 2,   /* dq_rounding (default DQ_ROUND_STRATIFIED) */
     DQ_OPT_TIMING = 3,     /* 1: time every launch with HIP events on its stream */
     DQ_OPT_ALLOC = 4,      /* dq_alloc (default DQ_ALLOC_THRESHOLD); takes effect at the
                               next dq_allocate */

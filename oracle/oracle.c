@@ -148,7 +148,7 @@ or_ctx *or_create(int64_t n_coords, int32_t n_workers, int32_t topology,
     c->budget = avg_bits;
     c->seed = 1;
     c->round = 0;
-    c->rounding = OR_CORRELATED;
+    c->rounding = OR_STRATIFIED;
     c->eps = 0.5;
     build_tables(c);
     c->sum = (float *)calloc((size_t)c->J, sizeof(float));
@@ -606,13 +606,9 @@ static void read_sg(const or_ctx *c, const sg_slot *sl, float *x) {
 /*   independent: tag 1 + event, d = d0.                                   */
 /* ------------------------------------------------------------------ */
 
-void or_dithers(uint64_t seed, uint32_t round, int64_t j, int32_t mode,
-                int32_t worker, int32_t n_workers, int32_t event, uint16_t *d) {
+void or_dithers_tagged(uint64_t seed, uint32_t round, int64_t j, uint32_t tag, uint32_t stagger,
+                       uint16_t *d) {
     uint32_t key[2] = {(uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32)};
-    uint32_t tag = (mode == OR_CORRELATED) ? 0u : (uint32_t)(1 + event);
-    uint32_t stagger = (mode == OR_CORRELATED)
-                           ? (uint32_t)(((uint64_t)worker * 65536u) / (uint64_t)n_workers)
-                           : 0u;
     for (int blk = 0; blk < 32; blk++) {
         uint32_t ctr[4] = {(uint32_t)blk, (uint32_t)j, round, tag};
         uint32_t out[4];
@@ -623,6 +619,62 @@ void or_dithers(uint64_t seed, uint32_t round, int64_t j, int32_t mode,
             uint32_t d0 = (t & 1) ? (word >> 16) : (word & 0xFFFFu);
             d[i] = (uint16_t)((d0 + stagger) & 0xFFFFu);
         }
+    }
+}
+
+void or_dithers(uint64_t seed, uint32_t round, int64_t j, int32_t mode,
+                int32_t worker, int32_t n_workers, int32_t event, uint16_t *d) {
+    uint32_t tag = (mode == OR_CORRELATED) ? 0u : (uint32_t)(1 + event);
+    uint32_t stagger = (mode == OR_CORRELATED)
+                           ? (uint32_t)(((uint64_t)worker * 65536u) / (uint64_t)n_workers)
+                           : 0u;
+    or_dithers_tagged(seed, round, j, tag, stagger, d);
+}
+
+/* Level-stratified dithers (reading of correlated rounding that keeps every  */
+/* hop unbiased; correlated-quantisation reference of the pith.science       */
+/* review, "Circularity"): the workers that quantise the same coordinate in  */
+/* parallel -- whose inputs do not depend on each other's rounding -- share  */
+/* one uniform, staggered by their index among those workers; quantisations */
+/* in series (a compress and the hops that consume it, one level and the    */
+/* next) take fresh uniforms.                                                */
+/*   ring:      the chain of a part is serial: step t takes tag 1 + t, no    */
+/*              stagger (each part's coordinates are quantised by one worker */
+/*              per step);                                                   */
+/*   butterfly: the compress (sending half) takes tag 1 and the n/2 senders  */
+/*              of a half are staggered by w mod (n/2); the hop of level s   */
+/*              takes tag 1 + s and the 2^(L-s) workers on a part are        */
+/*              staggered by w mod 2^(L-s);                                  */
+/*   n = 1:     tag 1, no stagger.                                           */
+/* Stagger for index k of P workers: floor(k 65536 / P).                     */
+static void stratified_params(const or_ctx *c, int32_t w, int32_t step, int is_compress,
+                              uint32_t *tag, uint32_t *stagger) {
+    uint32_t P = 1, k = 0;
+    if (c->n == 1) {
+        *tag = 1u;
+    } else if (c->topo == OR_RING) {
+        *tag = 1u + (uint32_t)step;
+    } else if (is_compress) {
+        *tag = 1u;
+        P = (uint32_t)(c->n / 2);
+        k = (uint32_t)w % P;
+    } else {
+        *tag = 1u + (uint32_t)step;
+        P = 1u << (c->log2n - step);
+        k = (uint32_t)w % P;
+    }
+    *stagger = (uint32_t)(((uint64_t)k * 65536u) / P);
+}
+
+/* dithers of super-group j for the quantisation event (worker, step) */
+static void event_dithers(const or_ctx *c, int64_t j, int32_t worker, int32_t step, int is_compress,
+                          int32_t event, uint16_t *d) {
+    if (c->rounding == OR_STRATIFIED) {
+        uint32_t tag, stagger;
+        stratified_params(c, worker, step, is_compress, &tag, &stagger);
+        or_dithers_tagged(c->seed, c->round, j, tag, stagger, d);
+    } else {
+        or_dithers(c->seed, c->round, j, c->rounding, worker, c->n, event, d);
     }
 }
 
@@ -728,7 +780,7 @@ int or_compress(or_ctx *c, int32_t worker, int32_t step, const void *grad,
         float y[OR_SG];
         for (int i = 0; i < OR_SG; i++) y[i] = load_elem(grad, dtype, j * OR_SG + i) - mu;
         uint16_t d[OR_SG];
-        or_dithers(c->seed, c->round, j, c->rounding, worker, c->n, event, d);
+        event_dithers(c, j, worker, step, 1, event, d);
         uint8_t codes[OR_SG], cg[16];
         float s;
         encode_sg(y, Q_OF_CLASS[k], c->L[k], c->W[k], d, codes, &s, cg);
@@ -800,7 +852,7 @@ int or_hop(or_ctx *c, int32_t worker, int32_t step, const uint8_t *region_in,
             continue;
         }
         uint16_t d[OR_SG];
-        or_dithers(c->seed, c->round, j, c->rounding, worker, c->n, event, d);
+        event_dithers(c, j, worker, step, 0, event, d);
         uint8_t codes[OR_SG], cg[16];
         float s;
         encode_sg(y, Q_OF_CLASS[k], c->L[k], c->W[k], d, codes, &s, cg);

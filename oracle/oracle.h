@@ -51,7 +51,17 @@ enum { OR_BF16 = 0, OR_F32 = 1, OR_PACKED = 2, OR_PARTIAL = 3 };
  *   OR_OWN_PACKED  the kept child is a packed region, local kind OR_PACKED
  *   OR_OWN_F32     the kept child is fp32, local kind OR_PARTIAL */
 enum { OR_OWN_PACKED = 0, OR_OWN_F32 = 1 };
-enum { OR_CORRELATED = 0, OR_INDEPENDENT = 1 };
+/* Rounding modes (scribe notes, "Key idea and contribution": correlated
+ * rounding, shared randomness across workers; pith.science review, "Core
+ * claim": unbiased at each hop):
+ *   OR_CORRELATED   one shared uniform per coordinate for every quantisation
+ *                   of every worker, staggered by the quantising worker's
+ *                   rank (biased along serial hops)
+ *   OR_INDEPENDENT  a fresh uniform per quantisation event
+ *   OR_STRATIFIED   a fresh uniform per level (serial events independent, so
+ *                   every hop is unbiased), shared and staggered among the
+ *                   workers that quantise a coordinate in parallel */
+enum { OR_CORRELATED = 0, OR_INDEPENDENT = 1, OR_STRATIFIED = 2 };
 /* Allocation variants (pith.science review, referee major 1: the thresholds
  * see F_j although the quantised values have squared norm F_j - n S mu_j^2,
  * and Table 6 compares variable with uniform widths):
@@ -147,8 +157,12 @@ void or_roundtrip_sg(const float *y, int32_t q, const uint16_t *dither,
 /* Batch: K rows of y and dithers -> K rows of decoded values. */
 void or_roundtrip_batch(const float *y, int64_t K, int32_t q,
                         const uint16_t *dither, double eps, float *decoded);
+/* The 256 dithers of super-group j for Philox counter tag `tag`, each
+ * raised by `stagger` modulo 65536. */
+void or_dithers_tagged(uint64_t seed, uint32_t round, int64_t j, uint32_t tag, uint32_t stagger,
+                       uint16_t *d);
 /* The 256 dithers the oracle uses for super-group j in one quantisation
- * event (mode, worker rank, event index). */
+ * event (mode OR_CORRELATED or OR_INDEPENDENT, worker rank, event index). */
 void or_dithers(uint64_t seed, uint32_t round, int64_t j, int32_t mode,
                 int32_t worker, int32_t n_workers, int32_t event,
                 uint16_t *d);

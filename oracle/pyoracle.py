@@ -12,7 +12,7 @@ from . import build as _build
 
 RING, BUTTERFLY = 0, 1
 BF16, F32, PACKED, PARTIAL = 0, 1, 2, 3
-CORRELATED, INDEPENDENT = 0, 1
+CORRELATED, INDEPENDENT, STRATIFIED = 0, 1, 2
 ALLOC_THRESHOLD, ALLOC_MEAN_CORRECTED, ALLOC_UNIFORM, ALLOC_EXACT = 0, 1, 2, 3
 OWN_PACKED, OWN_F32 = 0, 1
 Q_OF_CLASS = (2, 4, 8)
@@ -66,6 +66,7 @@ def lib():
             "or_roundtrip_sg": (None, [vp, i32, vp, f64, vp, vp, vp, vp]),
             "or_roundtrip_batch": (None, [vp, i64, i32, vp, f64, vp]),
             "or_dithers": (None, [u64, u32, i64, i32, i32, i32, i32, vp]),
+            "or_dithers_tagged": (None, [u64, u32, i64, u32, u32, vp]),
             "or_mxfp8_roundtrip": (None, [vp, i64, vp]),
             "or_mx_roundtrip": (None, [i32, vp, i64, vp]),
             "or_mx_allreduce": (C.c_int, [vp, i32, vp, i32, vp]),
@@ -135,6 +136,12 @@ def dithers(seed, rnd, j, mode, worker, n, event):
     return d
 
 
+def dithers_tagged(seed, rnd, j, tag, stagger):
+    d = np.zeros(256, np.uint16)
+    lib().or_dithers_tagged(int(seed), int(rnd), int(j), int(tag), int(stagger), _p(d))
+    return d
+
+
 def roundtrip_sg(y, q, dither, eps=0.5):
     y = np.ascontiguousarray(y, dtype=np.float32)
     d = np.ascontiguousarray(dither, dtype=np.uint16)
@@ -184,7 +191,7 @@ class Oracle:
     """One simulated round on the CPU (mirrors the stage order of the library)."""
 
     def __init__(self, n_coords, n_workers, topology=RING, avg_bits=5.0, seed=1, rnd=0,
-                 rounding=CORRELATED, eps=None, alloc=ALLOC_THRESHOLD, own=OWN_PACKED):
+                 rounding=STRATIFIED, eps=None, alloc=ALLOC_THRESHOLD, own=OWN_PACKED):
         self.d = int(n_coords)
         self.n = int(n_workers)
         self.topology = int(topology)

@@ -72,7 +72,9 @@ def test_options(lib):
     rc, h = _create(lib)
     assert lib.dq_plan_set_u64(h, dq.OPT_SEED, 2 ** 64 - 1) == dq.DQ_OK
     assert lib.dq_plan_set_u64(h, dq.OPT_ROUND, 2 ** 32) == dq.DQ_EINVAL
-    assert lib.dq_plan_set_u64(h, dq.OPT_ROUNDING, 2) == dq.DQ_EINVAL
+    for mode in (dq.CORRELATED, dq.INDEPENDENT, dq.STRATIFIED):
+        assert lib.dq_plan_set_u64(h, dq.OPT_ROUNDING, mode) == dq.DQ_OK
+    assert lib.dq_plan_set_u64(h, dq.OPT_ROUNDING, 3) == dq.DQ_EINVAL
     assert lib.dq_plan_set_u64(h, dq.OPT_TIMING, 3) == dq.DQ_EINVAL
     for mode in (dq.ALLOC_THRESHOLD, dq.ALLOC_MEAN_CORRECTED, dq.ALLOC_UNIFORM):
         assert lib.dq_plan_set_u64(h, dq.OPT_ALLOC, mode) == dq.DQ_OK

@@ -75,7 +75,7 @@ class Round:
     """Drives the same schedule on the GPU and on the oracle, keeping every
     region both produce (fresh zeroed buffers per step)."""
 
-    def __init__(self, grads, topo, budget=5.0, seed=1, rnd=0, rounding=dq.CORRELATED,
+    def __init__(self, grads, topo, budget=5.0, seed=1, rnd=0, rounding=dq.STRATIFIED,
                  alloc=dq.ALLOC_THRESHOLD, eps=None):
         self.grads = grads
         self.gnp = _grads_np(grads)
@@ -340,10 +340,13 @@ def test_worker_counts(n, topo):
     full_round(grads, topo)
 
 
+@pytest.mark.parametrize("mode", [dq.INDEPENDENT, dq.CORRELATED], ids=["independent", "rank-correlated"])
 @pytest.mark.parametrize("topo", [dq.RING, dq.BUTTERFLY])
-def test_independent_rounding_bit_exact(topo):
+def test_rounding_modes_bit_exact(topo, mode):
+    """The non-default rounding modes (the default, level-stratified, runs in
+    every other test)."""
     _need_gpu()
-    full_round(_scaled("gemma", 1031), topo, rounding=dq.INDEPENDENT, seed=2 ** 40 + 17, rnd=9)
+    full_round(_scaled("gemma", 1031), topo, rounding=mode, seed=2 ** 40 + 17, rnd=9)
 
 
 @pytest.mark.parametrize("J,n,topo", [(1, 8, dq.RING), (3, 8, dq.BUTTERFLY), (7, 4, dq.RING),
@@ -438,8 +441,8 @@ def test_timing_counts_coordinates():
 # butterfly variant: the kept child stays fp32 (DQ_OWN_F32)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("n,rounding", [(2, dq.CORRELATED), (4, dq.INDEPENDENT), (8, dq.CORRELATED),
-                                        (16, dq.INDEPENDENT)])
+@pytest.mark.parametrize("n,rounding", [(2, dq.STRATIFIED), (4, dq.INDEPENDENT), (8, dq.STRATIFIED),
+                                        (16, dq.CORRELATED)])
 def test_own_fp32_round_bit_exact(n, rounding):
     _need_gpu()
     J = 777
