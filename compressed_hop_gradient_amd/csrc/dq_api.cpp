@@ -733,6 +733,28 @@ dq_status dq_allreduce(dq_plan *p, const void *const *grads, int32_t kind, void 
     return DQ_OK;
 }
 
+size_t dq_noalloc_max_bytes(void) { return kScratchBytes; }
+
+dq_status dq_allreduce_noalloc(dq_plan *p, const void *const *grads, int32_t kind, float *out,
+                               void *stream) {
+    if (!p || !grads || !out) return DQ_ENULL;
+    const size_t ws = align_up(p->lay.total, kAlign);
+    const size_t arena = arena_plan(p).total;
+    if (ws + arena > kScratchBytes) return DQ_EWORKSPACE;
+    void *base = nullptr;
+    if (scratch_address(&base) != hipSuccess || !base) return DQ_EHIP;
+    // the plan's state moves into the scratch (a bind: tables are rebuilt by
+    // this round's first dq_stats, every stage clears what it accumulates);
+    // launch timing would create events, so it is off for this call
+    dq_status st = dq_plan_bind(p, base, ws);
+    if (st != DQ_OK) return st;
+    const bool timing = p->timing;
+    p->timing = false;
+    st = dq_allreduce(p, grads, kind, static_cast<uint8_t *>(base) + ws, arena, out, stream);
+    p->timing = timing;
+    return st;
+}
+
 // ---- inspection --------------------------------------------------------------
 
 dq_status dq_check_reciprocal(uint32_t lo, uint32_t count, unsigned long long *d_mismatches, void *stream) {

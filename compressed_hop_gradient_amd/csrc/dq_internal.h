@@ -141,6 +141,11 @@ hipError_t launch_part_table(const unsigned long long *class_counts, int32_t n, 
                              PartInfo *table, hipStream_t s);
 hipError_t launch_mx(const MxArgs &a, int fmt, int local, hipStream_t s);
 hipError_t launch_check_recip(uint32_t lo, uint32_t n, unsigned long long *count, hipStream_t s);
+// static device scratch (dq_allreduce_noalloc): its device address on the
+// current device (looked up once per device)
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kScratchDevices = 64;
+hipError_t scratch_address(void **ptr);
 // streaming probe: `tiles` tiles of reads_per_write x 1 KB read (0: read only)
 hipError_t launch_probe_stream(const void *src, int64_t tiles, int reads_per_write, void *dst, hipStream_t s);
 int64_t probe_stream_sink_bytes();

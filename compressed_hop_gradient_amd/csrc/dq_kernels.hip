@@ -1427,6 +1427,33 @@ __global__ void k_zero_u32(uint32_t *p, int64_t n) {
 }
 
 // ---------------------------------------------------------------------------
+// static scratch for callers that cannot allocate (dq_allreduce_noalloc): the
+// plan workspace and the region arena of one round, in a device array every
+// GPU the library runs on holds until the process ends.  Host code uses the
+// array only through the device address hipGetSymbolAddress returns, taken
+// once per device with that device current.
+// ---------------------------------------------------------------------------
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_address(void **ptr) {
+    static void *addr[kScratchDevices];
+    *ptr = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    if (!addr[dev]) {
+        void *a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = a;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 

@@ -74,6 +74,8 @@ _SIGS = {
     "dq_arena_bytes": (C.c_size_t, [C.c_void_p]),
     "dq_allreduce": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
                                C.c_void_p, C.c_void_p]),
+    "dq_noalloc_max_bytes": (C.c_size_t, []),
+    "dq_allreduce_noalloc": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p]),
     "dq_mxfp8_arena_bytes": (C.c_size_t, [C.c_void_p]),
     "dq_mxfp8_allreduce": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
                                      C.c_void_p, C.c_void_p]),
@@ -352,6 +354,16 @@ class Plan:
         kind, out, arena, nbytes, ptrs = self._round_buffers(grads, out, arena, self.arena_bytes())
         _check(lib().dq_allreduce(self.h, ptrs, kind, _ptr(arena), nbytes, _ptr(out),
                                   _stream(stream)), "dq_allreduce")
+        return out
+
+    def allreduce_noalloc(self, grads, out, stream=None):
+        """dq_allreduce_noalloc: the round in the library's static scratch
+        (binds the plan there)."""
+        kind = self._check_grads(grads)
+        _tensor(out, "out", self.device, min_bytes=4 * self.d, dtype=torch.float32)
+        ptrs = (C.c_void_p * self.n)(*[g.data_ptr() for g in grads])
+        _check(lib().dq_allreduce_noalloc(self.h, ptrs, kind, _ptr(out), _stream(stream)),
+               "dq_allreduce_noalloc")
         return out
 
     def mxfp8_allreduce(self, grads, out=None, arena=None, stream=None):

@@ -322,6 +322,24 @@ size_t dq_arena_bytes(const dq_plan *plan);
 dq_status dq_allreduce(dq_plan *plan, const void *const *h_grads, int32_t kind,
                        void *d_arena, size_t arena_bytes, float *d_out, void *stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: dq_allreduce
+ * with the plan workspace and the region arena taken from a static device
+ * array of the library (dq_noalloc_max_bytes() = 64 MiB per GPU, held by
+ * every GPU the library runs on until the process ends) instead of caller
+ * buffers.  The caller passes the gradients (h_grads: a HOST array of n
+ * device pointers) and d_out (float[n_coords]) as for dq_allreduce.  The
+ * plan is bound to that array by the call (as dq_plan_bind does: its state,
+ * e.g. for dq_get_info, lives there until the next bind) and launch timing
+ * is off during the call.  Every call on one GPU uses the same array, which
+ * keeps the last round's contents; calls that overlap on one GPU (another
+ * stream, another thread, another plan) race.  Nothing is allocated.
+ * Errors: as dq_allreduce; DQ_EWORKSPACE when dq_workspace_bytes plus
+ * dq_arena_bytes (each 256-byte aligned) exceed dq_noalloc_max_bytes(). */
+size_t dq_noalloc_max_bytes(void);
+dq_status dq_allreduce_noalloc(dq_plan *plan, const void *const *h_grads, int32_t kind, float *d_out,
+                               void *stream);
+
 /* The same schedule with the MXFP8 reference codec (OCP MX v1.0: 32-element
  * blocks, E8M0 scale, E4M3 elements) on parts of the ORIGINAL order
  * (part c of m = super-groups [floor(cJ/m), floor((c+1)J/m))), re-encoded
