@@ -114,21 +114,40 @@ struct or_ctx {
     int32_t alloc;
     int32_t own;
     double eps;
-    float L[3][256];
-    float W[3][256];
+    int32_t qmax;             /* widest class: 8, or 16 with the 16-bit class */
+    int32_t ncls;             /* 3 classes (2, 4, 8) or 4 (2, 4, 8, 16) */
+    float Lb[3][256], Wb[3][256];
+    float *L16, *W16;         /* 65536 levels of the 16-bit class (qmax 16) */
+    const float *L[4], *W[4]; /* level and weight tables of each class */
     float *sum, *F, *mu;      /* J, original order */
     int32_t stats_done;
     int allocated, reordered;
     uint32_t rho_bits;
     uint8_t *width;           /* J */
     int32_t *perm, *inv;      /* J */
-    int64_t C[3];             /* class counts (q = 2, 4, 8) */
+    int64_t C[4];             /* class counts (q = 2, 4, 8, 16) */
 };
 
-static const int Q_OF_CLASS[3] = {2, 4, 8};
+static const int Q_OF_CLASS[4] = {2, 4, 8, 16};
+
+static int class_of_width(int q) { return q == 2 ? 0 : (q == 4 ? 1 : (q == 8 ? 2 : 3)); }
 
 static void build_tables(or_ctx *c) {
-    for (int k = 0; k < 3; k++) or_levels(Q_OF_CLASS[k], c->eps, c->L[k], c->W[k]);
+    for (int k = 0; k < 3; k++) {
+        or_levels(Q_OF_CLASS[k], c->eps, c->Lb[k], c->Wb[k]);
+        c->L[k] = c->Lb[k];
+        c->W[k] = c->Wb[k];
+    }
+    c->L[3] = c->W[3] = NULL;
+    if (c->qmax == 16) {
+        if (!c->L16) {
+            c->L16 = (float *)malloc(65536 * sizeof(float));
+            c->W16 = (float *)malloc(65536 * sizeof(float));
+        }
+        or_levels(16, c->eps, c->L16, c->W16);
+        c->L[3] = c->L16;
+        c->W[3] = c->W16;
+    }
 }
 
 or_ctx *or_create(int64_t n_coords, int32_t n_workers, int32_t topology,
@@ -150,6 +169,8 @@ or_ctx *or_create(int64_t n_coords, int32_t n_workers, int32_t topology,
     c->round = 0;
     c->rounding = OR_STRATIFIED;
     c->eps = 0.5;
+    c->qmax = 8;
+    c->ncls = 3;
     build_tables(c);
     c->sum = (float *)calloc((size_t)c->J, sizeof(float));
     c->F = (float *)calloc((size_t)c->J, sizeof(float));
@@ -164,6 +185,7 @@ void or_destroy(or_ctx *c) {
     if (!c) return;
     free(c->sum); free(c->F); free(c->mu);
     free(c->width); free(c->perm); free(c->inv);
+    free(c->L16); free(c->W16);
     free(c);
 }
 
@@ -179,6 +201,16 @@ void or_set_alloc(or_ctx *c, int32_t mode) {
 }
 
 void or_set_eps(or_ctx *c, double eps) { c->eps = eps; build_tables(c); }
+
+int or_set_max_width(or_ctx *c, int32_t q) {
+    if (q != 8 && q != 16) return -1;
+    c->qmax = q;
+    c->ncls = q == 16 ? 4 : 3;
+    build_tables(c);
+    c->allocated = 0;
+    c->reordered = 0;
+    return 0;
+}
 
 /* ------------------------------------------------------------------ */
 /* Stage 1: statistics (scribe notes, "Key idea and contribution": per    */
@@ -232,16 +264,42 @@ int or_stats(or_ctx *c, int32_t worker, const void *grad, int32_t dtype) {
 /* ------------------------------------------------------------------ */
 
 int64_t or_budget_bits(const or_ctx *c) {
-    /* sum_j q_j never exceeds 8 J, so every budget of 8 bits or more is the */
-    /* same constraint; capping it keeps the product finite (B may be +inf) */
-    const double b = c->budget < 8.0f ? (double)c->budget : 8.0;
+    /* sum_j q_j never exceeds qmax J, so every budget of qmax bits or more */
+    /* is the same constraint; capping it keeps the product finite (B may be */
+    /* +inf) */
+    const double cap = (double)c->qmax;
+    const double b = (double)c->budget < cap ? (double)c->budget : cap;
     return (int64_t)floor(b * (double)c->J);
 }
 
-static int width_of(float F, float t4, float t8) {
+/* Threshold multipliers: T = fl(K rho).  Widths {2,4,8}: K12, K24, K48 =
+ * 85, 544, 16384 (ratios 5/32 and 17/512).  With the 16-bit class the chain
+ * continues with T48 / T816 = 257 / 2^17 (Fig. 3 caption); all four are
+ * scaled by 257 so that they stay integers exact in fp32: 21845, 139808,
+ * 4210688, 2^31. */
+static void multipliers(int qmax, float K[4]) {
+    if (qmax == 16) {
+        K[0] = 21845.0f; K[1] = 139808.0f; K[2] = 4210688.0f; K[3] = 2147483648.0f;
+    } else {
+        K[0] = 85.0f; K[1] = 544.0f; K[2] = 16384.0f; K[3] = INFINITY;
+    }
+}
+
+static int width_of(float F, float t4, float t8, float t16) {
+    if (F >= t16) return 16;
     if (F >= t8) return 8;
     if (F >= t4) return 4;
     return 2;
+}
+
+/* the thresholds T24, T48 and T816 (+inf without the 16-bit class) of rho */
+static void thresholds_of(int qmax, uint32_t rho_bits, float *t4, float *t8, float *t16) {
+    float K[4];
+    multipliers(qmax, K);
+    const float rho = f_from_bits(rho_bits);
+    *t4 = K[1] * rho;
+    *t8 = K[2] * rho;
+    *t16 = qmax == 16 ? K[3] * rho : INFINITY;
 }
 
 void or_thresholds(uint32_t rho_bits, float out[3]) {
@@ -270,17 +328,24 @@ void or_get_alloc_key(const or_ctx *c, float *out) {
     else memcpy(out, c->F, (size_t)c->J * sizeof(float));
 }
 
-static int64_t count_bits_on(const float *key, int64_t J, uint32_t rho_bits) {
-    float rho = f_from_bits(rho_bits);
-    float t4 = 544.0f * rho, t8 = 16384.0f * rho;
+static int64_t count_bits_on(const float *key, int64_t J, int qmax, uint32_t rho_bits) {
+    float t4, t8, t16;
+    thresholds_of(qmax, rho_bits, &t4, &t8, &t16);
     int64_t total = 0;
 #pragma omp parallel for reduction(+ : total) schedule(static)
-    for (int64_t j = 0; j < J; j++) total += width_of(key[j], t4, t8);
+    for (int64_t j = 0; j < J; j++) total += width_of(key[j], t4, t8, t16);
     return total;
 }
 
 int64_t or_count_bits(const or_ctx *c, uint32_t rho_bits) {
-    return count_bits_on(c->F, c->J, rho_bits);
+    return count_bits_on(c->F, c->J, c->qmax, rho_bits);
+}
+
+void or_thresholds_wide(uint32_t rho_bits, float out[4]) {
+    float K[4];
+    multipliers(16, K);
+    const float rho = f_from_bits(rho_bits);
+    for (int k = 0; k < 4; k++) out[k] = K[k] * rho;
 }
 
 /* ------------------------------------------------------------------ */
@@ -296,12 +361,13 @@ int64_t or_count_bits(const or_ctx *c, uint32_t rho_bits) {
 /* Returns the minimal cost, or -1 if J is out of range.                   */
 /* ------------------------------------------------------------------ */
 
-double or_alloc_exact(const float *F, int64_t J, int64_t budget_bits, uint8_t *widths) {
-    if (J < 1 || J > 4096 || budget_bits < 2 * J) return -1.0;
+double or_alloc_exact_q(const float *F, int64_t J, int64_t budget_bits, int32_t qmax, uint8_t *widths) {
+    if (J < 1 || J > 4096 || budget_bits < 2 * J || (qmax != 8 && qmax != 16)) return -1.0;
+    const int ncls = qmax == 16 ? 4 : 3;
+    const int units[4] = {0, 1, 3, 7};
+    const double inv4q[4] = {1.0 / 16.0, 1.0 / 256.0, 1.0 / 65536.0, 1.0 / 4294967296.0};
     int64_t U = (budget_bits - 2 * J) / 2;
-    if (U > 3 * J) U = 3 * J;
-    const int units[3] = {0, 1, 3};
-    const double inv4q[3] = {1.0 / 16.0, 1.0 / 256.0, 1.0 / 65536.0};
+    if (U > (int64_t)units[ncls - 1] * J) U = (int64_t)units[ncls - 1] * J;
     double *best = (double *)malloc((size_t)(U + 1) * sizeof(double));
     double *next = (double *)malloc((size_t)(U + 1) * sizeof(double));
     uint8_t *choice = (uint8_t *)malloc((size_t)J * (size_t)(U + 1));
@@ -311,7 +377,7 @@ double or_alloc_exact(const float *F, int64_t J, int64_t budget_bits, uint8_t *w
         for (int64_t u = 0; u <= U; u++) {
             double b = INFINITY;
             uint8_t ch = 0;
-            for (int k = 0; k < 3; k++) {
+            for (int k = 0; k < ncls; k++) {
                 if (units[k] > u) break;
                 const double v = best[u - units[k]] + (double)F[j] * inv4q[k];
                 if (v < b) { b = v; ch = (uint8_t)k; }
@@ -336,26 +402,31 @@ double or_alloc_exact(const float *F, int64_t J, int64_t budget_bits, uint8_t *w
     return cost;
 }
 
+double or_alloc_exact(const float *F, int64_t J, int64_t budget_bits, uint8_t *widths) {
+    return or_alloc_exact_q(F, J, budget_bits, 8, widths);
+}
+
 int or_allocate(or_ctx *c) {
     if (c->stats_done != c->n) return -3;
     const float denom = (float)(256 * c->n);
     for (int64_t j = 0; j < c->J; j++) c->mu[j] = c->sum[j] / denom;
     const int64_t budget = or_budget_bits(c);
-    c->C[0] = c->C[1] = c->C[2] = 0;
+    c->C[0] = c->C[1] = c->C[2] = c->C[3] = 0;
     if (c->alloc == OR_ALLOC_EXACT) {
         /* the exact minimiser of the error model under the budget; no scalar */
-        if (or_alloc_exact(c->F, c->J, budget, c->width) < 0.0) return -1;
-        for (int64_t j = 0; j < c->J; j++) c->C[c->width[j] == 2 ? 0 : (c->width[j] == 4 ? 1 : 2)]++;
+        if (or_alloc_exact_q(c->F, c->J, budget, c->qmax, c->width) < 0.0) return -1;
+        for (int64_t j = 0; j < c->J; j++) c->C[class_of_width(c->width[j])]++;
         c->rho_bits = 0x7FC00000u;
         c->allocated = 1;
         c->reordered = 0;
         return 0;
     }
     if (c->alloc == OR_ALLOC_UNIFORM) {
-        /* widest q in {2,4,8} with q <= B, i.e. q J <= floor(B J) */
-        const int q = c->budget >= 8.0f ? 8 : (c->budget >= 4.0f ? 4 : 2);
+        /* widest q of the width set with q <= B, i.e. q J <= floor(B J) */
+        const int q = (c->qmax == 16 && c->budget >= 16.0f) ? 16
+                      : (c->budget >= 8.0f ? 8 : (c->budget >= 4.0f ? 4 : 2));
         for (int64_t j = 0; j < c->J; j++) c->width[j] = (uint8_t)q;
-        c->C[q == 2 ? 0 : (q == 4 ? 1 : 2)] = c->J;
+        c->C[class_of_width(q)] = c->J;
         c->rho_bits = 0x7FC00000u;
         c->allocated = 1;
         c->reordered = 0;
@@ -369,23 +440,23 @@ int or_allocate(or_ctx *c) {
         key = G;
     }
     uint32_t rho;
-    if (count_bits_on(key, c->J, 0u) <= budget) {
+    if (count_bits_on(key, c->J, c->qmax, 0u) <= budget) {
         rho = 0u;
     } else {
         uint32_t lo = 0u, hi = 0x7F800000u; /* +inf: every width is 2 */
         while (hi - lo > 1u) {
             uint32_t mid = lo + (hi - lo) / 2u;
-            if (count_bits_on(key, c->J, mid) <= budget) hi = mid; else lo = mid;
+            if (count_bits_on(key, c->J, c->qmax, mid) <= budget) hi = mid; else lo = mid;
         }
         rho = hi;
     }
     c->rho_bits = rho;
-    float r = f_from_bits(rho);
-    float t4 = 544.0f * r, t8 = 16384.0f * r;
+    float t4, t8, t16;
+    thresholds_of(c->qmax, rho, &t4, &t8, &t16);
     for (int64_t j = 0; j < c->J; j++) {
-        int q = width_of(key[j], t4, t8);
+        int q = width_of(key[j], t4, t8, t16);
         c->width[j] = (uint8_t)q;
-        c->C[q == 2 ? 0 : (q == 4 ? 1 : 2)]++;
+        c->C[class_of_width(q)]++;
     }
     free(G);
     c->allocated = 1;
@@ -401,7 +472,7 @@ int or_allocate(or_ctx *c) {
 int or_reorder(or_ctx *c) {
     if (!c->allocated) return -3;
     int64_t p = 0;
-    for (int k = 0; k < 3; k++)
+    for (int k = 0; k < c->ncls; k++)
         for (int64_t j = 0; j < c->J; j++)
             if (c->width[j] == Q_OF_CLASS[k]) {
                 c->perm[p] = (int32_t)j;
@@ -426,6 +497,9 @@ void or_get_perm(const or_ctx *c, int32_t *perm, int32_t *inv) {
 void or_get_class_counts(const or_ctx *c, int64_t counts[3]) {
     counts[0] = c->C[0]; counts[1] = c->C[1]; counts[2] = c->C[2];
 }
+void or_get_class_counts4(const or_ctx *c, int64_t counts[4]) {
+    for (int k = 0; k < 4; k++) counts[k] = c->C[k];
+}
 
 /* ------------------------------------------------------------------ */
 /* Parts and region layout (readings; the pages give no wire format).      */
@@ -439,15 +513,16 @@ void or_get_class_counts(const or_ctx *c, int64_t counts[3]) {
 /* ------------------------------------------------------------------ */
 
 typedef struct {
-    int64_t lo[3], cnt[3];    /* stream positions per class */
+    int64_t lo[4], cnt[4];    /* stream positions per class */
     int64_t N;
-    int64_t off_codes[3], off_s, off_c, bytes;
+    int64_t off_codes[4], off_s, off_c, bytes;
 } part_layout;
 
 static void layout_part(const or_ctx *c, int64_t m, int64_t part, part_layout *pl) {
     int64_t base = 0;
     pl->N = 0;
-    for (int k = 0; k < 3; k++) {
+    for (int k = 0; k < 4; k++) pl->lo[k] = pl->cnt[k] = pl->off_codes[k] = 0;
+    for (int k = 0; k < c->ncls; k++) {
         int64_t a = part * c->C[k] / m, b = (part + 1) * c->C[k] / m;
         pl->lo[k] = base + a;
         pl->cnt[k] = b - a;
@@ -455,7 +530,7 @@ static void layout_part(const or_ctx *c, int64_t m, int64_t part, part_layout *p
         base += c->C[k];
     }
     int64_t off = 0;
-    for (int k = 0; k < 3; k++) {
+    for (int k = 0; k < c->ncls; k++) {
         pl->off_codes[k] = off;
         off += pl->cnt[k] * 32 * Q_OF_CLASS[k];
     }
@@ -467,10 +542,10 @@ static void layout_part(const or_ctx *c, int64_t m, int64_t part, part_layout *p
     pl->bytes = off;
 }
 
-int64_t or_region_bytes(const or_ctx *c, int64_t m, int64_t part, int64_t counts_out[3]) {
+int64_t or_region_bytes(const or_ctx *c, int64_t m, int64_t part, int64_t counts_out[4]) {
     part_layout pl;
     layout_part(c, m, part, &pl);
-    if (counts_out) for (int k = 0; k < 3; k++) counts_out[k] = pl.cnt[k];
+    if (counts_out) for (int k = 0; k < 4; k++) counts_out[k] = pl.cnt[k];
     return pl.bytes;
 }
 
@@ -518,7 +593,7 @@ static float step_of(float A) {
 }
 
 static void encode_sg(const float *y, int q, const float *L, const float *W,
-                      const uint16_t *d, uint8_t *codes, float *s_out, uint8_t *cg) {
+                      const uint16_t *d, uint16_t *codes, float *s_out, uint8_t *cg) {
     const int Q = 1 << q;
     float a[OR_NGROUPS];
     float A = 0.0f;
@@ -544,16 +619,27 @@ static void encode_sg(const float *y, int q, const float *L, const float *W,
             float v = y[idx] * inv;
             if (v < -1.0f) v = -1.0f;
             if (v > 1.0f) v = 1.0f;
-            int r = Q - 2;
-            while (r > 0 && L[r] > v) r--;
+            int r;
+            if (q <= 8) {
+                r = Q - 2;
+                while (r > 0 && L[r] > v) r--;
+            } else {
+                /* 65536 levels: bisection for the same r (L is increasing) */
+                int lo = 0, hi = Q - 2;          /* L[lo] <= v always (L[0] = -1) */
+                while (lo < hi) {
+                    int mid = lo + (hi - lo + 1) / 2;
+                    if (L[mid] <= v) lo = mid; else hi = mid - 1;
+                }
+                r = lo;
+            }
             float p65536 = (v - L[r]) * W[r];
             float dd = (float)d[idx] + 0.5f;
-            codes[idx] = (uint8_t)(r + (dd < p65536 ? 1 : 0));
+            codes[idx] = (uint16_t)(r + (dd < p65536 ? 1 : 0));
         }
     }
 }
 
-static void decode_sg(const uint8_t *codes, int q, const float *L, float s,
+static void decode_sg(const uint16_t *codes, int q, const float *L, float s,
                       const uint8_t *cg, float *x) {
     (void)q;
     for (int g = 0; g < OR_NGROUPS; g++) {
@@ -565,30 +651,38 @@ static void decode_sg(const uint8_t *codes, int q, const float *L, float s,
     }
 }
 
-static void pack_codes(const uint8_t *codes, int q, uint8_t *out) {
+/* code i at bit q i of the payload, least significant bit first; a 16-bit
+   code takes two bytes, low byte first */
+static void pack_codes(const uint16_t *codes, int q, uint8_t *out) {
     memset(out, 0, (size_t)(32 * q));
     for (int i = 0; i < OR_SG; i++) {
         int bit = q * i;
-        out[bit / 8] |= (uint8_t)(codes[i] << (bit % 8));
+        if (q == 16) {
+            out[bit / 8] = (uint8_t)(codes[i] & 0xFF);
+            out[bit / 8 + 1] = (uint8_t)(codes[i] >> 8);
+        } else {
+            out[bit / 8] |= (uint8_t)(codes[i] << (bit % 8));
+        }
     }
 }
 
-static void unpack_codes(const uint8_t *in, int q, uint8_t *codes) {
+static void unpack_codes(const uint8_t *in, int q, uint16_t *codes) {
     const int mask = (1 << q) - 1;
     for (int i = 0; i < OR_SG; i++) {
         int bit = q * i;
-        codes[i] = (uint8_t)((in[bit / 8] >> (bit % 8)) & mask);
+        if (q == 16) codes[i] = (uint16_t)(in[bit / 8] | (in[bit / 8 + 1] << 8));
+        else codes[i] = (uint16_t)((in[bit / 8] >> (bit % 8)) & mask);
     }
 }
 
-static void write_sg(const sg_slot *sl, const uint8_t *codes, float s, const uint8_t *cg) {
+static void write_sg(const sg_slot *sl, const uint16_t *codes, float s, const uint8_t *cg) {
     pack_codes(codes, sl->q, sl->codes);
     memcpy(sl->s, &s, 4);
     memcpy(sl->cg, cg, 16);
 }
 
 static void read_sg(const or_ctx *c, const sg_slot *sl, float *x) {
-    uint8_t codes[OR_SG];
+    uint16_t codes[OR_SG];
     float s;
     unpack_codes(sl->codes, sl->q, codes);
     memcpy(&s, sl->s, 4);
@@ -745,7 +839,7 @@ static int64_t collect_refs(const part_layout *pl, const int64_t *filter, int64_
     int64_t cap = pl->N;
     sg_ref *refs = (sg_ref *)malloc((size_t)(cap > 0 ? cap : 1) * sizeof(sg_ref));
     int64_t n = 0;
-    for (int k = 0; k < 3; k++) {
+    for (int k = 0; k < 4; k++) {
         int64_t lo = pl->lo[k], hi = pl->lo[k] + pl->cnt[k];
         if (!filter) {
             for (int64_t p = lo; p < hi; p++) { refs[n].k = k; refs[n].idx = p - lo; refs[n].pos = p; n++; }
@@ -781,7 +875,8 @@ int or_compress(or_ctx *c, int32_t worker, int32_t step, const void *grad,
         for (int i = 0; i < OR_SG; i++) y[i] = load_elem(grad, dtype, j * OR_SG + i) - mu;
         uint16_t d[OR_SG];
         event_dithers(c, j, worker, step, 1, event, d);
-        uint8_t codes[OR_SG], cg[16];
+        uint16_t codes[OR_SG];
+        uint8_t cg[16];
         float s;
         encode_sg(y, Q_OF_CLASS[k], c->L[k], c->W[k], d, codes, &s, cg);
         sg_slot sl;
@@ -853,7 +948,8 @@ int or_hop(or_ctx *c, int32_t worker, int32_t step, const uint8_t *region_in,
         }
         uint16_t d[OR_SG];
         event_dithers(c, j, worker, step, 0, event, d);
-        uint8_t codes[OR_SG], cg[16];
+        uint16_t codes[OR_SG];
+        uint8_t cg[16];
         float s;
         encode_sg(y, Q_OF_CLASS[k], c->L[k], c->W[k], d, codes, &s, cg);
         sg_slot so;
@@ -900,9 +996,10 @@ int or_finalize(or_ctx *c, int64_t part, const uint8_t *region, float *out,
 /* ------------------------------------------------------------------ */
 
 static int64_t worst_region_bytes(const or_ctx *c) {
-    /* every region is at most one part of m >= 2 (or the whole vector) */
+    /* every region is at most one part of m >= 2 (or the whole vector), each
+       super-group at most 32 qmax code bytes + 20 */
     int64_t N = c->J + 3;
-    return N * (256 + 20) + 64;
+    return N * (32 * c->qmax + 20) + 64;
 }
 
 int or_allreduce(or_ctx *c, const void *const *grads, int32_t dtype, float *out) {
@@ -970,33 +1067,36 @@ int or_allreduce(or_ctx *c, const void *const *grads, int32_t dtype, float *out)
 /* Codec entry points for statistical pins                             */
 /* ------------------------------------------------------------------ */
 
-static int class_of_q(int q) { return q == 2 ? 0 : (q == 4 ? 1 : 2); }
-
 void or_roundtrip_sg(const float *y, int32_t q, const uint16_t *dither, double eps,
-                     float *decoded, uint8_t *codes_out, float *scale, uint8_t *cg_out) {
-    float L[256], W[256];
+                     float *decoded, uint16_t *codes_out, float *scale, uint8_t *cg_out) {
+    float *L = (float *)malloc(65536 * sizeof(float)), *W = (float *)malloc(65536 * sizeof(float));
     or_levels(q, eps, L, W);
-    uint8_t codes[OR_SG], cg[16];
+    uint16_t codes[OR_SG];
+    uint8_t cg[16];
     float s;
     encode_sg(y, q, L, W, dither, codes, &s, cg);
     decode_sg(codes, q, L, s, cg, decoded);
-    if (codes_out) memcpy(codes_out, codes, OR_SG);
+    if (codes_out) memcpy(codes_out, codes, sizeof(codes));
     if (scale) *scale = s;
     if (cg_out) memcpy(cg_out, cg, 16);
-    (void)class_of_q;
+    free(L);
+    free(W);
 }
 
 void or_roundtrip_batch(const float *y, int64_t K, int32_t q, const uint16_t *dither,
                         double eps, float *decoded) {
-    float L[256], W[256];
+    float *L = (float *)malloc(65536 * sizeof(float)), *W = (float *)malloc(65536 * sizeof(float));
     or_levels(q, eps, L, W);
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < K; t++) {
-        uint8_t codes[OR_SG], cg[16];
+        uint16_t codes[OR_SG];
+        uint8_t cg[16];
         float s;
         encode_sg(y + t * OR_SG, q, L, W, dither + t * OR_SG, codes, &s, cg);
         decode_sg(codes, q, L, s, cg, decoded + t * OR_SG);
     }
+    free(L);
+    free(W);
 }
 
 /* ------------------------------------------------------------------ */

@@ -98,6 +98,11 @@ void or_set_rounding(or_ctx *c, int32_t mode);
 void or_set_eps(or_ctx *c, double eps);
 void or_set_alloc(or_ctx *c, int32_t mode);
 void or_set_own(or_ctx *c, int32_t mode);
+/* Width set: qmax 8 gives {2,4,8} (the method: the clamp of the review's
+ * referee minor 2), qmax 16 adds the 16-bit class of the threshold chain of
+ * the review's Fig. 3 caption (T48 = 257/2^17 T816).  Returns -1 for any
+ * other value. */
+int or_set_max_width(or_ctx *c, int32_t qmax);
 
 /* Stage 1: per-worker statistics, called in rank order 0..n-1. */
 int or_stats(or_ctx *c, int32_t worker, const void *grad, int32_t dtype);
@@ -115,18 +120,26 @@ void or_get_alloc_key(const or_ctx *c, float *out);
 void or_get_widths(const or_ctx *c, uint8_t *w);
 void or_get_perm(const or_ctx *c, int32_t *perm, int32_t *inv);
 void or_get_class_counts(const or_ctx *c, int64_t counts[3]);
+/* with the 16-bit class (counts[3] is 0 without it) */
+void or_get_class_counts4(const or_ctx *c, int64_t counts[4]);
 int64_t or_budget_bits(const or_ctx *c);
 int64_t or_count_bits(const or_ctx *c, uint32_t rho_bits);
 /* Widths q_j in {2,4,8} minimising sum_j F_j 4^-q_j subject to
  * sum_j q_j <= budget_bits (J <= 4096, budget_bits >= 2 J); returns that
  * minimum (fp64), or -1 on bad arguments. */
 double or_alloc_exact(const float *F, int64_t J, int64_t budget_bits, uint8_t *widths);
+/* the same over the width set of qmax (8 or 16) */
+double or_alloc_exact_q(const float *F, int64_t J, int64_t budget_bits, int32_t qmax, uint8_t *widths);
 /* T12, T24, T48 for the scalar with bit pattern rho_bits. */
 void or_thresholds(uint32_t rho_bits, float out[3]);
+/* With the 16-bit class: T12, T24, T48, T816 = fl(K rho) with the chain
+ * scaled by 257, K = 21845, 139808, 4210688, 2^31. */
+void or_thresholds_wide(uint32_t rho_bits, float out[4]);
 
-/* Region of part (m, part): bytes and per-class counts. */
+/* Region of part (m, part): bytes and per-class counts (4 entries; the
+ * last is 0 without the 16-bit class). */
 int64_t or_region_bytes(const or_ctx *c, int64_t m, int64_t part,
-                        int64_t counts_out[3]);
+                        int64_t counts_out[4]);
 
 /* Schedule steps.  `filter` (sorted global stream positions, may be NULL)
  * restricts the work to those super-groups; other bytes are left untouched.
@@ -150,9 +163,10 @@ int or_allreduce(or_ctx *c, const void *const *grads, int32_t dtype,
                  float *out);
 
 /* Codec on one super-group with explicit 16-bit dithers (for statistical
- * pins): encodes y[256] at width q and returns the decoded values. */
+ * pins): encodes y[256] at width q (2, 4, 8 or 16) and returns the decoded
+ * values, the codes, the scale unit and the group codes. */
 void or_roundtrip_sg(const float *y, int32_t q, const uint16_t *dither,
-                     double eps, float *decoded, uint8_t *codes, float *scale,
+                     double eps, float *decoded, uint16_t *codes, float *scale,
                      uint8_t *cg);
 /* Batch: K rows of y and dithers -> K rows of decoded values. */
 void or_roundtrip_batch(const float *y, int64_t K, int32_t q,

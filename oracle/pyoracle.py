@@ -57,6 +57,10 @@ def lib():
             "or_count_bits": (i64, [vp, u32]),
             "or_thresholds": (None, [u32, vp]),
             "or_alloc_exact": (f64, [vp, i64, i64, vp]),
+            "or_alloc_exact_q": (f64, [vp, i64, i64, i32, vp]),
+            "or_set_max_width": (C.c_int, [vp, i32]),
+            "or_get_class_counts4": (None, [vp, vp]),
+            "or_thresholds_wide": (None, [u32, vp]),
             "or_region_bytes": (i64, [vp, i64, i64, vp]),
             "or_compress": (C.c_int, [vp, i32, i32, vp, i32, vp, vp, i64]),
             "or_hop": (C.c_int, [vp, i32, i32, vp, vp, i32, vp, vp, vp, i64]),
@@ -106,22 +110,28 @@ def philox4x32(ctr, key, rounds=10):
 
 
 def levels(q, eps=0.5):
-    L = np.zeros(256, np.float32)
-    W = np.zeros(256, np.float32)
+    L = np.zeros(max(256, 1 << q), np.float32)
+    W = np.zeros(max(256, 1 << q), np.float32)
     lib().or_levels(int(q), float(eps), _p(L), _p(W))
     Q = 1 << q
     return L[:Q].copy(), W[:Q - 1].copy()
 
 
-def alloc_exact(F, budget_bits):
-    """(widths, cost): the widths in {2,4,8} minimising sum F 4^-q under
-    sum q <= budget_bits, and that minimum."""
+def alloc_exact(F, budget_bits, qmax=8):
+    """(widths, cost): the widths in {2,4,8} (or {2,4,8,16} for qmax 16)
+    minimising sum F 4^-q under sum q <= budget_bits, and that minimum."""
     F = np.ascontiguousarray(F, dtype=np.float32)
     w = np.zeros(F.size, np.uint8)
-    cost = lib().or_alloc_exact(_p(F), F.size, int(budget_bits), _p(w))
+    cost = lib().or_alloc_exact_q(_p(F), F.size, int(budget_bits), int(qmax), _p(w))
     if cost < 0:
         raise ValueError("or_alloc_exact: J out of range or budget below 2 bits")
     return w, cost
+
+
+def thresholds_wide(rho_bits):
+    out = np.zeros(4, np.float32)
+    lib().or_thresholds_wide(int(rho_bits), _p(out))
+    return out
 
 
 def thresholds(rho_bits):
@@ -146,7 +156,7 @@ def roundtrip_sg(y, q, dither, eps=0.5):
     y = np.ascontiguousarray(y, dtype=np.float32)
     d = np.ascontiguousarray(dither, dtype=np.uint16)
     dec = np.zeros(256, np.float32)
-    codes = np.zeros(256, np.uint8)
+    codes = np.zeros(256, np.uint16)
     s = np.zeros(1, np.float32)
     cg = np.zeros(16, np.uint8)
     lib().or_roundtrip_sg(_p(y), int(q), _p(d), float(eps), _p(dec), _p(codes), _p(s), _p(cg))
@@ -191,7 +201,7 @@ class Oracle:
     """One simulated round on the CPU (mirrors the stage order of the library)."""
 
     def __init__(self, n_coords, n_workers, topology=RING, avg_bits=5.0, seed=1, rnd=0,
-                 rounding=STRATIFIED, eps=None, alloc=ALLOC_THRESHOLD, own=OWN_PACKED):
+                 rounding=STRATIFIED, eps=None, alloc=ALLOC_THRESHOLD, own=OWN_PACKED, max_width=8):
         self.d = int(n_coords)
         self.n = int(n_workers)
         self.topology = int(topology)
@@ -206,6 +216,9 @@ class Oracle:
             lib().or_set_eps(self.h, float(eps))
         lib().or_set_alloc(self.h, int(alloc))
         lib().or_set_own(self.h, int(own))
+        if max_width != 8 and lib().or_set_max_width(self.h, int(max_width)) != 0:
+            raise ValueError("max_width must be 8 or 16")
+        self.max_width = int(max_width)
         self.log2n = max(0, (self.n - 1).bit_length())
 
     def __del__(self):
@@ -257,9 +270,10 @@ class Oracle:
         return p, i
 
     def class_counts(self):
-        c = np.zeros(3, np.int64)
-        lib().or_get_class_counts(self.h, _p(c))
-        return c
+        """Super-groups per class: (2, 4, 8), or (2, 4, 8, 16) with the 16-bit class."""
+        c = np.zeros(4, np.int64)
+        lib().or_get_class_counts4(self.h, _p(c))
+        return c[:4 if self.max_width == 16 else 3]
 
     def budget_bits(self):
         return int(lib().or_budget_bits(self.h))
@@ -268,12 +282,12 @@ class Oracle:
         return int(lib().or_count_bits(self.h, int(rho_bits)))
 
     def region_bytes(self, m, part):
-        cnt = np.zeros(3, np.int64)
+        cnt = np.zeros(4, np.int64)
         b = lib().or_region_bytes(self.h, int(m), int(part), _p(cnt))
-        return int(b), cnt
+        return int(b), cnt[:4 if self.max_width == 16 else 3]
 
     def worst_region_bytes(self):
-        return (self.J + 3) * 276 + 64
+        return (self.J + 3) * (32 * self.max_width + 20) + 64
 
     def compress(self, w, step, g, region, filt=None):
         f = None if filt is None else np.ascontiguousarray(filt, np.int64)

@@ -1265,3 +1265,155 @@ def test_exact_allocation_special_budgets_and_pipeline():
     assert np.isnan(o.rho())
     exact = np.sum([g.astype(np.float64) for g in gs], axis=0)
     assert np.sum((out - exact) ** 2) / np.sum(exact ** 2) < 1e-2
+
+
+# ---------------------------------------------------------------------------
+# the 16-bit class (pith.science review, Fig. 3 caption: the threshold chain
+# continues to T48 = 257/2^17 T816; "What carries the argument": the per-bit
+# benefit of the 4^-b model); off by default, where the widths are {2,4,8}
+# ---------------------------------------------------------------------------
+
+def test_wide_threshold_chain_is_exact():
+    """The four multipliers of the 16-bit chain (the 85 : 544 : 16384 chain
+    scaled by 257, then 2^31) carry the pages' ratios exactly, the last one
+    equalising the 8 -> 16 per-bit benefit 65535 / 2^35 with the 4 -> 8 one;
+    and fp32 thresholds at powers of two keep them exactly."""
+    g = gold("pages_constants.json")
+    K = [Fraction(21845), Fraction(139808), Fraction(4210688), Fraction(2 ** 31)]
+    assert K[0] / K[1] == frac(g["ratio_T12_over_T24"]["value"])
+    assert K[1] / K[2] == frac(g["ratio_T24_over_T48"]["value"])
+    assert K[2] / K[3] == frac(g["ratio_T48_over_T816"]["value"])
+    b816 = (Fraction(1, 4 ** 8) - Fraction(1, 4 ** 16)) / 8
+    assert b816 == Fraction(65535, 2 ** 35)
+    assert b816 / frac(g["per_bit_benefit_4_to_8"]["value"]) == frac(g["ratio_T48_over_T816"]["value"])
+    for rho in (1.0, 2.0 ** -30, 2.0 ** 5):
+        t = [Fraction(float(x)) for x in po.thresholds_wide(f32_bits(rho))]
+        assert t[1] / t[2] == frac(g["ratio_T24_over_T48"]["value"])
+        assert t[2] / t[3] == frac(g["ratio_T48_over_T816"]["value"])
+
+
+def _alloc_wide(F, budget):
+    J = len(F)
+    o = po.Oracle(256 * J, 1, po.RING, budget, max_width=16)
+    g = np.zeros(256 * J, np.float32)
+    g[::256] = np.sqrt(F).astype(np.float32)
+    o.stats(0, g)
+    o.allocate()
+    _, Fo, _ = o.stats_arrays()
+    return o, Fo
+
+
+def test_wide_allocation_brute_force_8_super_groups():
+    """Against all 4^8 assignments of {2,4,8,16}: Lagrangian optimality,
+    threshold consistency at rho (the chain 544 : 16384 : 16384 * 2^17 / 257
+    in exact rationals), minimal rho, budget kept; and the exact programme
+    over the four widths returns the brute-force optimum."""
+    rng = np.random.default_rng(71)
+    assigns = np.array(list(itertools.product((2, 4, 8, 16), repeat=8)), dtype=np.int64)
+    bits = assigns.sum(1)
+    pw = 4.0 ** (-assigns.astype(np.float64))
+    for trial in range(120):
+        F = np.exp(rng.uniform(-40, 5, 8)) if trial % 2 else rng.lognormal(0, 6, 8)
+        budget = float(rng.choice([2.0, 3.0, 4.5, 6.0, 8.0, 9.5, 11.0, 13.0, 15.9, 16.0, 20.0]))
+        o, Fo = _alloc_wide(F, budget)
+        F64 = Fo.astype(np.float64)
+        q = o.widths().astype(np.int64)
+        total = int(q.sum())
+        assert set(np.unique(q)) <= {2, 4, 8, 16}
+        assert total <= min(budget, 16.0) * 8 + 1e-9
+        rb = o.rho_bits()
+        assert o.count_bits(rb) == total
+        if rb > 0:
+            assert o.count_bits(rb - 1) > o.budget_bits()
+        err = pw @ F64
+        mine = float((F64 * 4.0 ** (-q.astype(np.float64))).sum())
+        assert mine <= err[bits <= total].min() * (1 + 1e-9)
+        rho = Fraction(float(f32_from_bits(rb)))
+        T816 = rho * 2 ** 31
+        T48 = T816 * Fraction(257, 2 ** 17)
+        T24 = T48 * Fraction(17, 512)
+        for Fj, qj in zip(F64, q):
+            Fr = Fraction(float(Fj))
+            exp_q = 16 if Fr >= T816 else (8 if Fr >= T48 else (4 if Fr >= T24 else 2))
+            if exp_q != qj:
+                # only a tie inside one fp32 rounding of T48 or T24 may differ
+                assert min(abs(Fr - T48) / T48, abs(Fr - T24) / T24) <= Fraction(1, 2 ** 23)
+        # the exact programme over the four widths
+        w, cost = po.alloc_exact(Fo, o.budget_bits(), qmax=16)
+        best = err[bits <= o.budget_bits()].min()
+        assert abs(cost - best) <= 1e-12 * best and int(w.astype(np.int64).sum()) <= o.budget_bits()
+
+
+def test_wide_allocation_special_budgets():
+    rng = np.random.default_rng(72)
+    F = rng.lognormal(0, 3, 64)
+    o, _ = _alloc_wide(F, 16.0)
+    assert (o.widths() == 16).all() and o.rho_bits() == 0
+    o, _ = _alloc_wide(F, 1e9)
+    assert (o.widths() == 16).all()
+    o, _ = _alloc_wide(F, 2.0)
+    assert (o.widths() == 2).all()
+    o8, _ = _alloc(F, 8.0)
+    assert (o8.widths() == 8).all()          # the default width set caps at 8
+    with pytest.raises(ValueError):
+        po.Oracle(256, 1, po.RING, 5.0, max_width=12)
+
+
+def test_level_table_16_bits():
+    L, W = po.levels(16)
+    assert L.size == 65536 and L[0] == -1.0 and L[-1] == 1.0
+    assert np.all(np.diff(L.astype(np.float64)) > 0)
+    assert np.array_equal(L[::-1], -L)
+    # the widest interval is at the ends, the narrowest at zero (denser near 0)
+    gaps = np.diff(L.astype(np.float64))
+    assert gaps[32767] < gaps[0] and gaps[0] / gaps[32767] > 2.5
+    # the same closed form as the narrower classes at their shared levels:
+    # u = (2r + 1 - Q) / (Q - 1), L = u (1 + |u|) / 2 for eps = 1/2
+    r = np.array([0, 1, 100, 32767, 32768, 65534, 65535])
+    u = (2.0 * r + 1 - 65536) / 65535
+    assert np.array_equal(L[r], (u * (0.5 + 0.5 * np.abs(u))).astype(np.float32))
+
+
+def test_codec_16_bits_unbiased_and_bounded():
+    """Monte Carlo over 10^4 dithers (D23 gate) and the deterministic bound
+    |x_hat - y| <= sigma (L[r+1] - L[r]) at 65,536 levels."""
+    rng = np.random.default_rng(73)
+    K = 10000
+    y = (rng.standard_normal(256) * np.repeat(10.0 ** rng.uniform(-3, 0, 16), 16)).astype(np.float32)
+    Y = np.tile(y, (K, 1))
+    D = rng.integers(0, 65536, size=(K, 256), dtype=np.uint16)
+    dec = po.roundtrip_batch(Y, 16, D).astype(np.float64)
+    sd = dec.std(0, ddof=1)
+    ok = sd > 0
+    _d23_gate((dec.mean(0)[ok] - y[ok]) / (sd[ok] / np.sqrt(K)))
+    L, _ = po.levels(16)
+    for t in range(20):
+        x, codes, s, cg = po.roundtrip_sg(y, 16, D[t])
+        sigma = (cg.astype(np.float32).repeat(16) * np.float32(s)).astype(np.float64)
+        r = np.clip(codes.astype(np.int64), 1, 65534)
+        width = sigma * np.maximum(L[r].astype(np.float64) - L[r - 1], L[r + 1].astype(np.float64) - L[r])
+        assert np.all(np.abs(x - y) <= width * (1 + 1e-6) + 1e-30)
+        assert codes.max() <= 65535
+
+
+def test_wide_round_budget_exactness_and_gain():
+    """Whole rounds with the 16-bit class: the budget holds, constant and
+    zero super-groups are exact, and at 10 bits per coordinate the error is
+    below the {2,4,8} round at its 8-bit cap."""
+    rng = np.random.default_rng(74)
+    n, J = 4, 48
+    gs = _grads(rng, n, J, 3)
+    for g in gs:
+        g[0:256] = 0.0
+        g[512:768] = 0.25
+    exact = np.sum([g.astype(np.float64) for g in gs], 0)
+    for topo in (po.RING, po.BUTTERFLY):
+        o = po.Oracle(256 * J, n, topo, 10.0, max_width=16)
+        out = o.allreduce(gs)
+        q = o.widths().astype(np.int64)
+        assert q.sum() <= 10 * J and (q == 16).any()
+        assert np.all(out[0:256] == 0.0) and np.all(out[512:768] == np.float32(n * 0.25))
+        v16 = np.sum((out - exact) ** 2) / np.sum(exact ** 2)
+        o8 = po.Oracle(256 * J, n, topo, 8.0)
+        v8 = np.sum((o8.allreduce(gs) - exact) ** 2) / np.sum(exact ** 2)
+        assert v16 < v8
