@@ -43,6 +43,7 @@ struct dq_plan {
     bool timing = false;
     uint32_t timing_kinds = (1u << DQ_K_COUNT) - 1u;   // kinds timed while timing is on
     double eps = kDefaultEps;                          // level shape
+    int32_t qmax = 8;                                  // widest class: 8, or 16 (DQ_OPT_MAX_WIDTH)
     bool tables_dirty = true;                          // workspace tables to (re)build
 
     uint8_t *ws = nullptr;
@@ -60,7 +61,7 @@ struct dq_plan {
     hipStream_t aux = nullptr;
     hipEvent_t fork_ev = nullptr, join_ev = nullptr;
     dq_timing acc{};
-    int64_t host_counts[3] = {0, 0, 0};
+    int64_t host_counts[kClasses] = {0, 0, 0, 0};
 };
 
 namespace {
@@ -73,7 +74,7 @@ int32_t *blkcnt_of(dq_plan *p) {
 }
 PartInfo *parts_of(dq_plan *p) {
     return reinterpret_cast<PartInfo *>(p->ws + p->lay.ctrl + align_up(sizeof(Ctrl), kAlign) +
-                                        align_up(4 * 3 * (size_t)p->nblk, kAlign));
+                                        align_up(4 * kClasses * (size_t)p->nblk, kAlign));
 }
 const PartInfo *part_entry(dq_plan *p, int64_t m, int64_t c) {
     return parts_of(p) + part_table_index(p->n, p->topo, m, c);
@@ -91,8 +92,14 @@ void compute_layout(dq_plan *p) {
     p->lay.tables = off; off = align_up(off + sizeof(DeviceTables), kAlign);
     p->lay.ctrl = off;
     off = align_up(off + sizeof(Ctrl), kAlign);
-    off = align_up(off + 4 * 3 * (size_t)p->nblk, kAlign);
+    off = align_up(off + 4 * kClasses * (size_t)p->nblk, kAlign);
     off = align_up(off + sizeof(PartInfo) * (size_t)part_table_entries(p->n, p->topo), kAlign);
+    // the 16-bit class's 65,536 levels and weights
+    p->lay.tables16 = 0;
+    if (p->qmax == 16) {
+        p->lay.tables16 = off;
+        off = align_up(off + 2 * 65536 * sizeof(float), kAlign);
+    }
     p->lay.total = off;
 }
 
@@ -214,6 +221,22 @@ void fill_common(dq_plan *p, CodecArgs &a) {
     a.perm = i32_at(p, p->lay.perm);
     a.mu_stream = f32_at(p, p->lay.mu_stream);
     a.n_workers_f = (float)p->n;
+    if (p->qmax == 16) {
+        a.L16 = f32_at(p, p->lay.tables16);
+        a.W16 = a.L16 + 65536;
+    }
+    a.eps = (float)p->eps;
+}
+
+// bytes of one super-group in a region at the widest class: codes, scale
+// unit, group codes
+size_t sg_region_bytes(const dq_plan *p) { return (size_t)(32 * p->qmax + 4 + 16); }
+
+// a part of the smallest m the schedule uses must stay below 4 GB (32-bit
+// region offsets in the kernels)
+bool region_fits(int64_t n_coords, int32_t n, int32_t topology, size_t per_sg) {
+    const int64_t m_min = n == 1 ? 1 : (topology == DQ_RING ? n : 2);
+    return (n_coords / kSG / m_min + 3) * (int64_t)per_sg + 256 < ((int64_t)1 << 32);
 }
 
 int64_t max_part_sg(const dq_plan *p, int64_t m) { return p->J / m + 3; }
@@ -308,8 +331,7 @@ dq_status dq_plan_create(int64_t n_coords, int32_t n_workers, int32_t topology, 
     if (!(avg_bits >= 2.0f)) return DQ_EBUDGET;
     // codec kernels address a region with 32-bit offsets: the largest region
     // (a part of the smallest m the schedule uses) must stay below 4 GB
-    const int64_t m_min = n_workers == 1 ? 1 : (topology == DQ_RING ? n_workers : 2);
-    if ((n_coords / kSG / m_min + 3) * (256 + 4 + 16) + 256 >= ((int64_t)1 << 32)) return DQ_EINVAL;
+    if (!region_fits(n_coords, n_workers, topology, 256 + 4 + 16)) return DQ_EINVAL;
     dq_plan *p = new (std::nothrow) dq_plan();
     if (!p) return DQ_EINVAL;
     p->d = n_coords;
@@ -370,6 +392,20 @@ dq_status dq_plan_set_u64(dq_plan *p, int32_t option, uint64_t v) {
                 return DQ_EINVAL;
             p->alloc = (int32_t)v;
             return DQ_OK;
+        case DQ_OPT_MAX_WIDTH: {
+            if (v != 8 && v != 16) return DQ_EINVAL;
+            if (v == 16 && !region_fits(p->d, p->n, p->topo, 512 + 4 + 16)) return DQ_EINVAL;
+            p->qmax = (int32_t)v;
+            p->budget_bits = (long long)std::floor(std::min((double)p->budget, (double)p->qmax) * (double)p->J);
+            compute_layout(p);
+            // the workspace size changed: bind again before the next round
+            p->ws = nullptr;
+            p->ws_bytes = 0;
+            p->stats_done = 0;
+            p->allocated = p->reordered = false;
+            p->tables_dirty = true;
+            return DQ_OK;
+        }
         case DQ_OPT_STREAMS:
             if (v != 1 && v != 2) return DQ_EINVAL;
             if (v == 2) {
@@ -432,7 +468,7 @@ size_t dq_partial_bytes_max(const dq_plan *p, int64_t m) {
 size_t dq_region_bytes_max(const dq_plan *p, int64_t m) {
     if (!p || m < 1 || m > p->n || (p->n % m) != 0) return 0;
     const int64_t N = max_part_sg(p, m);
-    return align_up((size_t)N * (256 + 4 + 16) + 16, kAlign);
+    return align_up((size_t)N * sg_region_bytes(p) + 16, kAlign);
 }
 
 int64_t dq_final_part(const dq_plan *p, int32_t w) {
@@ -459,6 +495,10 @@ dq_status dq_stats(dq_plan *p, int32_t w, const void *grad, int32_t kind, void *
         // on the device, ahead of every codec launch on this stream
         if (e == hipSuccess && p->tables_dirty)
             e = launch_build_tables(reinterpret_cast<DeviceTables *>(p->ws + p->lay.tables), p->eps, s);
+        if (e == hipSuccess && p->tables_dirty && p->qmax == 16) {
+            float *L16 = f32_at(p, p->lay.tables16);
+            e = launch_build_tables16(L16, L16 + 65536, p->eps, s);
+        }
         if (e != hipSuccess) return DQ_EHIP;
         p->tables_dirty = false;
     }
@@ -494,8 +534,9 @@ dq_status dq_allocate(dq_plan *p, void *stream) {
     a.sum = f32_at(p, p->lay.sum);
     a.denom = (float)(256 * p->n);
     a.mode = p->alloc;
+    a.wide = p->qmax == 16;
     // uniform: the widest class whose width fits the budget
-    a.uniform_k = p->budget >= 8.0f ? 2 : (p->budget >= 4.0f ? 1 : 0);
+    a.uniform_k = (a.wide && p->budget >= 16.0f) ? 3 : (p->budget >= 8.0f ? 2 : (p->budget >= 4.0f ? 1 : 0));
     Launch L;
     hipError_t e = timed_begin(p, DQ_K_ALLOCATE, 0, 0, s, L);
     // histograms, class counts, prefix and flag start at zero (a fill kernel,
@@ -556,7 +597,7 @@ dq_status dq_compress(dq_plan *p, int32_t w, int32_t step, const void *grad, int
     a.out = static_cast<uint8_t *>(out);
     Launch L;
     hipError_t e = timed_begin(p, DQ_K_COMPRESS, sp.m, sp.part, s, L);
-    if (e == hipSuccess) e = launch_codec(a, kCompress, local_of_kind(kind), max_part_sg(p, sp.m), s);
+    if (e == hipSuccess) e = launch_codec(a, kCompress, local_of_kind(kind), max_part_sg(p, sp.m), p->qmax == 16, s);
     if (e == hipSuccess) e = timed_end(p, L, s);
     return hip_status(e);
 }
@@ -612,7 +653,8 @@ dq_status hop_impl(dq_plan *p, int32_t w, int32_t step, const void *in, const vo
         const int mode = h == keep ? kPartial : (final_out ? kHopFinal : kHop);
         Launch L;
         e = timed_begin(p, kindk, m_out, c_out, s, L);
-        if (e == hipSuccess) e = launch_codec(a, mode, local_of_kind(local_kind), max_part_sg(p, m_out), s);
+        if (e == hipSuccess)
+            e = launch_codec(a, mode, local_of_kind(local_kind), max_part_sg(p, m_out), p->qmax == 16, s);
         if (e == hipSuccess) e = timed_end(p, L, s);
     }
     return hip_status(e);
@@ -645,7 +687,7 @@ dq_status dq_finalize(dq_plan *p, int64_t part, const void *region, float *out, 
     a.out_f32 = out;
     Launch L;
     hipError_t e = timed_begin(p, DQ_K_FINALIZE, p->n, part, s, L);
-    if (e == hipSuccess) e = launch_codec(a, kFinalize, kLocalNone, max_part_sg(p, p->n), s);
+    if (e == hipSuccess) e = launch_codec(a, kFinalize, kLocalNone, max_part_sg(p, p->n), p->qmax == 16, s);
     if (e == hipSuccess) e = timed_end(p, L, s);
     return hip_status(e);
 }
@@ -790,16 +832,20 @@ dq_status dq_get_info(dq_plan *p, dq_info *out, void *stream) {
     std::memset(out, 0, sizeof(*out));
     out->rho_bits = c.rho_bits;
     std::memcpy(&out->rho, &c.rho_bits, 4);
-    out->t12 = 85.0f * out->rho;
-    out->t24 = 544.0f * out->rho;
-    out->t48 = 16384.0f * out->rho;
+    const bool wide = p->qmax == 16;
+    out->t12 = (wide ? 21845.0f : 85.0f) * out->rho;
+    out->t24 = (wide ? 139808.0f : 544.0f) * out->rho;
+    out->t48 = (wide ? 4210688.0f : 16384.0f) * out->rho;
+    out->t816 = wide ? 2147483648.0f * out->rho : INFINITY;
     out->budget_bits = p->budget_bits;
     int64_t used = 0;
-    for (int k = 0; k < 3; k++) {
-        out->class_counts[k] = (int64_t)c.class_counts[k];
-        p->host_counts[k] = out->class_counts[k];
-        used += out->class_counts[k] * (2 << k);
+    for (int k = 0; k < kClasses; k++) {
+        const int64_t ck = (int64_t)c.class_counts[k];
+        if (k < 3) out->class_counts[k] = ck;
+        p->host_counts[k] = ck;
+        used += ck * (2 << k);
     }
+    out->class_count16 = (int64_t)c.class_counts[3];
     out->used_bits = used;
     out->achieved_bits = (double)used / (double)p->J;
     out->nonfinite = c.nonfinite ? 1 : 0;
@@ -826,7 +872,7 @@ dq_status dq_timing_read(dq_plan *p, dq_timing *out) {
         if (L.m == 0) {
             sg = p->J;
         } else {
-            for (int k = 0; k < 3; k++) {
+            for (int k = 0; k < kClasses; k++) {
                 const int64_t Ck = (int64_t)c.class_counts[k];
                 sg += (L.part + 1) * Ck / L.m - L.part * Ck / L.m;
             }

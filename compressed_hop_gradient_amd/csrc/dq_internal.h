@@ -21,7 +21,8 @@ constexpr int kRadixCand = 256;
 struct Ctrl {
     unsigned int hist4[kRadixCand + 1];       // per-pass histograms (see k_alloc_count)
     unsigned int hist8[kRadixCand + 1];
-    unsigned long long class_counts[3];       // super-groups at 2, 4, 8 bits
+    unsigned int hist16[kRadixCand + 1];      // (the 16-bit class)
+    unsigned long long class_counts[4];       // super-groups at 2, 4, 8 (and 16) bits
     uint32_t prefix;                          // bits of rho fixed so far
     uint32_t done;                            // 1 once rho is known
     uint32_t rho_bits;
@@ -34,15 +35,19 @@ struct Ctrl {
 // decoded final sum of its part (what finalize would compute from it).
 enum Mode { kCompress = 0, kHop = 1, kFinalize = 2, kPartial = 3, kHopFinal = 4 };
 
+// Width classes: 2, 4, 8 bits, and 16 when a plan takes the 16-bit class
+// (DQ_OPT_MAX_WIDTH); without it the fourth class is empty everywhere.
+constexpr int kClasses = 4;
+
 // Layout of one part (m, c) of the bitwidth-sorted stream and of its region;
 // computed once per round on the device (k_part_table) for every part the
 // schedule uses.
 struct PartInfo {
-    int64_t lo[3];     // first stream position of each class in the part
-    int64_t cnt[3];    // super-groups of each class
-    int64_t pre[3];    // part-local index of each class's first super-group
-    int64_t N;         // super-groups in the part
-    int64_t offc[3];   // region byte offset of each class's codes
+    int64_t lo[kClasses];     // first stream position of each class in the part
+    int64_t cnt[kClasses];    // super-groups of each class
+    int64_t pre[kClasses];    // part-local index of each class's first super-group
+    int64_t N;                // super-groups in the part
+    int64_t offc[kClasses];   // region byte offset of each class's codes
     int64_t offs;      // region byte offset of the fp32 scale units
     int64_t offg;      // region byte offset of the UINT8 group codes
     int64_t bytes;     // region size
@@ -72,6 +77,10 @@ struct CodecArgs {
     float *out_f32;                          // finalize output, original order
     float n_workers_f;                       // finalize: fl(n * mu)
     uint32_t key0, key1, round, tag, stagger;
+    // the 16-bit class: its 65,536 levels and weights (workspace), and the
+    // level shape for the first guess of the interval search
+    const float *L16, *W16;
+    float eps;
 };
 
 struct StatsArgs {
@@ -90,11 +99,12 @@ struct AllocArgs {
     float denom;        // fl(256 n)
     int32_t mode;       // AllocMode
     int32_t uniform_k;  // class of every super-group under kAllocUniform
+    int32_t wide;       // 1: widths {2,4,8,16} (thresholds 139808, 4210688, 2^31 rho)
     int64_t J;
     long long budget;   // floor(B * J)
     Ctrl *ctrl;
     uint8_t *widths;
-    int32_t *blkcnt;    // [3][nblk]
+    int32_t *blkcnt;    // [kClasses][nblk]
     int64_t nblk;
 };
 
@@ -104,7 +114,7 @@ struct ReorderArgs {
     float denom;        // fl(256 n)
     int64_t J;
     const Ctrl *ctrl;
-    int32_t *blkcnt;    // [3][nblk] counts in, offsets out (scan)
+    int32_t *blkcnt;    // [kClasses][nblk] counts in, offsets out (scan)
     int64_t nblk;
     int32_t *perm, *inv;
     float *mu_stream;
@@ -132,7 +142,10 @@ hipError_t launch_stats(const StatsArgs &a, int f32, hipStream_t s);
 hipError_t launch_alloc_pass(const AllocArgs &a, int pass, hipStream_t s);
 hipError_t launch_alloc_final(const AllocArgs &a, hipStream_t s);
 hipError_t launch_reorder(const ReorderArgs &a, hipStream_t s);
-hipError_t launch_codec(const CodecArgs &a, int mode, int local, int64_t max_sg, hipStream_t s);
+// wide: the plan has the 16-bit class (kernels with its code path)
+hipError_t launch_codec(const CodecArgs &a, int mode, int local, int64_t max_sg, bool wide, hipStream_t s);
+// the 16-bit class's level and weight tables (65,536 each) for level shape eps
+hipError_t launch_build_tables16(float *L16, float *W16, double eps, hipStream_t s);
 // part table for the schedule of n workers: ring entry c = part c of n;
 // butterfly entry (m - 2) + c = part c of m for m = 2, 4, .., n; n = 1: one entry
 int32_t part_table_entries(int32_t n, int32_t topology);

@@ -174,6 +174,45 @@ __device__ __forceinline__ uint32_t search_levels(float v, const uint8_t *est_ta
     return r;
 }
 
+// 16-bit search over the 65,536 levels in the workspace: r = the largest
+// r <= 65534 with L[r] <= v (v already clamped to [-1, 1], so L[0] = -1 <= v).
+// First guess from the closed form of the levels, |v| = t (eps + (1 - eps) t)
+// and u = (2 r + 1 - Q) / (Q - 1), i.e. r = floor((u + 1) (Q - 1) / 2); then
+// steps of one level until L[r] <= v < L[r+1]; a bisection in the (never
+// expected) case that 32 steps do not settle it.
+__device__ __forceinline__ uint32_t search_levels16(float v, const float *L, const float *W, float eps,
+                                                    float &Lr, float &Wr) {
+    const float av = fabsf(v), ce = 1.0f - eps;
+    const float t = ce > 0.0f ? (sqrtf(eps * eps + 4.0f * ce * av) - eps) / (2.0f * ce) : av;
+    const float u = v < 0.0f ? -t : t;
+    int r = (int)floorf((u + 1.0f) * 32767.5f);
+    r = min(max(r, 0), 65534);
+    int it = 0;
+    for (; it < 32; it++) {
+        if (r < 65534 && L[r + 1] <= v) {
+            r++;
+            continue;
+        }
+        if (r > 0 && L[r] > v) {
+            r--;
+            continue;
+        }
+        break;
+    }
+    if (it == 32) {
+        int lo = 0, hi = 65534;
+        while (lo < hi) {
+            const int mid = lo + (hi - lo + 1) / 2;
+            if (L[mid] <= v) lo = mid;
+            else hi = mid - 1;
+        }
+        r = lo;
+    }
+    Lr = L[r];
+    Wr = W[r];
+    return (uint32_t)r;
+}
+
 // 2-bit search: two compares against the inner levels c1 = L[1], c2 = L[2]
 __device__ __forceinline__ uint32_t search_levels2(float v, float c1, float c2, const Pair *lw,
                                                    float &Lr, float &Wr) {
@@ -194,7 +233,7 @@ __device__ __forceinline__ void part_info(const unsigned long long *C, int64_t m
     int64_t base = 0, off = 0;
     p.N = 0;
 #pragma unroll
-    for (int k = 0; k < 3; k++) {
+    for (int k = 0; k < kClasses; k++) {
         const int64_t Ck = (int64_t)C[k];
         const int64_t a = c * Ck / m, b = (c + 1) * Ck / m;
         p.lo[k] = base + a;
@@ -204,7 +243,7 @@ __device__ __forceinline__ void part_info(const unsigned long long *C, int64_t m
         base += Ck;
     }
 #pragma unroll
-    for (int k = 0; k < 3; k++) {
+    for (int k = 0; k < kClasses; k++) {
         p.offc[k] = off;
         off += p.cnt[k] * 32 * (2 << k);
     }
@@ -217,18 +256,21 @@ __device__ __forceinline__ void part_info(const unsigned long long *C, int64_t m
 }
 
 
+// level of a code; the 16-bit class reads its 65,536 levels from the
+// workspace (L2-resident), the others from the block's LDS tables
 template <int B>
-__device__ __forceinline__ float level_of(const SharedTables &T, uint32_t code) {
+__device__ __forceinline__ float level_of(const SharedTables &T, const float *L16, uint32_t code) {
     if constexpr (B == 2) return T.dec2[code];
     else if constexpr (B == 4) return T.dec4[code];
-    else return T.dec8[code];
+    else if constexpr (B == 8) return T.dec8[code];
+    else return L16[code];
 }
 
 // x[i] = fl(sigma * L[code i]) for the 16 codes of one group.  2- and 4-bit
 // codes are looked up a byte at a time (four or two levels per LDS read).
 template <int B>
 __device__ __forceinline__ void decode_codes(const uint32_t (&w)[B / 2], float sigma, const SharedTables &T,
-                                             float (&x)[16]) {
+                                             const float *L16, float (&x)[16]) {
     if constexpr (B == 2) {
 #pragma unroll
         for (int k = 0; k < 4; k++) {
@@ -245,16 +287,23 @@ __device__ __forceinline__ void decode_codes(const uint32_t (&w)[B / 2], float s
             x[2 * k] = sigma * l.x;
             x[2 * k + 1] = sigma * l.y;
         }
-    } else {
+    } else if constexpr (B == 8) {
 #pragma unroll
         for (int i = 0; i < 16; i++) x[i] = sigma * T.dec8[(w[i >> 2] >> (8 * (i & 3))) & 0xFFu];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; i++) x[i] = sigma * L16[(w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu];
     }
 }
 
 // load / store the 2B bytes of one group's codes (B = bits per code)
 template <int B>
 __device__ __forceinline__ void load_codes(const uint8_t *p, uint32_t (&w)[B / 2]) {
-    if constexpr (B == 8) {
+    if constexpr (B == 16) {
+        const uint4 v0 = reinterpret_cast<const uint4 *>(p)[0], v1 = reinterpret_cast<const uint4 *>(p)[1];
+        w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
+        w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
+    } else if constexpr (B == 8) {
         const uint4 v = *reinterpret_cast<const uint4 *>(p);
         w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
     } else if constexpr (B == 4) {
@@ -267,7 +316,10 @@ __device__ __forceinline__ void load_codes(const uint8_t *p, uint32_t (&w)[B / 2
 
 template <int B>
 __device__ __forceinline__ void store_codes(uint8_t *p, const uint32_t (&w)[B / 2]) {
-    if constexpr (B == 8) {
+    if constexpr (B == 16) {
+        reinterpret_cast<uint4 *>(p)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        reinterpret_cast<uint4 *>(p)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    } else if constexpr (B == 8) {
         *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
     } else if constexpr (B == 4) {
         *reinterpret_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
@@ -280,14 +332,14 @@ __device__ __forceinline__ void store_codes(uint8_t *p, const uint32_t (&w)[B / 
 // values (a part holds fewer than 2^31 super-groups), so that a launch keeps
 // a dozen scalar registers of layout instead of the whole 64-bit PartInfo.
 struct PartU32 {
-    uint32_t lo[3];    // first stream position of each class
-    uint32_t pre[3];   // part-local index of each class's first super-group
+    uint32_t lo[kClasses];    // first stream position of each class
+    uint32_t pre[kClasses];   // part-local index of each class's first super-group
 };
 
 __device__ __forceinline__ PartU32 part_u32(const PartInfo &P) {
     PartU32 q;
 #pragma unroll
-    for (int k = 0; k < 3; k++) {
+    for (int k = 0; k < kClasses; k++) {
         q.lo[k] = (uint32_t)P.lo[k];
         q.pre[k] = (uint32_t)P.pre[k];
     }
@@ -297,14 +349,14 @@ __device__ __forceinline__ PartU32 part_u32(const PartInfo &P) {
 // Region pointers of one part, split by class (uniform over a launch).  Offsets
 // added to them are 32-bit: the host keeps every region below 4 GB.
 struct RegionBase {
-    const uint8_t *codes[3];   // codes of class k
+    const uint8_t *codes[kClasses];   // codes of class k
     const uint8_t *s;          // fp32 scale units
     const uint8_t *g;          // UINT8 group codes
 };
 
 __device__ __forceinline__ RegionBase region_base(const uint8_t *r, const PartInfo &P) {
     RegionBase b;
-    for (int k = 0; k < 3; k++) b.codes[k] = r + P.offc[k];
+    for (int k = 0; k < kClasses; k++) b.codes[k] = r + P.offc[k];
     b.s = r + P.offs;
     b.g = r + P.offg;
     return b;
@@ -314,13 +366,13 @@ __device__ __forceinline__ RegionBase region_base(const uint8_t *r, const PartIn
 // class-local index idx of class K (B = bits per code)
 template <int B, int K>
 __device__ __forceinline__ void decode_group(const RegionBase &R, uint32_t t, uint32_t idx, int g,
-                                             const SharedTables &T, float (&x)[16]) {
+                                             const SharedTables &T, const float *L16, float (&x)[16]) {
     uint32_t w[B / 2];
     load_codes<B>(R.codes[K] + (idx * (32u * B) + (uint32_t)g * (2u * B)), w);
     const float s = *reinterpret_cast<const float *>(R.s + 4u * t);
     const uint32_t c = R.g[16u * t + (uint32_t)g];
     const float sigma = (float)c * s;
-    decode_codes<B>(w, sigma, T, x);
+    decode_codes<B>(w, sigma, T, L16, x);
 }
 
 // ---------------------------------------------------------------------------
@@ -347,7 +399,7 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartU32 &Po, 
                                          const RegionBase &Out, uint32_t t, uint32_t j, float mu,
                                          uint32_t pos_next, uint32_t *slot_j, float *slot_mu, int g,
                                          const SharedTables &T, float *stage_row) {
-    constexpr int K = Q == 2 ? 0 : (Q == 4 ? 1 : 2);
+    constexpr int K = Q == 2 ? 0 : (Q == 4 ? 1 : (Q == 8 ? 2 : 3));
     const uint32_t idx = t - (uint32_t)Po.pre[K];        // index in the class, output part
     const uint32_t pos = (uint32_t)Po.lo[K] + idx;       // stream position
     const uint32_t idx_in = pos - (uint32_t)Pi.lo[K];    // index in the class, input part
@@ -358,7 +410,7 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartU32 &Po, 
     }
     float y[16];
 
-    if constexpr (MODE != kCompress) decode_group<Q, K>(In, t_in, idx_in, g, T, y);
+    if constexpr (MODE != kCompress) decode_group<Q, K>(In, t_in, idx_in, g, T, a.L16, y);
 
     if constexpr (LOCAL == kLocalBF16) {
         const uint4 *src = reinterpret_cast<const uint4 *>(
@@ -391,7 +443,7 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartU32 &Po, 
         }
     } else if constexpr (LOCAL == kLocalPacked) {
         float own[16];
-        decode_group<Q, K>(Own, t_in, idx_in, g, T, own);
+        decode_group<Q, K>(Own, t_in, idx_in, g, T, a.L16, own);
 #pragma unroll
         for (int i = 0; i < 16; i++) y[i] = y[i] + own[i];
     } else if constexpr (LOCAL == kLocalPartial) {
@@ -474,12 +526,17 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartU32 &Po, 
             // same, P(+1) >= 65535.99 > any d + 0.5 so rounding up stays
             // certain, and P < 0 below -1 keeps rounding down certain.  The
             // clamp is therefore left out.
-            const float v = y[i] * inv;
+            float v = y[i] * inv;
             float Lr, Wr;
             uint32_t r;
             if constexpr (Q == 2) r = search_levels2(v, c1, c2, T.lw2, Lr, Wr);
             else if constexpr (Q == 4) r = search_levels<16>(v, T.b4, T.cl4, T.lw4, Lr, Wr);
-            else r = search_levels<256>(v, T.b8, T.cl8, T.lw8, Lr, Wr);
+            else if constexpr (Q == 8) r = search_levels<256>(v, T.b8, T.cl8, T.lw8, Lr, Wr);
+            else {
+                // the clamp of the definition, kept for the 16-bit class
+                v = v < -1.0f ? -1.0f : (v > 1.0f ? 1.0f : v);
+                r = search_levels16(v, a.L16, a.W16, a.eps, Lr, Wr);
+            }
             const float P = (v - Lr) * Wr;
             const uint32_t dd = (ii & 1) ? (d[ii >> 1] >> 16) : (d[ii >> 1] & 0xFFFFu);
             const uint32_t code = r + (((float)dd + 0.5f) < P ? 1u : 0u);
@@ -506,7 +563,7 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartU32 &Po, 
             for (int ii = 0; ii < 4; ii++) {
                 const int i = 4 * v + ii;
                 const uint32_t code = (w[(i * Q) / 32] >> ((i * Q) % 32)) & ((1u << Q) - 1u);
-                x[ii] = sigma * level_of<Q>(T, code) + add;
+                x[ii] = sigma * level_of<Q>(T, a.L16, code) + add;
             }
             stage[4 * g + v] = f32x4_t{x[0], x[1], x[2], x[3]};
         }
@@ -538,7 +595,9 @@ struct CodecShape {
     static constexpr int waves_per_simd = blocks_per_cu * threads / 256;   // 4 SIMDs per CU
 };
 
-template <int MODE, int LOCAL>
+// WIDE: the plan has the 16-bit class (a fourth class after the 8-bit one);
+// the default kernels are built without its code path.
+template <int MODE, int LOCAL, bool WIDE>
 __global__ __launch_bounds__((CodecShape<MODE, LOCAL>::threads))
 __attribute__((amdgpu_waves_per_eu(CodecShape<MODE, LOCAL>::waves_per_simd)))
 void k_codec(CodecArgs a) {
@@ -561,6 +620,7 @@ void k_codec(CodecArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane & 15, row = lane >> 4;
     const uint32_t N = (uint32_t)Po.N, pre1 = (uint32_t)Po.pre[1], pre2 = (uint32_t)Po.pre[2];
+    const uint32_t pre3 = WIDE ? (uint32_t)Po.pre[3] : N;
     // the fused final hop stages each row's decoded super-group here
     constexpr int kStageRows = MODE == kHopFinal ? kThreads / 16 : 1;
     __shared__ __align__(16) float stage[kStageRows][kSG];
@@ -574,8 +634,10 @@ void k_codec(CodecArgs a) {
     // (selects, not an index into Po's arrays: a runtime index would put the
     // part layout in scratch memory)
     const uint32_t lo0 = (uint32_t)Po.lo[0], lo1 = (uint32_t)Po.lo[1], lo2 = (uint32_t)Po.lo[2];
+    const uint32_t lo3 = WIDE ? (uint32_t)Po.lo[3] : 0u;
     auto pos_of = [&](uint32_t tt) -> uint32_t {
-        return tt < pre1 ? lo0 + tt : (tt < pre2 ? lo1 + (tt - pre1) : lo2 + (tt - pre2));
+        return tt < pre1 ? lo0 + tt
+                         : (tt < pre2 ? lo1 + (tt - pre1) : (tt < pre3 ? lo2 + (tt - pre2) : lo3 + (tt - pre3)));
     };
     const uint32_t stride = gridDim.x * kSGPerBlock;
     constexpr bool kAhead = codec_ahead<MODE, LOCAL>();
@@ -604,7 +666,9 @@ void k_codec(CodecArgs a) {
         }
         if (t < pre1) codec_sg<2, MODE, LOCAL>(a, po, pi, In, Own, Out, t, j, mu, pn, slot_j, slot_mu, g, T, stage_row);
         else if (t < pre2) codec_sg<4, MODE, LOCAL>(a, po, pi, In, Own, Out, t, j, mu, pn, slot_j, slot_mu, g, T, stage_row);
-        else codec_sg<8, MODE, LOCAL>(a, po, pi, In, Own, Out, t, j, mu, pn, slot_j, slot_mu, g, T, stage_row);
+        else if (t < pre3) codec_sg<8, MODE, LOCAL>(a, po, pi, In, Own, Out, t, j, mu, pn, slot_j, slot_mu, g, T, stage_row);
+        else if constexpr (WIDE)
+            codec_sg<16, MODE, LOCAL>(a, po, pi, In, Own, Out, t, j, mu, pn, slot_j, slot_mu, g, T, stage_row);
     }
 }
 
@@ -618,7 +682,7 @@ void k_codec(CodecArgs a) {
 template <int Q>
 __device__ __forceinline__ void finalize_sg(const CodecArgs &a, const PartInfo &P, int64_t t,
                                             int g, const SharedTables &T) {
-    constexpr int K = Q == 2 ? 0 : (Q == 4 ? 1 : 2);
+    constexpr int K = Q == 2 ? 0 : (Q == 4 ? 1 : (Q == 8 ? 2 : 3));
     const int64_t idx = t - P.pre[K];
     const int64_t pos = P.lo[K] + idx;
     const int64_t j = a.perm[pos];
@@ -636,15 +700,16 @@ __device__ __forceinline__ void finalize_sg(const CodecArgs &a, const PartInfo &
         const uint32_t c = (cgw[v] >> shift) & 0xFFu;
         const float sigma = (float)c * s;
         const int c0 = 64 * v + 4 * g;                  // first coordinate of the piece
-        uint32_t w;
-        if constexpr (Q == 8) w = *reinterpret_cast<const uint32_t *>(codes + c0);
+        uint64_t w;
+        if constexpr (Q == 16) w = *reinterpret_cast<const unsigned long long *>(codes + 2 * c0);
+        else if constexpr (Q == 8) w = *reinterpret_cast<const uint32_t *>(codes + c0);
         else if constexpr (Q == 4) w = *reinterpret_cast<const uint16_t *>(codes + c0 / 2);
         else w = codes[c0 / 4];
         float x[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const uint32_t code = (w >> (i * Q)) & ((1u << Q) - 1u);
-            x[i] = sigma * level_of<Q>(T, code) + add;
+            const uint32_t code = (uint32_t)(w >> (i * Q)) & ((1u << Q) - 1u);
+            x[i] = sigma * level_of<Q>(T, a.L16, code) + add;
         }
         // the output is written once and not read back here: non-temporal
         const f32x4_t xv = {x[0], x[1], x[2], x[3]};
@@ -652,6 +717,7 @@ __device__ __forceinline__ void finalize_sg(const CodecArgs &a, const PartInfo &
     }
 }
 
+template <bool WIDE>
 __global__ __launch_bounds__(256) void k_finalize(CodecArgs a) {
     __shared__ __align__(16) SharedTables T;
     const LevelTables &lev = a.tab->lev;
@@ -668,7 +734,8 @@ __global__ __launch_bounds__(256) void k_finalize(CodecArgs a) {
         if (t >= P.N) continue;
         if (t < P.pre[1]) finalize_sg<2>(a, P, t, g, T);
         else if (t < P.pre[2]) finalize_sg<4>(a, P, t, g, T);
-        else finalize_sg<8>(a, P, t, g, T);
+        else if (!WIDE || t < P.pre[3]) finalize_sg<8>(a, P, t, g, T);
+        else if constexpr (WIDE) finalize_sg<16>(a, P, t, g, T);
     }
 }
 
@@ -875,6 +942,13 @@ __device__ __forceinline__ float alloc_key(const AllocArgs &a, float F, float su
     return g < 0.0f ? 0.0f : g;
 }
 
+// Threshold multipliers T = fl(K rho): widths {2,4,8} K24 = 544, K48 = 16384;
+// with the 16-bit class the chain is scaled by 257 so that T48 / T816 =
+// 257 / 2^17 stays exact: K24 = 139808, K48 = 4210688, K816 = 2^31.
+__device__ __forceinline__ float k24(int wide) { return wide ? 139808.0f : 544.0f; }
+__device__ __forceinline__ float k48(int wide) { return wide ? 4210688.0f : 16384.0f; }
+constexpr float kK816 = 2147483648.0f;
+
 // number of entries of the non-decreasing t[0..n) that are <= F
 __device__ __forceinline__ uint32_t count_le(const float *t, int n, float F) {
     uint32_t lo = 0, len = (uint32_t)n;
@@ -896,24 +970,27 @@ __device__ __forceinline__ uint32_t count_le(const float *t, int n, float F) {
 __global__ __launch_bounds__(256) void k_alloc_count(AllocArgs a, int pass) {
     Ctrl *c = a.ctrl;
     if (c->done) return;
-    __shared__ float t4[kRadixCand], t8[kRadixCand];
-    __shared__ unsigned int h4[kRadixCand + 1], h8[kRadixCand + 1];
+    __shared__ float t4[kRadixCand], t8[kRadixCand], t16[kRadixCand];
+    __shared__ unsigned int h4[kRadixCand + 1], h8[kRadixCand + 1], h16[kRadixCand + 1];
     const int n = radix_ncand(pass), shift = radix_shift(pass);
     const uint32_t prefix = c->prefix;
     for (int i = threadIdx.x; i < kRadixCand + 1; i += blockDim.x) {
         h4[i] = 0u;
         h8[i] = 0u;
+        h16[i] = 0u;
     }
     if (threadIdx.x < n) {
         const float rho = __uint_as_float(prefix + ((uint32_t)threadIdx.x << shift));
-        t4[threadIdx.x] = 544.0f * rho;
-        t8[threadIdx.x] = 16384.0f * rho;
+        t4[threadIdx.x] = k24(a.wide) * rho;
+        t8[threadIdx.x] = k48(a.wide) * rho;
+        t16[threadIdx.x] = kK816 * rho;
     }
     __syncthreads();
     // count 0 adds to no suffix sum and is skipped; count n (F at or above
     // every candidate threshold) is kept in a register
     const float lo4 = t4[0], hi4 = t4[n - 1], lo8 = t8[0], hi8 = t8[n - 1];
-    uint32_t top4 = 0u, top8 = 0u;
+    const float lo16 = t16[0], hi16 = t16[n - 1];
+    uint32_t top4 = 0u, top8 = 0u, top16 = 0u;
     for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < a.J;
          j += (int64_t)gridDim.x * blockDim.x) {
         const float F = alloc_key(a, a.sumsq[j], a.mode == kAllocMeanCorrected ? a.sum[j] : 0.0f);
@@ -921,20 +998,27 @@ __global__ __launch_bounds__(256) void k_alloc_count(AllocArgs a, int pass) {
         else if (F >= lo4) atomicAdd(&h4[count_le(t4, n, F)], 1u);
         if (F >= hi8) top8++;
         else if (F >= lo8) atomicAdd(&h8[count_le(t8, n, F)], 1u);
+        if (a.wide) {
+            if (F >= hi16) top16++;
+            else if (F >= lo16) atomicAdd(&h16[count_le(t16, n, F)], 1u);
+        }
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) {
         top4 += __shfl_xor(top4, d, 64);
         top8 += __shfl_xor(top8, d, 64);
+        top16 += __shfl_xor(top16, d, 64);
     }
     if ((threadIdx.x & 63) == 0) {
         if (top4) atomicAdd(&h4[n], top4);
         if (top8) atomicAdd(&h8[n], top8);
+        if (top16) atomicAdd(&h16[n], top16);
     }
     __syncthreads();
     for (int i = threadIdx.x; i < n + 1; i += blockDim.x) {
         if (h4[i]) atomicAdd(&c->hist4[i], h4[i]);
         if (h8[i]) atomicAdd(&c->hist8[i], h8[i]);
+        if (h16[i]) atomicAdd(&c->hist16[i], h16[i]);
     }
 }
 
@@ -944,25 +1028,30 @@ __global__ __launch_bounds__(256) void k_alloc_count(AllocArgs a, int pass) {
 __global__ __launch_bounds__(256) void k_alloc_decide(AllocArgs a, int pass) {
     Ctrl *c = a.ctrl;
     if (c->done) return;
-    __shared__ unsigned long long s4[kRadixCand], s8[kRadixCand];
+    __shared__ unsigned long long s4[kRadixCand], s8[kRadixCand], s16[kRadixCand];
     __shared__ int first;
     const int n = radix_ncand(pass), shift = radix_shift(pass);
     const int t = threadIdx.x;
     // s[t] starts as hist[t + 1]; after the scan s[t] = #{j : i_j > t}
     s4[t] = t < n ? c->hist4[t + 1] : 0ull;
     s8[t] = t < n ? c->hist8[t + 1] : 0ull;
+    s16[t] = t < n ? c->hist16[t + 1] : 0ull;
     if (t == 0) first = n;
     __syncthreads();
     for (int d = 1; d < kRadixCand; d <<= 1) {
         const unsigned long long v4 = t + d < kRadixCand ? s4[t + d] : 0ull;
         const unsigned long long v8 = t + d < kRadixCand ? s8[t + d] : 0ull;
+        const unsigned long long v16 = t + d < kRadixCand ? s16[t + d] : 0ull;
         __syncthreads();
         s4[t] += v4;
         s8[t] += v8;
+        s16[t] += v16;
         __syncthreads();
     }
     if (t < n) {
-        const long long total = 2 * (long long)a.J + 2 * (long long)s4[t] + 4 * (long long)s8[t];
+        // 2 bits each, +2 at 4 bits, +4 more at 8, +8 more at 16
+        const long long total = 2 * (long long)a.J + 2 * (long long)s4[t] + 4 * (long long)s8[t] +
+                                8 * (long long)s16[t];
         if (total <= a.budget) atomicMin(&first, t);
     }
     __syncthreads();
@@ -982,6 +1071,7 @@ __global__ __launch_bounds__(256) void k_alloc_decide(AllocArgs a, int pass) {
     for (int i = t; i < kRadixCand + 1; i += blockDim.x) {
         c->hist4[i] = 0u;
         c->hist8[i] = 0u;
+        c->hist16[i] = 0u;
     }
 }
 
@@ -992,8 +1082,9 @@ __global__ __launch_bounds__(256) void k_alloc_final(AllocArgs a) {
     // the uniform variant has no scalar (block 0 stores NaN below, nobody reads it)
     const uint32_t rb = uniform ? 0u : c->rho_bits;
     const float rho = __uint_as_float(rb);
-    const float t4 = 544.0f * rho, t8 = 16384.0f * rho;
-    uint32_t cnt[3] = {0u, 0u, 0u};
+    const float t4 = k24(a.wide) * rho, t8 = k48(a.wide) * rho;
+    const float t16 = a.wide ? kK816 * rho : __builtin_huge_valf();
+    uint32_t cnt[kClasses] = {0u, 0u, 0u, 0u};
     const int64_t j0 = (int64_t)blockIdx.x * kReorderSGPerBlock + threadIdx.x * 4;
     if (j0 + 4 <= a.J) {
         // the arrays are 256-byte aligned in the workspace and j0 is a multiple of 4
@@ -1005,7 +1096,7 @@ __global__ __launch_bounds__(256) void k_alloc_final(AllocArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const float G = alloc_key(a, F[i], S[i]);
-            const int k = uniform ? a.uniform_k : (G >= t8 ? 2 : (G >= t4 ? 1 : 0));
+            const int k = uniform ? a.uniform_k : (G >= t16 ? 3 : (G >= t8 ? 2 : (G >= t4 ? 1 : 0)));
             w |= (2u << k) << (8 * i);
             cnt[k]++;
         }
@@ -1013,42 +1104,42 @@ __global__ __launch_bounds__(256) void k_alloc_final(AllocArgs a) {
     } else {
         for (int64_t j = j0; j < a.J; j++) {
             const float G = alloc_key(a, a.sumsq[j], centred ? a.sum[j] : 0.0f);
-            const int k = uniform ? a.uniform_k : (G >= t8 ? 2 : (G >= t4 ? 1 : 0));
+            const int k = uniform ? a.uniform_k : (G >= t16 ? 3 : (G >= t8 ? 2 : (G >= t4 ? 1 : 0)));
             a.widths[j] = (uint8_t)(2 << k);
             cnt[k]++;
         }
     }
     if (uniform && blockIdx.x == 0 && threadIdx.x == 0) c->rho_bits = 0x7FC00000u;
-    // pack three counts (each <= 1024) into 16-bit fields and reduce
+    // pack four counts (each <= 1024) into 16-bit fields and reduce
     unsigned long long v = (unsigned long long)cnt[0] | ((unsigned long long)cnt[1] << 16) |
-                           ((unsigned long long)cnt[2] << 32);
+                           ((unsigned long long)cnt[2] << 32) | ((unsigned long long)cnt[3] << 48);
     const unsigned long long tot = block_sum_u64(v);
     if (threadIdx.x == 0) {
 #pragma unroll
-        for (int k = 0; k < 3; k++)
+        for (int k = 0; k < kClasses; k++)
             a.blkcnt[k * a.nblk + blockIdx.x] = (int32_t)((tot >> (16 * k)) & 0xFFFFu);
     }
 }
 
 // Class totals from the per-block counts (one block; no contended atomics).
 __global__ __launch_bounds__(1024) void k_alloc_totals(AllocArgs a) {
-    __shared__ unsigned long long part[16][3];
-    unsigned long long s[3] = {0ull, 0ull, 0ull};
+    __shared__ unsigned long long part[16][kClasses];
+    unsigned long long s[kClasses] = {0ull, 0ull, 0ull, 0ull};
     for (int64_t b = threadIdx.x; b < a.nblk; b += blockDim.x) {
 #pragma unroll
-        for (int k = 0; k < 3; k++) s[k] += (unsigned long long)a.blkcnt[k * a.nblk + b];
+        for (int k = 0; k < kClasses; k++) s[k] += (unsigned long long)a.blkcnt[k * a.nblk + b];
     }
 #pragma unroll
-    for (int k = 0; k < 3; k++) {
+    for (int k = 0; k < kClasses; k++) {
 #pragma unroll
         for (int d = 32; d >= 1; d >>= 1) s[k] += __shfl_xor(s[k], d, 64);
     }
     if ((threadIdx.x & 63) == 0) {
 #pragma unroll
-        for (int k = 0; k < 3; k++) part[threadIdx.x >> 6][k] = s[k];
+        for (int k = 0; k < kClasses; k++) part[threadIdx.x >> 6][k] = s[k];
     }
     __syncthreads();
-    if (threadIdx.x < 3) {
+    if (threadIdx.x < kClasses) {
         unsigned long long t = 0ull;
         for (int w = 0; w < (int)(blockDim.x >> 6); w++) t += part[w][threadIdx.x];
         a.ctrl->class_counts[threadIdx.x] = t;
@@ -1061,7 +1152,7 @@ __global__ __launch_bounds__(1024) void k_reorder_scan(ReorderArgs a) {
     const int64_t per = (nb + 1023) / 1024;
     const int64_t b0 = threadIdx.x * per, b1 = min(nb, b0 + per);
     int64_t base = 0;
-    for (int k = 0; k < 3; k++) {
+    for (int k = 0; k < kClasses; k++) {
         int64_t mine = 0;
         for (int64_t b = b0; b < b1; b++) mine += a.blkcnt[k * nb + b];
         sh[threadIdx.x] = mine;
@@ -1088,19 +1179,19 @@ __global__ __launch_bounds__(256) void k_reorder_scatter(ReorderArgs a) {
     __shared__ unsigned long long wtot[4];
     const int64_t j0 = (int64_t)blockIdx.x * kReorderSGPerBlock + threadIdx.x * 4;
     int k_of[4];
-    uint32_t cnt[3] = {0u, 0u, 0u};
+    uint32_t cnt[kClasses] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const int64_t j = j0 + i;
         k_of[i] = -1;
         if (j < a.J) {
             const uint8_t q = a.widths[j];
-            k_of[i] = q == 2 ? 0 : (q == 4 ? 1 : 2);
+            k_of[i] = q == 2 ? 0 : (q == 4 ? 1 : (q == 8 ? 2 : 3));
             cnt[k_of[i]]++;
         }
     }
     const unsigned long long mine = (unsigned long long)cnt[0] | ((unsigned long long)cnt[1] << 16) |
-                                    ((unsigned long long)cnt[2] << 32);
+                                    ((unsigned long long)cnt[2] << 32) | ((unsigned long long)cnt[3] << 48);
     // inclusive scan inside the wave
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     unsigned long long inc = mine;
@@ -1114,9 +1205,9 @@ __global__ __launch_bounds__(256) void k_reorder_scatter(ReorderArgs a) {
     unsigned long long before = 0;
     for (int w = 0; w < wave; w++) before += wtot[w];
     unsigned long long excl = before + inc - mine;
-    int32_t pos[3];
+    int32_t pos[kClasses];
 #pragma unroll
-    for (int k = 0; k < 3; k++)
+    for (int k = 0; k < kClasses; k++)
         pos[k] = a.blkcnt[k * a.nblk + blockIdx.x] + (int32_t)((excl >> (16 * k)) & 0xFFFFu);
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -1415,6 +1506,21 @@ __global__ __launch_bounds__(256) void k_build_tables(DeviceTables *t, double ep
     }
 }
 
+// the 16-bit class: L[r] and W[r] = fl32(65536 / (L[r+1] - L[r])) for
+// r < 65,536, from the same fp64 definitions as the narrower classes (W[65535]
+// is unused and set to 0)
+__global__ __launch_bounds__(256) void k_build_tables16(float *L16, float *W16, double eps) {
+    for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < 65536; r += gridDim.x * blockDim.x) {
+        L16[r] = level_f(r, 65536, eps);
+        W16[r] = r < 65535 ? weight_f(r, 65536, eps) : 0.0f;
+    }
+}
+
+hipError_t launch_build_tables16(float *L16, float *W16, double eps, hipStream_t s) {
+    hipLaunchKernelGGL(k_build_tables16, dim3(256), dim3(256), 0, s, L16, W16, eps);
+    return hipGetLastError();
+}
+
 hipError_t launch_build_tables(DeviceTables *t, double eps, hipStream_t s) {
     hipLaunchKernelGGL(k_build_tables, dim3(1), dim3(256), 0, s, t, eps);
     return hipGetLastError();
@@ -1548,31 +1654,38 @@ static dim3 codec_grid(int64_t n, int64_t blocks_per_cu, int64_t sg_per_block) {
     return dim3(grid_for(n, sg_per_block, wave * waves));
 }
 
-template <int MODE, int LOCAL>
-static hipError_t launch_codec_t(const CodecArgs &a, int64_t max_sg, hipStream_t s) {
+template <int MODE, int LOCAL, bool WIDE>
+static hipError_t launch_codec_w(const CodecArgs &a, int64_t max_sg, hipStream_t s) {
     using Shape = CodecShape<MODE, LOCAL>;
-    hipLaunchKernelGGL((k_codec<MODE, LOCAL>), codec_grid(max_sg, Shape::blocks_per_cu, Shape::sg_per_block),
+    hipLaunchKernelGGL((k_codec<MODE, LOCAL, WIDE>), codec_grid(max_sg, Shape::blocks_per_cu, Shape::sg_per_block),
                        dim3(Shape::threads), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_codec(const CodecArgs &a, int mode, int local, int64_t max_sg, hipStream_t s) {
-    if (mode == kCompress && local == kLocalBF16) return launch_codec_t<kCompress, kLocalBF16>(a, max_sg, s);
-    if (mode == kCompress && local == kLocalF32) return launch_codec_t<kCompress, kLocalF32>(a, max_sg, s);
-    if (mode == kHop && local == kLocalBF16) return launch_codec_t<kHop, kLocalBF16>(a, max_sg, s);
-    if (mode == kHop && local == kLocalF32) return launch_codec_t<kHop, kLocalF32>(a, max_sg, s);
-    if (mode == kHop && local == kLocalPacked) return launch_codec_t<kHop, kLocalPacked>(a, max_sg, s);
-    if (mode == kHop && local == kLocalPartial) return launch_codec_t<kHop, kLocalPartial>(a, max_sg, s);
-    if (mode == kPartial && local == kLocalBF16) return launch_codec_t<kPartial, kLocalBF16>(a, max_sg, s);
-    if (mode == kPartial && local == kLocalF32) return launch_codec_t<kPartial, kLocalF32>(a, max_sg, s);
-    if (mode == kPartial && local == kLocalPartial) return launch_codec_t<kPartial, kLocalPartial>(a, max_sg, s);
-    if (mode == kHopFinal && local == kLocalBF16) return launch_codec_t<kHopFinal, kLocalBF16>(a, max_sg, s);
-    if (mode == kHopFinal && local == kLocalF32) return launch_codec_t<kHopFinal, kLocalF32>(a, max_sg, s);
-    if (mode == kHopFinal && local == kLocalPacked) return launch_codec_t<kHopFinal, kLocalPacked>(a, max_sg, s);
-    if (mode == kHopFinal && local == kLocalPartial) return launch_codec_t<kHopFinal, kLocalPartial>(a, max_sg, s);
+template <int MODE, int LOCAL>
+static hipError_t launch_codec_t(const CodecArgs &a, int64_t max_sg, bool wide, hipStream_t s) {
+    return wide ? launch_codec_w<MODE, LOCAL, true>(a, max_sg, s) : launch_codec_w<MODE, LOCAL, false>(a, max_sg, s);
+}
+
+hipError_t launch_codec(const CodecArgs &a, int mode, int local, int64_t max_sg, bool w, hipStream_t s) {
+    if (mode == kCompress && local == kLocalBF16) return launch_codec_t<kCompress, kLocalBF16>(a, max_sg, w, s);
+    if (mode == kCompress && local == kLocalF32) return launch_codec_t<kCompress, kLocalF32>(a, max_sg, w, s);
+    if (mode == kHop && local == kLocalBF16) return launch_codec_t<kHop, kLocalBF16>(a, max_sg, w, s);
+    if (mode == kHop && local == kLocalF32) return launch_codec_t<kHop, kLocalF32>(a, max_sg, w, s);
+    if (mode == kHop && local == kLocalPacked) return launch_codec_t<kHop, kLocalPacked>(a, max_sg, w, s);
+    if (mode == kHop && local == kLocalPartial) return launch_codec_t<kHop, kLocalPartial>(a, max_sg, w, s);
+    if (mode == kPartial && local == kLocalBF16) return launch_codec_t<kPartial, kLocalBF16>(a, max_sg, w, s);
+    if (mode == kPartial && local == kLocalF32) return launch_codec_t<kPartial, kLocalF32>(a, max_sg, w, s);
+    if (mode == kPartial && local == kLocalPartial) return launch_codec_t<kPartial, kLocalPartial>(a, max_sg, w, s);
+    if (mode == kHopFinal && local == kLocalBF16) return launch_codec_t<kHopFinal, kLocalBF16>(a, max_sg, w, s);
+    if (mode == kHopFinal && local == kLocalF32) return launch_codec_t<kHopFinal, kLocalF32>(a, max_sg, w, s);
+    if (mode == kHopFinal && local == kLocalPacked) return launch_codec_t<kHopFinal, kLocalPacked>(a, max_sg, w, s);
+    if (mode == kHopFinal && local == kLocalPartial) return launch_codec_t<kHopFinal, kLocalPartial>(a, max_sg, w, s);
     if (mode == kFinalize) {
         // finalize streams at memory speed: 8 blocks per CU
-        hipLaunchKernelGGL(k_finalize, dim3(grid_for(max_sg, kSGPerBlock, device_cus() * 8)), dim3(256), 0, s, a);
+        const dim3 grid(grid_for(max_sg, kSGPerBlock, device_cus() * 8));
+        if (w) hipLaunchKernelGGL(k_finalize<true>, grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(k_finalize<false>, grid, dim3(256), 0, s, a);
         return hipGetLastError();
     }
     return hipErrorInvalidValue;

@@ -21,6 +21,7 @@ OWN_PACKED, OWN_F32 = 0, 1
 CORRELATED, INDEPENDENT, STRATIFIED = 0, 1, 2
 OPT_SEED, OPT_ROUND, OPT_ROUNDING, OPT_TIMING, OPT_ALLOC, OPT_TIMING_KINDS, OPT_OWN = 0, 1, 2, 3, 4, 5, 6
 OPT_STREAMS = 7
+OPT_MAX_WIDTH = 8
 ALLOC_THRESHOLD, ALLOC_MEAN_CORRECTED, ALLOC_UNIFORM = 0, 1, 2
 MX_FP8_E4M3, MX_FP6_E3M2, MX_FP6_E2M3, MX_FP4_E2M1 = 0, 1, 2, 3
 OPT_EPS = 0   # dq_option_f64
@@ -32,12 +33,13 @@ class dq_info(C.Structure):
     _fields_ = [("rho_bits", C.c_uint32), ("rho", C.c_float), ("t12", C.c_float),
                 ("t24", C.c_float), ("t48", C.c_float), ("class_counts", C.c_int64 * 3),
                 ("budget_bits", C.c_int64), ("used_bits", C.c_int64),
-                ("achieved_bits", C.c_double), ("nonfinite", C.c_int32)]
+                ("achieved_bits", C.c_double), ("nonfinite", C.c_int32), ("t816", C.c_float),
+                ("class_count16", C.c_int64)]
 
 
 class dq_layout(C.Structure):
     _fields_ = [(n, C.c_size_t) for n in ("sum", "sumsq", "widths", "perm", "inv", "mu_stream",
-                                          "tables", "ctrl", "total")]
+                                          "tables", "ctrl", "total", "tables16")]
 
 
 class dq_timing(C.Structure):
@@ -190,7 +192,7 @@ class Plan:
 
     def __init__(self, n_coords, n_workers, topology=RING, avg_bits=5.0, seed=1, rnd=0,
                  rounding=STRATIFIED, device="cuda", timing=False, alloc=ALLOC_THRESHOLD, eps=None,
-                 own=OWN_PACKED, streams=1):
+                 own=OWN_PACKED, streams=1, max_width=8):
         self.d = int(n_coords)
         self.n = int(n_workers)
         self.J = self.d // 256
@@ -209,6 +211,9 @@ class Plan:
         self.set(OPT_TIMING, 1 if timing else 0)
         self.set(OPT_ALLOC, alloc)
         self.set(OPT_OWN, own)
+        self.max_width = int(max_width)
+        if self.max_width != 8:
+            self.set(OPT_MAX_WIDTH, self.max_width)
         if eps is not None:
             _check(lib().dq_plan_set_f64(self.h, OPT_EPS, float(eps)), "dq_plan_set_f64")
         if streams != 1:
@@ -386,8 +391,9 @@ class Plan:
         rc = lib().dq_get_info(self.h, C.byref(i), _stream(stream))
         if rc not in (DQ_OK, DQ_ENONFINITE):
             _check(rc, "dq_get_info")
+        counts = list(i.class_counts) + ([i.class_count16] if self.max_width == 16 else [])
         return {"rho_bits": i.rho_bits, "rho": i.rho, "t12": i.t12, "t24": i.t24, "t48": i.t48,
-                "class_counts": list(i.class_counts), "budget_bits": i.budget_bits,
+                "t816": i.t816, "class_counts": counts, "budget_bits": i.budget_bits,
                 "used_bits": i.used_bits, "achieved_bits": i.achieved_bits,
                 "nonfinite": bool(i.nonfinite), "status": rc}
 

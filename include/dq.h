@@ -141,8 +141,20 @@ typedef enum dq_option {
     DQ_OPT_TIMING_KINDS = 5, /* bit mask of dq_kernel_kind: which launches DQ_OPT_TIMING
                                 times (default all); fewer events, less overhead */
     DQ_OPT_OWN = 6,          /* dq_own (default DQ_OWN_PACKED); set between rounds */
-    DQ_OPT_STREAMS = 7       /* 1 (default) or 2: dq_allreduce runs the independent launches
+    DQ_OPT_STREAMS = 7,      /* 1 (default) or 2: dq_allreduce runs the independent launches
                                 of each schedule step on two streams (see dq_allreduce) */
+    DQ_OPT_MAX_WIDTH = 8     /* 8 (default) or 16: the widest class.  The method's widths
+                                are {2,4,8} (the clamp of the pith.science referee's
+                                minor comment 2); 16 adds the 16-bit class of the threshold
+                                chain of its Fig. 3 caption, T48 = 257/2^17 T816: thresholds
+                                fl(K rho) with K24, K48, K816 = 139808, 4210688, 2^31 (the
+                                544 : 16384 chain scaled by 257, every ratio exact), budget
+                                capped at 16 bits, a fourth width stream and region section
+                                after the 8-bit one (code i at bit 16 i, 532 bytes per
+                                super-group), 65,536 levels of the same closed form in the
+                                workspace.  Changes the workspace size: the plan must be
+                                bound again (dq_workspace_bytes) before its next round.
+                                DQ_EINVAL if the widest region would reach 4 GB. */
 } dq_option;
 
 typedef struct dq_plan dq_plan;
@@ -151,12 +163,15 @@ typedef struct dq_plan dq_plan;
 typedef struct dq_info {
     uint32_t rho_bits;         /* fp32 bit pattern of the scalar rho */
     float rho;
-    float t12, t24, t48;       /* fl(85 rho), fl(544 rho), fl(16384 rho) */
+    float t12, t24, t48;       /* fl(85 rho), fl(544 rho), fl(16384 rho); with the 16-bit
+                                  class fl(21845 rho), fl(139808 rho), fl(4210688 rho) */
     int64_t class_counts[3];   /* super-groups at 2, 4, 8 bits */
     int64_t budget_bits;       /* floor(min(avg_bits, 8) * J) */
     int64_t used_bits;         /* sum of widths over super-groups */
     double achieved_bits;      /* used_bits / J (payload bits per coordinate) */
     int32_t nonfinite;         /* 1 if a gradient value or square was not finite */
+    float t816;                /* fl(2^31 rho) with the 16-bit class, +inf without */
+    int64_t class_count16;     /* super-groups at 16 bits (0 without the class) */
 } dq_info;
 
 /* Byte offsets of the plan state inside the bound workspace (for inspection). */
@@ -170,6 +185,7 @@ typedef struct dq_layout {
     size_t tables;     /* level and bucket tables of the plan's level shape */
     size_t ctrl;       /* control block (counts, rho, flags) */
     size_t total;
+    size_t tables16;   /* float[65536] levels, float[65536] weights of the 16-bit class (0: none) */
 } dq_layout;
 
 /* Accumulated kernel time per launch kind while DQ_OPT_TIMING is on. */

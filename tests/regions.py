@@ -1,26 +1,28 @@
 """Region layout helpers for the tests (written from the layout reading, not
 shared with either the oracle or the library).
 
-Part c of m holds, for each width class k (q = 2, 4, 8), the stream positions
+Part c of m holds, for each width class k (q = 2, 4, 8, and 16 when a plan
+has the 16-bit class; C lists the classes' counts), the stream positions
 [base_k + floor(c C_k / m), base_k + floor((c+1) C_k / m)).  Its region is:
-codes of the 2-bit, 4-bit, 8-bit super-groups (32 q bytes each), then one
-fp32 scale unit per super-group, zero padding to 16 bytes, then 16 UINT8
-group codes per super-group.  Code i sits at bit q*i of its payload, LSB first.
+codes of the 2-bit, 4-bit, 8-bit (16-bit) super-groups (32 q bytes each),
+then one fp32 scale unit per super-group, zero padding to 16 bytes, then 16
+UINT8 group codes per super-group.  Code i sits at bit q*i of its payload,
+LSB first.
 """
 import numpy as np
 
-QS = (2, 4, 8)
+QS = (2, 4, 8, 16)
 
 
 def class_bases(C):
-    return [0, int(C[0]), int(C[0]) + int(C[1])]
+    return [int(sum(int(x) for x in C[:k])) for k in range(len(C))]
 
 
 def part_ranges(C, m, c):
-    """[(lo, count)] in stream positions for the three classes."""
+    """[(lo, count)] in stream positions for each class of C."""
     base = class_bases(C)
     out = []
-    for k in range(3):
+    for k in range(len(C)):
         a = (c * int(C[k])) // m
         b = ((c + 1) * int(C[k])) // m
         out.append((base[k] + a, b - a))
@@ -30,7 +32,7 @@ def part_ranges(C, m, c):
 def layout(counts):
     off = 0
     codes = []
-    for k in range(3):
+    for k in range(len(counts)):
         codes.append(off)
         off += int(counts[k]) * 32 * QS[k]
     N = int(sum(counts))
@@ -47,11 +49,11 @@ def region_bytes(C, m, c):
 
 
 def sg_fields(region, C, m, c, pos):
-    """(class k, codes[256] uint8, s float32, cg[16] uint8) of stream position pos."""
+    """(class k, codes[256], s float32, cg[16] uint8) of stream position pos."""
     rng = part_ranges(C, m, c)
     counts = [n for _, n in rng]
     lay = layout(counts)
-    for k in range(3):
+    for k in range(len(C)):
         lo, n = rng[k]
         if lo <= pos < lo + n:
             idx = pos - lo
@@ -72,7 +74,7 @@ def sg_raw(region, C, m, c, pos):
     rng = part_ranges(C, m, c)
     counts = [n for _, n in rng]
     lay = layout(counts)
-    for k in range(3):
+    for k in range(len(C)):
         lo, n = rng[k]
         if lo <= pos < lo + n:
             idx = pos - lo
@@ -87,8 +89,8 @@ def sg_raw(region, C, m, c, pos):
 def unpack(raw, q):
     raw = np.asarray(raw, dtype=np.uint8)
     bits = np.unpackbits(raw, bitorder="little").reshape(256, q)
-    weights = (1 << np.arange(q)).astype(np.uint16)
-    return (bits.astype(np.uint16) * weights).sum(1).astype(np.uint8)
+    weights = (1 << np.arange(q)).astype(np.uint32)
+    return (bits.astype(np.uint32) * weights).sum(1).astype(np.uint16 if q > 8 else np.uint8)
 
 
 def part_positions(C, m, c):

@@ -205,3 +205,32 @@ def test_streams_option(lib):
     assert lib.dq_plan_set_u64(h, dq.OPT_STREAMS, 0) == dq.DQ_EINVAL
     assert lib.dq_plan_set_u64(h, dq.OPT_STREAMS, 3) == dq.DQ_EINVAL
     lib.dq_plan_destroy(h)
+
+
+def test_max_width_option(lib):
+    """DQ_OPT_MAX_WIDTH: 8 or 16; 16 adds the 16-bit tables to the workspace
+    and 256 more region bytes per super-group, unbinds the plan, and is
+    refused where a widest region would reach 4 GB."""
+    J = 4096
+    rc, h = _create(lib, 256 * J, 4, dq.RING, 5.0)
+    ws8 = lib.dq_workspace_bytes(h)
+    r8 = lib.dq_region_bytes_max(h, 4)
+    for v in (0, 4, 12, 32):
+        assert lib.dq_plan_set_u64(h, dq.OPT_MAX_WIDTH, v) == dq.DQ_EINVAL
+    assert lib.dq_plan_set_u64(h, dq.OPT_MAX_WIDTH, 16) == dq.DQ_OK
+    assert lib.dq_workspace_bytes(h) >= ws8 + 2 * 65536 * 4
+    assert lib.dq_region_bytes_max(h, 4) - r8 >= (J // 4) * 256
+    lay = dq.dq_layout()
+    assert lib.dq_workspace_layout(h, C.byref(lay)) == dq.DQ_OK
+    assert lay.tables16 > 0 and lay.tables16 + 2 * 65536 * 4 <= lay.total
+    # the workspace size changed: the plan is unbound
+    g = C.c_void_p(256)
+    assert lib.dq_stats(h, 0, g, dq.F32, None) == dq.DQ_EWORKSPACE
+    assert lib.dq_plan_set_u64(h, dq.OPT_MAX_WIDTH, 8) == dq.DQ_OK
+    assert lib.dq_workspace_bytes(h) == ws8
+    lib.dq_plan_destroy(h)
+    # a ring of two workers with 1.5e7 super-groups per part fits at 8 bits, not at 16
+    rc, h = _create(lib, 256 * 2 * 15_000_000, 2, dq.RING, 5.0)
+    assert rc == dq.DQ_OK
+    assert lib.dq_plan_set_u64(h, dq.OPT_MAX_WIDTH, 16) == dq.DQ_EINVAL
+    lib.dq_plan_destroy(h)

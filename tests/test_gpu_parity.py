@@ -76,16 +76,16 @@ class Round:
     region both produce (fresh zeroed buffers per step)."""
 
     def __init__(self, grads, topo, budget=5.0, seed=1, rnd=0, rounding=dq.STRATIFIED,
-                 alloc=dq.ALLOC_THRESHOLD, eps=None):
+                 alloc=dq.ALLOC_THRESHOLD, eps=None, max_width=8):
         self.grads = grads
         self.gnp = _grads_np(grads)
         self.n = len(grads)
         self.d = grads[0].numel()
         self.topo = topo
         self.plan = dq.Plan(self.d, self.n, topo, budget, seed=seed, rnd=rnd, rounding=rounding,
-                            alloc=alloc, eps=eps)
+                            alloc=alloc, eps=eps, max_width=max_width)
         self.orc = po.Oracle(self.d, self.n, topo, budget, seed=seed, rnd=rnd, rounding=rounding,
-                             alloc=alloc, eps=eps)
+                             alloc=alloc, eps=eps, max_width=max_width)
 
     def stages(self):
         for w in range(self.n):
@@ -560,3 +560,41 @@ def test_fused_final_hop_matches_hop_then_finalize(n, topo):
             with pytest.raises(dq.DQError):
                 r.plan.hop_finalize(w, last - 1, g_in, loc, reg, out)
     assert np.array_equal(_bits(out.cpu().numpy()), _bits(out_ref))
+
+
+# ---------------------------------------------------------------------------
+# the 16-bit class (DQ_OPT_MAX_WIDTH = 16): widths, streams, regions and
+# output bit-exact with the oracle's 16-bit class
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,n,topo,budget", [("gemma", 8, dq.BUTTERFLY, 6.0), ("bert", 4, dq.RING, 9.0),
+                                                ("llama", 5, dq.RING, 12.0), ("tiny", 4, dq.RING, 5.0),
+                                                ("large", 4, dq.BUTTERFLY, 16.0)])
+def test_sixteen_bit_class_bit_exact(name, n, topo, budget):
+    _need_gpu()
+    J = 1200 if name != "tiny" else 256
+    grads = _scaled(name, J, workers=range(n))
+    r, info, out = full_round(grads, topo, budget=budget, max_width=16)
+    assert len(info["class_counts"]) == 4
+    assert info["used_bits"] <= info["budget_bits"]
+    if budget >= 9.0:
+        assert info["class_counts"][3] > 0         # some super-groups at 16 bits
+    if budget == 16.0:
+        assert info["class_counts"][3] == J
+
+
+def test_sixteen_bit_class_level_tables_and_eps():
+    """The workspace's 65,536 levels and weights equal the oracle's table,
+    for the default shape and another one."""
+    _need_gpu()
+    for eps in (None, 0.2):
+        p = dq.Plan(256 * 64, 2, dq.RING, 10.0, max_width=16, eps=eps)
+        g = [torch.ones(256 * 64, dtype=torch.float32, device=DEV) for _ in range(2)]
+        p.stats(0, g[0])
+        p.stats(1, g[1])
+        torch.cuda.synchronize()
+        off = p.layout["tables16"]
+        T = p.workspace[off:off + 2 * 65536 * 4].view(torch.float32).cpu().numpy()
+        L, W = po.levels(16, 0.5 if eps is None else eps)
+        assert np.array_equal(_bits(T[:65536]), _bits(L))
+        assert np.array_equal(_bits(T[65536:65536 + 65535]), _bits(W))
