@@ -342,8 +342,9 @@ def main():
         v_mx4 = vnmse(plan.mx_allreduce(dq.MX_FP4_E2M1, grads, out=torch.empty_like(out), arena=mx_arena))
         del mx_arena
 
-        def variant(gs, bits, alloc, ref, eps=None):
-            p = dq.Plan(wl.d, wl.n, topo, bits, seed=wl.rounding_seed, alloc=alloc, device=dev, eps=eps)
+        def variant(gs, bits, alloc, ref, eps=None, max_width=8):
+            p = dq.Plan(wl.d, wl.n, topo, bits, seed=wl.rounding_seed, alloc=alloc, device=dev, eps=eps,
+                        max_width=max_width)
             a = torch.empty(p.arena_bytes(), dtype=torch.uint8, device=dev)
             o = p.allreduce(gs, out=torch.empty_like(out), arena=a)
             return ((o.double() - ref) ** 2).sum().item() / norm
@@ -356,6 +357,11 @@ def main():
         # the level shape eps the pages leave open (review's ledger)
         v_eps = {str(e): variant(grads, budget, dq.ALLOC_THRESHOLD, exact, eps=e)
                  for e in (0.05, 0.25, 0.5, 0.75, 1.0)}
+        # the 16-bit class of the threshold chain (widths {2,4,8,16}) at the
+        # workload's budget and at 6 bits, against {2,4,8} at 6 bits
+        v_w16 = {str(bb): variant(grads, bb, dq.ALLOC_THRESHOLD, exact, max_width=16)
+                 for bb in (budget, 6.0)}
+        v_w8_6 = variant(grads, 6.0, dq.ALLOC_THRESHOLD, exact)
         v_var4 = variant(grads, 4.0, dq.ALLOC_THRESHOLD, exact)
         v_uni4 = variant(grads, 4.0, dq.ALLOC_UNIFORM, exact)
         shuffled = exact_s = None
@@ -390,6 +396,7 @@ def main():
                    "stats_traffic_ratio": 8.0 / (256 * 2), "class_counts": info["class_counts"],
                    "vnmse_mxfp6_e3m2": v_mx6a, "vnmse_mxfp6_e2m3": v_mx6b, "vnmse_mxfp4_e2m1": v_mx4,
                    "vnmse_mean_corrected_alloc": v_mc, "vnmse_by_level_shape_eps": v_eps,
+                   "vnmse_16bit_class_by_budget": v_w16, "vnmse_6bit_without_16bit_class": v_w8_6,
                    "own_fp32_butterfly": own32,
                    "vnmse_4bit_variable": v_var4, "vnmse_4bit_uniform": v_uni4,
                    "vnmse_4bit_variable_shuffled": v_var4_s, "vnmse_4bit_uniform_shuffled": v_uni4_s}
