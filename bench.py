@@ -183,15 +183,24 @@ def cpu_baseline(args, wl_name, budget, device):
 
 
 def cpu_model():
-    """The host CPU's model name (what lscpu reports), from /proc/cpuinfo."""
+    """The host CPU's model name (what lscpu reports), from /proc/cpuinfo,
+    with its family / model / stepping numbers (a virtual machine may report
+    only a generic name; the numbers still identify the generation)."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break                       # the first processor's block only
+                k, _, v = line.partition(":")
+                fields[k.strip()] = v.strip()
     except OSError:
-        pass
-    return None
+        return None
+    name = fields.get("model name")
+    if name is None:
+        return None
+    ids = [f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields]
+    return f"{name} ({', '.join(ids)})" if ids else name
 
 
 def dar_coords_per_round(n, topology, d):
