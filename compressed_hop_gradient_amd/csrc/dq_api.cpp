@@ -806,6 +806,14 @@ dq_status dq_check_reciprocal(uint32_t lo, uint32_t count, unsigned long long *d
     return hip_status(launch_check_recip(lo, count, d_mismatches, static_cast<hipStream_t>(stream)));
 }
 
+dq_status dq_check_round_half_up(uint32_t lo, uint32_t count, unsigned long long *d_mismatches,
+                                 void *stream) {
+    if (!d_mismatches) return DQ_ENULL;
+    if ((uint64_t)lo + count > 0x100000000ull) return DQ_EINVAL;
+    if (count == 0) return DQ_OK;
+    return hip_status(launch_check_rpi(lo, count, d_mismatches, static_cast<hipStream_t>(stream)));
+}
+
 dq_status dq_probe_stream(const void *src, size_t src_bytes, void *dst, size_t dst_bytes,
                           int32_t reads_per_write, void *stream) {
     if (!src || !dst) return DQ_ENULL;

@@ -154,6 +154,7 @@ hipError_t launch_part_table(const unsigned long long *class_counts, int32_t n, 
                              PartInfo *table, hipStream_t s);
 hipError_t launch_mx(const MxArgs &a, int fmt, int local, hipStream_t s);
 hipError_t launch_check_recip(uint32_t lo, uint32_t n, unsigned long long *count, hipStream_t s);
+hipError_t launch_check_rpi(uint32_t lo, uint32_t n, unsigned long long *count, hipStream_t s);
 // static device scratch (dq_allreduce_noalloc): its device address on the
 // current device (looked up once per device)
 constexpr size_t kScratchBytes = size_t(64) << 20;

@@ -136,6 +136,21 @@ __device__ __forceinline__ float recip_rn(float x) {
     return y;
 }
 
+// floor(x + 0.5) as an integer, exactly, for every finite fp32 x: the
+// hardware's round-half-up conversion (values beyond the int range saturate,
+// and so does NaN, by its sign bit; checked over every bit pattern by
+// dq_check_round_half_up).  The rounding decision d + 0.5 <= P of a 16-bit
+// dither d then reads d < round_half_up(P): one conversion and one integer
+// compare, where the float form needs a conversion, an add and a compare.
+// P is finite for every finite input (an overflowing 1/sigma is handled
+// before the search); a NaN P comes only from non-finite gradients, which
+// the statistics flag, and still gives a code inside the class.
+__device__ __forceinline__ int round_half_up(float x) {
+    int n;
+    asm("v_cvt_rpi_i32_f32 %0, %1" : "=v"(n) : "v"(x));
+    return n;
+}
+
 // Smallest c in [0, 255] with fl(c * s) >= a (exists because fl(255 s) >= A >= a).
 // For a normal s the estimate ceil(a * rcp(s)) (rcp within 1 ulp) is within one
 // of the answer, so one checked step down or up settles it; subnormal s (scale
@@ -491,7 +506,19 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartU32 &Po, 
     const float s = scale_unit(A);
     const int c = group_code(amax, s);
     const float sigma = (float)c * s;
-    const float inv = sigma == 0.0f ? 0.0f : recip_rn(sigma);
+    float inv = sigma == 0.0f ? 0.0f : recip_rn(sigma);
+    // 1/sigma overflows only for sigma below 2^-128 (a subnormal scale unit):
+    // there v = y * inf would be +-inf, or NaN where y = 0.  Such a group takes
+    // the definition literally, v = 0 where y = 0 and clamp(y * inv) elsewhere,
+    // with the values put in place of y and inv = 1 for the loop below.
+    if (__builtin_expect(!(inv <= 3.4028234663852886e38f), 0)) {
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const float v = y[i] == 0.0f ? 0.0f : y[i] * inv;
+            y[i] = v < -1.0f ? -1.0f : (v > 1.0f ? 1.0f : v);
+        }
+        inv = 1.0f;
+    }
     float c1 = 0.0f, c2 = 0.0f;
     if constexpr (Q == 2) {
         c1 = T.dec2[1];
@@ -519,13 +546,14 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartU32 &Po, 
 #pragma unroll
         for (int ii = 0; ii < 8; ii++) {
             const int i = 8 * h + ii;
-            // The definition clamps v to [-1, 1].  Here |y| <= sigma, so v
-            // exceeds 1 in magnitude by at most 2 ulps, and there every step
-            // below gives the clamped value's code: the bucket key and the
-            // capped interval (r = 2^q - 2 above +1, r = 0 below -1) are the
-            // same, P(+1) >= 65535.99 > any d + 0.5 so rounding up stays
-            // certain, and P < 0 below -1 keeps rounding down certain.  The
-            // clamp is therefore left out.
+            // The definition clamps v to [-1, 1].  With a finite 1/sigma,
+            // |y| <= sigma makes v exceed 1 in magnitude by at most 2 ulps,
+            // and there every step below gives the clamped value's code: the
+            // bucket key and the capped interval (r = 2^q - 2 above +1, r = 0
+            // below -1) are the same, P(+1) >= 65535.99 >= any d + 0.5 so
+            // rounding up stays certain, and P < 0 below -1 keeps rounding
+            // down certain.  The clamp is therefore left out (an overflowing
+            // 1/sigma has been dealt with above).
             float v = y[i] * inv;
             float Lr, Wr;
             uint32_t r;
@@ -537,9 +565,10 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartU32 &Po, 
                 v = v < -1.0f ? -1.0f : (v > 1.0f ? 1.0f : v);
                 r = search_levels16(v, a.L16, a.W16, a.eps, Lr, Wr);
             }
+            // round up iff d + 0.5 <= P, i.e. d < floor(P + 0.5)
             const float P = (v - Lr) * Wr;
             const uint32_t dd = (ii & 1) ? (d[ii >> 1] >> 16) : (d[ii >> 1] & 0xFFFFu);
-            const uint32_t code = r + (((float)dd + 0.5f) < P ? 1u : 0u);
+            const uint32_t code = r + ((int)dd < round_half_up(P) ? 1u : 0u);
             w[(i * Q) / 32] |= code << ((i * Q) % 32);
         }
     }
@@ -1240,6 +1269,27 @@ __global__ __launch_bounds__(256) void k_check_recip(uint32_t lo, uint32_t n, un
     if ((threadIdx.x & 63) == 0 && m) atomicAdd(count, (unsigned long long)__popcll(m));
 }
 
+// round_half_up against the exact floor(x + 0.5) (in double, where x + 0.5
+// is exact) for the bit patterns lo .. lo + n - 1, with the conversion's
+// saturation beyond the int range; NaN saturates by its sign bit
+__global__ __launch_bounds__(256) void k_check_rpi(uint32_t lo, uint32_t n, unsigned long long *count) {
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    bool bad = false;
+    if (i < n) {
+        const float x = __uint_as_float(lo + i);
+        int want;
+        if (x != x) {
+            want = (lo + i) >> 31 ? (-2147483647 - 1) : 2147483647;
+        } else {
+            const double f = floor((double)x + 0.5);
+            want = f >= 2147483647.0 ? 2147483647 : (f <= -2147483648.0 ? (-2147483647 - 1) : (int)f);
+        }
+        bad = round_half_up(x) != want;
+    }
+    const unsigned long long m = __ballot(bad);
+    if ((threadIdx.x & 63) == 0 && m) atomicAdd(count, (unsigned long long)__popcll(m));
+}
+
 __device__ __forceinline__ int floor_log2(float a) {   // a > 0
     const uint32_t b = __float_as_uint(a);
     const int e = (int)(b >> 23);
@@ -1582,6 +1632,18 @@ hipError_t launch_check_recip(uint32_t lo, uint32_t n, unsigned long long *count
     for (uint32_t done = 0; done < n;) {
         const uint32_t k = n - done < kChunk ? n - done : kChunk;
         hipLaunchKernelGGL(k_check_recip, dim3((k + 255) / 256), dim3(256), 0, s, lo + done, k, count);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        done += k;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_check_rpi(uint32_t lo, uint32_t n, unsigned long long *count, hipStream_t s) {
+    constexpr uint32_t kChunk = 1u << 28;   // bit patterns per launch
+    for (uint32_t done = 0; done < n;) {
+        const uint32_t k = n - done < kChunk ? n - done : kChunk;
+        hipLaunchKernelGGL(k_check_rpi, dim3((k + 255) / 256), dim3(256), 0, s, lo + done, k, count);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         done += k;

@@ -89,6 +89,7 @@ _SIGS = {
     "dq_mx_allreduce": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
                                   C.c_void_p, C.c_void_p]),
     "dq_check_reciprocal": (C.c_int, [C.c_uint32, C.c_uint32, C.c_void_p, C.c_void_p]),
+    "dq_check_round_half_up": (C.c_int, [C.c_uint32, C.c_uint32, C.c_void_p, C.c_void_p]),
     "dq_probe_stream": (C.c_int, [C.c_void_p, C.c_size_t, C.c_void_p, C.c_size_t, C.c_int32,
                                   C.c_void_p]),
     "dq_get_info": (C.c_int, [C.c_void_p, C.POINTER(dq_info), C.c_void_p]),
@@ -169,6 +170,18 @@ def check_reciprocal(lo_bits, count, device=None, stream=None):
     cnt = torch.zeros(1, dtype=torch.int64, device=dev)
     _check(lib().dq_check_reciprocal(int(lo_bits), int(count), _ptr(cnt), _stream(stream)),
            "dq_check_reciprocal")
+    return int(cnt.item())
+
+
+def check_round_half_up(lo_bits, count, device=None, stream=None):
+    """Mismatches between the codec's round-half-up conversion and the exact
+    floor(x + 0.5) (NaN saturated by its sign) over the fp32 bit patterns
+    [lo_bits, lo_bits + count)
+    (runs on the GPU)."""
+    dev = torch.device("cuda") if device is None else torch.device(device)
+    cnt = torch.zeros(1, dtype=torch.int64, device=dev)
+    _check(lib().dq_check_round_half_up(int(lo_bits), int(count), _ptr(cnt), _stream(stream)),
+           "dq_check_round_half_up")
     return int(cnt.item())
 
 

@@ -406,6 +406,18 @@ dq_status dq_timing_read(dq_plan *plan, dq_timing *out);
 dq_status dq_check_reciprocal(uint32_t lo_bits, uint32_t count, unsigned long long *d_mismatches,
                               void *stream);
 
+/* Self-check of the conversion behind the codec's rounding decision: a
+ * 16-bit dither d rounds up iff d + 0.5 <= P, evaluated as d < floor(P + 0.5)
+ * with the hardware's round-half-up conversion.  Compares that conversion
+ * with the exact floor(x + 0.5) (saturated beyond the int32 range; NaN
+ * saturates by its sign bit)
+ * for the fp32 bit patterns [lo_bits, lo_bits + count) and ADDS the number of
+ * mismatches to *d_mismatches (device memory, one unsigned 64-bit counter,
+ * cleared by the caller).  Asynchronous on `stream`.
+ * Errors: DQ_ENULL, DQ_EINVAL (range past 0xFFFFFFFF), DQ_EHIP. */
+dq_status dq_check_round_half_up(uint32_t lo_bits, uint32_t count, unsigned long long *d_mismatches,
+                                 void *stream);
+
 /* Measurement probe: a plain coalesced streaming kernel with a fixed
  * read:write mix, for the HBM rate such a mix reaches on the device (the
  * ceiling against which a codec kernel's bandwidth is read; the hop with a

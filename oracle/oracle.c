@@ -580,10 +580,13 @@ static void slot_of(const part_layout *pl, uint8_t *region, int k, int64_t idx_i
 /*   s = fl(A/255), raised to the next fp32 while fl(255 s) < A;           */
 /*   c_g = smallest integer in [0,255] with fl(c_g s) >= a_g;              */
 /*   sigma_g = fl(c_g s);  inv_g = fl(1/sigma_g), or 0 when sigma_g = 0;   */
-/*   v = clamp(fl(y inv_g), -1, 1);                                        */
+/*   v = clamp(fl(y inv_g), -1, 1), and v = 0 where y = 0 (which differs   */
+/*   only where 1/sigma_g overflows, sigma_g < 2^-128: y * inf is NaN);    */
 /*   r = largest r <= 2^q - 2 with L[r] <= v;                              */
-/*   code = r + [ fl(d + 0.5) < fl(fl(v - L[r]) W[r]) ], d the 16-bit      */
-/*   dither;  decode: fl(fl(c_g s) L[code]).                               */
+/*   code = r + [ d + 0.5 <= fl(fl(v - L[r]) W[r]) ], d the 16-bit dither */
+/*   (d + 0.5 is exact in fp32; a tie rounds up, so P(up) is              */
+/*   floor(65536 p + 1/2) / 65536 for the interval fraction p, within     */
+/*   2^-17 of p);  decode: fl(fl(c_g s) L[code]).                          */
 /* ------------------------------------------------------------------ */
 
 static float step_of(float A) {
@@ -616,7 +619,7 @@ static void encode_sg(const float *y, int q, const float *L, const float *W,
         float inv = (sigma == 0.0f) ? 0.0f : 1.0f / sigma;
         for (int i = 0; i < OR_GROUP; i++) {
             int idx = g * OR_GROUP + i;
-            float v = y[idx] * inv;
+            float v = (y[idx] == 0.0f) ? 0.0f : y[idx] * inv;
             if (v < -1.0f) v = -1.0f;
             if (v > 1.0f) v = 1.0f;
             int r;
@@ -634,7 +637,7 @@ static void encode_sg(const float *y, int q, const float *L, const float *W,
             }
             float p65536 = (v - L[r]) * W[r];
             float dd = (float)d[idx] + 0.5f;
-            codes[idx] = (uint16_t)(r + (dd < p65536 ? 1 : 0));
+            codes[idx] = (uint16_t)(r + (dd <= p65536 ? 1 : 0));
         }
     }
 }

@@ -4,7 +4,9 @@ through the library's own device functions.
 The codecs compute v = y * fl(1/sigma) with one Newton step on the hardware
 reciprocal where sigma lies in [2^-126, 2^126), and with the IEEE division
 elsewhere.  Bit-exact parity with the oracle needs that reciprocal to be the
-correctly rounded quotient: checked here for every fp32 bit pattern."""
+correctly rounded quotient: checked here for every fp32 bit pattern.  The
+rounding decision uses the hardware's round-half-up conversion, checked the
+same way."""
 import pytest
 import torch
 
@@ -30,3 +32,13 @@ def test_reciprocal_fast_range_edges():
     lo, hi = 0x00800000, 0x7E800000          # 2^-126 .. 2^126: the Newton-step range
     assert dq.check_reciprocal(lo - 4096, 8192) == 0
     assert dq.check_reciprocal(hi - 4096, 8192) == 0
+
+
+def test_round_half_up_is_exact_for_every_float():
+    """The codec's rounding decision d + 0.5 <= P is evaluated as
+    d < floor(P + 0.5) with the hardware's round-half-up conversion: it must
+    equal the exact floor(x + 0.5) for every fp32 bit pattern (saturated
+    beyond the int32 range; NaN saturates by its sign bit)."""
+    _need_gpu()
+    bad = dq.check_round_half_up(0, 1 << 31) + dq.check_round_half_up(1 << 31, 1 << 31)
+    assert bad == 0

@@ -381,6 +381,44 @@ def test_zero_and_constant_super_groups_f32():
     assert np.all(out[256 * 5:256 * 6] == np.float32(1.5))
 
 
+def _subnormal_scale_grads(n, J, seed):
+    """fp32 gradients whose super-groups 3, 7, 11, ... hold values of a few
+    2^-145 (pairs +a, -a, so every worker's sum and the mean are exactly 0)
+    and exact zeros: their scale units are subnormal and 1/sigma overflows,
+    so y * inv would be +-inf, or NaN where y = 0.  The other super-groups
+    are ordinary."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        g = (rng.standard_normal(256 * J) * 1e-3).astype(np.float32)
+        for j in range(3, J, 4):
+            k = rng.integers(1, 2000, 128).astype(np.float32)
+            vals = np.empty(256, np.float32)
+            vals[0::2] = k * np.float32(2.0 ** -145)
+            vals[1::2] = -vals[0::2]
+            vals[rng.random(256) < 0.3] = 0.0
+            vals[1::2] = -vals[0::2]                    # keep the pairs after zeroing
+            g[256 * j:256 * (j + 1)] = vals
+        out.append(torch.from_numpy(g).to(DEV))
+    return out
+
+
+@pytest.mark.parametrize("budget,alloc,max_width,topo", [
+    (2.0, dq.ALLOC_THRESHOLD, 8, dq.RING), (8.0, dq.ALLOC_THRESHOLD, 8, dq.BUTTERFLY),
+    (4.0, dq.ALLOC_UNIFORM, 8, dq.RING), (5.0, dq.ALLOC_THRESHOLD, 8, dq.BUTTERFLY),
+    (16.0, dq.ALLOC_THRESHOLD, 16, dq.RING)])
+def test_subnormal_scale_super_groups_bit_exact(budget, alloc, max_width, topo):
+    """Groups whose 1/sigma overflows (sigma < 2^-128) follow the definition
+    exactly: v = 0 where y = 0 and clamp(y * inf) = +-1 elsewhere, in every
+    width class, through compress and every hop."""
+    _need_gpu()
+    n, J = 4, 64
+    grads = _subnormal_scale_grads(n, J, seed=int(budget * 10) + max_width)
+    r, info, out = full_round(grads, topo, budget=budget, alloc=alloc, max_width=max_width)
+    counts = info["class_counts"]
+    assert sum(counts) == J
+
+
 def test_all_zero_gradients():
     _need_gpu()
     g = [torch.zeros(256 * 33, dtype=torch.bfloat16, device=DEV) for _ in range(8)]

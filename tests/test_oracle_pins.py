@@ -405,7 +405,7 @@ def test_codec_eps1_q8_is_uniform_stochastic_rounding():
 
 def test_codec_rounding_probability_matches_dither_threshold():
     """For a fixed input the code is r+1 exactly for dithers d with
-    d + 0.5 < 65536 p, so the count of rounding-up dithers is 65536 p
+    d + 0.5 <= 65536 p, so the count of rounding-up dithers is 65536 p
     to within one dither."""
     y = np.zeros(256, np.float32)
     y[0] = 1.0           # group 0: sigma >= 1
@@ -426,6 +426,72 @@ def test_codec_rounding_probability_matches_dither_threshold():
         r = np.searchsorted(L, v, side="right") - 1
         p = (v - L[r]) / (np.float64(L[r + 1]) - L[r])
         assert abs(ups[t] / 4096 - p) <= 2.0 / 4096
+
+
+def test_codec_rounding_counts_every_dither_at_a_tie():
+    """Over all 65,536 dithers the number that round up is floor(P + 1/2)
+    for P = 65536 x (position in the interval), computed in fp32 as the
+    codec defines it; at a tie P = k + 1/2 that is k + 1 (d + 0.5 <= P
+    rounds up).  Enumerated on a coordinate whose P is an exact tie."""
+    Q, q = 16, 4
+    L, W = po.levels(q)
+    base = np.zeros(256, np.float32)
+    base[::16] = 1.0                      # every group: a_g = 1, the same sigma
+    _, _, s, cg = po.roundtrip_sg(base, q, np.zeros(256, np.uint16))
+    sigma = np.float32(cg[0]) * np.float32(s)
+    inv = np.float32(1) / sigma
+    rng = np.random.default_rng(5)
+    y1 = rng.uniform(-0.95, 0.95, 2_000_000).astype(np.float32)
+    v = (y1 * inv).astype(np.float32)
+    r = np.clip(np.searchsorted(L, v, side="right") - 1, 0, Q - 2)
+    P = ((v - L[r]).astype(np.float32) * W[r]).astype(np.float32)
+    ties = np.flatnonzero((P - np.floor(P) == 0.5) & (P > 1000))
+    assert ties.size > 0
+    i = ties[0]
+    y = base.copy()
+    mask = np.ones(256, bool)
+    mask[::16] = False
+    y[mask] = y1[i]
+    slots = np.flatnonzero(mask)          # 240 coordinates with this P
+    ups = 0
+    for d0 in range(0, 65536, slots.size):
+        d = np.zeros(256, np.uint16)
+        ds = np.arange(d0, min(d0 + slots.size, 65536))
+        d[slots[:ds.size]] = ds
+        _, codes, _, _ = po.roundtrip_sg(y, q, d)
+        c = codes[slots[:ds.size]].astype(np.int64)
+        assert np.all((c == r[i]) | (c == r[i] + 1))
+        ups += int(np.sum(c == r[i] + 1))
+    assert ups == int(np.floor(P[i])) + 1, (ups, P[i])
+
+
+def test_codec_unbiased_where_one_over_sigma_overflows():
+    """A group of values of a few 2^-145 has a subnormal scale unit and
+    1/sigma = inf: its zeros still quantise without bias (v = 0: the two
+    central levels, half each, mean 0) and its other values go to +-1."""
+    rng = np.random.default_rng(8)
+    k = rng.integers(1, 2000, 128).astype(np.float32)
+    y = np.empty(256, np.float32)
+    y[0::2] = k * np.float32(2.0 ** -145)
+    y[1::2] = -y[0::2]
+    zero = rng.random(256) < 0.3
+    y[zero] = 0.0
+    for q in (2, 4, 8, 16):
+        Q = 1 << q
+        K = 2000
+        dec = np.stack([po.roundtrip_sg(y, q, rng.integers(0, 65536, 256).astype(np.uint16))[0]
+                        for _ in range(K)])
+        _, codes, s, cg = po.roundtrip_sg(y, q, rng.integers(0, 65536, 256).astype(np.uint16))
+        sigma = np.float32(cg[0]) * np.float32(s)
+        assert sigma > 0 and np.isinf(np.float32(1) / sigma)
+        assert set(np.unique(codes[zero])) <= {Q // 2 - 1, Q // 2}
+        assert np.all(codes[~zero & (y > 0)] == Q - 1) and np.all(codes[~zero & (y < 0)] == 0)
+        z = dec[:, zero].astype(np.float64)
+        sd = z.std(0)
+        assert np.all(z[:, sd == 0] == 0)     # 16 bits: sigma L underflows to 0
+        if np.any(sd > 0):
+            zs = z.mean(0)[sd > 0] / (sd[sd > 0] / np.sqrt(K))
+            assert np.abs(zs).max() < 5, (q, np.abs(zs).max())
 
 
 # ---------------------------------------------------------------------------
