@@ -170,15 +170,16 @@ __device__ __forceinline__ int group_code(float a, float s) {
 }
 
 // Interval search over NL = 16 or 256 levels: r = largest r <= NL-2 with
-// L[r] <= v.  The bucket of v (sign, exponent and 7 mantissa bits) holds at
-// most one level boundary, so its table entry est is r or r - 1; one compare
-// with the next level settles it, and the pair (L[r], W[r]) is read at r.
+// L[r] <= v.  The linear bucket of v (one FMA and one mask: the bits of
+// fl(v M + 2^23 + NB/2) are 2^23 + the bucket) holds at most one level
+// boundary, so its table entry est is r or r - 1; one compare with the next
+// level settles it, and the pair (L[r], W[r]) is read at r.
 template <int NL>
 __device__ __forceinline__ uint32_t search_levels(float v, const uint8_t *est_tab, const float *cl,
                                                   const Pair *lw, float &Lr, float &Wr) {
-    const uint32_t b = __float_as_uint(v);
-    const uint32_t k = __builtin_elementwise_sub_sat((b >> 16) & 0x3FFFu, (uint32_t)kKeyBase);
-    const uint32_t est = est_tab[(k << 1) | (b >> 31)];
+    constexpr int NB = bucket_count(NL);
+    const float x = __builtin_fmaf(v, (float)(NB / 2 - 1), 8388608.0f + (float)(NB / 2));
+    const uint32_t est = est_tab[__float_as_uint(x) & (uint32_t)(NB - 1)];
     uint32_t r = est + (v >= cl[est + 1] ? 1u : 0u);
     // keep r opaque: the code is then formed as r + (round up), one carry-add,
     // rather than re-derived from est and both comparisons
@@ -1490,19 +1491,15 @@ hipError_t launch_probe_stream(const void *src, int64_t tiles, int reads_per_wri
 
 // Level, compare-level, (L, W) and bucket tables of the level shape eps, from
 // the same constexpr definitions the compile-time checks use (fp64, rounded
-// once to fp32); bucket entries by binary search for the largest r <= NL - 2
-// with L[r] <= the bucket's lower end (v >= 0) or <= -(its upper end) (v < 0).
+// once to fp32); bucket entry k = the number of interior levels L[1..NL-2]
+// whose bucket lies below k, by binary search (their buckets increase).
 template <int NL>
-__device__ int est_of(float x, double eps) {
-    int lo = 0, len = NL - 1;          // search r in [0, NL - 2]; L[0] = -1 <= x always
-    while (len > 1) {
-        const int half = len >> 1;
-        if (level_f(lo + half, NL, eps) <= x) {
-            lo += half;
-            len -= half;
-        } else {
-            len = half;
-        }
+__device__ int est_of(int k, double eps) {
+    int lo = 0, hi = NL - 2;           // the count lies in [0, NL - 2]
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (bucket_of<NL>(level_f(mid, NL, eps)) < k) lo = mid;
+        else hi = mid - 1;
     }
     return lo;
 }
@@ -1521,12 +1518,9 @@ __global__ __launch_bounds__(256) void k_build_tables(DeviceTables *t, double ep
         if (r < 4) v.L2[r] = level_f(r, 4, eps);
         if (r < 3) v.W2[r] = weight_f(r, 4, eps);
     }
-    for (int k = threadIdx.x; k < kKeys; k += blockDim.x) {
-        const float lo = key_lo(k), nh = -key_hi(k);
-        t->b8.est[2 * k] = (unsigned char)est_of<256>(lo, eps);
-        t->b8.est[2 * k + 1] = (unsigned char)est_of<256>(nh, eps);
-        t->b4.est[2 * k] = (unsigned char)est_of<16>(lo, eps);
-        t->b4.est[2 * k + 1] = (unsigned char)est_of<16>(nh, eps);
+    for (int k = threadIdx.x; k < bucket_count(256); k += blockDim.x) {
+        t->b8.est[k] = (unsigned char)est_of<256>(k, eps);
+        if (k < bucket_count(16)) t->b4.est[k] = (unsigned char)est_of<16>(k, eps);
     }
     // the LDS image, from the tables just written (visible to the whole block
     // after the barrier)
@@ -1544,9 +1538,9 @@ __global__ __launch_bounds__(256) void k_build_tables(DeviceTables *t, double ep
         if (i < 4) S.dec2[i] = v.L2[i];
         if (i < 3) S.lw2[i] = Pair{v.L2[i], v.W2[i]};
     }
-    for (int i = threadIdx.x; i < 2 * kKeys; i += blockDim.x) {
+    for (int i = threadIdx.x; i < bucket_count(256); i += blockDim.x) {
         S.b8[i] = t->b8.est[i];
-        S.b4[i] = t->b4.est[i];
+        if (i < bucket_count(16)) S.b4[i] = t->b4.est[i];
     }
     for (int b = threadIdx.x; b < 256; b += blockDim.x) {
 #pragma unroll

@@ -63,79 +63,70 @@ constexpr LevelTables make_tables(double eps) {
 constexpr LevelTables kLevelTables = make_tables(kDefaultEps);
 
 // ---------------------------------------------------------------------------
-// Bucket index for the interval search.  The key of v is 7 mantissa bits and
-// the exponent of |v| (fp32 bits >> 16), offset so that key 0 holds every
-// |v| < 2^-12 and key kKeyMax holds |v| = 1.  Each bucket is at most 2^-7
-// wide relative to its start; for every level shape the plan accepts, each
-// bucket contains at most one level boundary (checked when the tables are
-// built), so the table gives r or r - 1 and one compare with the next level
-// decides.  Entry 2k serves v >= 0 in bucket k, entry 2k + 1 serves v < 0.
+// Bucket index for the interval search, linear in v.  Class NL (16 or 256
+// levels) has NB buckets; bucket(v) = NB/2 + rne(v M) with M = NB/2 - 1 and
+// rne the round-to-nearest-even to an integer, so every |v| <= 1 + 2^-21
+// falls in [1, NB - 1].  The kernels compute it in two instructions: x =
+// fl(fma(v, M, 2^23 + NB/2)) lies in [2^23, 2^24), where fp32 values are the
+// integers, so x = 2^23 + bucket(v), and its bits masked to NB - 1 are
+// bucket(v).  The mask keeps every input, NaN and infinities included, inside
+// the table.  bucket() is non-decreasing in v; when the interior levels
+// L[1] < ... < L[NL-2] fall in strictly increasing buckets (checked for the
+// plan's level shape), the entry est[k] = #{interior levels in buckets < k}
+// is r(v) or r(v) - 1 for every v in bucket k, and one compare with
+// CL[est + 1] (CL[NL - 1] = +inf) decides.
 // ---------------------------------------------------------------------------
 
-constexpr int kKeyBase = 0x3980;              // fp32 bits of 2^-12, >> 16
-constexpr int kKeyMax = 0x3F80 - kKeyBase;    // key of 1.0
-// The kernels take the key from fp32 bits 29..16 (bit 30 is clear for every
-// |v| < 2), so a key never exceeds 0x3FFF - kKeyBase and needs no upper
-// clamp.  Keys above kKeyMax hold |v| > 1 + 2^-7, which finite inputs never
-// produce (|v| exceeds 1 by at most two ulps); they repeat the entries of
-// |v| = 1.  Non-finite inputs (flagged by the stats) land somewhere in the
-// table and give meaningless but in-bounds codes.
-constexpr int kKeys = 0x4000 - kKeyBase;
+constexpr int bucket_count(int NL) { return NL == 256 ? 8192 : 1024; }
 
-constexpr float key_lo(int k) {
-    return k == 0 ? 0.0f : (k >= kKeyMax ? 1.0f : __builtin_bit_cast(float, (unsigned)(k + kKeyBase) << 16));
+// rne(v * M) for |v| < 2 and 0 < M < 2^13, in exact integer arithmetic on the
+// bits of v (the product m M of the 24-bit significand fits 37 bits)
+constexpr long long rne_times(float v, int M) {
+    const unsigned b = __builtin_bit_cast(unsigned, v);
+    const int e = (int)((b >> 23) & 0xFFu);
+    const unsigned long long m = (unsigned long long)(b & 0x7FFFFFu) | (e ? 0x800000ull : 0ull);
+    const unsigned long long p = m * (unsigned long long)M;
+    const int s = 150 - (e ? e : 1);                   // value = p 2^-s
+    long long q = 0;
+    if (s <= 0) {
+        q = (long long)(p << -s);
+    } else if (s < 64) {
+        const unsigned long long fl = p >> s, rem = p & ((1ull << s) - 1ull), half = 1ull << (s - 1);
+        q = (long long)(fl + ((rem > half || (rem == half && (fl & 1ull))) ? 1ull : 0ull));
+    }
+    return (b >> 31) ? -q : q;
 }
-constexpr float key_hi(int k) {
-    return k >= kKeyMax ? 1.0f : __builtin_bit_cast(float, (unsigned)(k + 1 + kKeyBase) << 16);
+
+template <int NL>
+constexpr int bucket_of(float v) {
+    constexpr int NB = bucket_count(NL);
+    return NB / 2 + (int)rne_times(v, NB / 2 - 1);
 }
 
 template <int NL>
 struct BucketTable {
-    unsigned char est[2 * kKeys];
+    unsigned char est[bucket_count(NL)];
 };
 
-// est for v >= 0 in bucket k: largest r <= NL-2 with L[r] <= key_lo(k);
-// est for v < 0: largest r <= NL-2 with L[r] <= -key_hi(k).  Both by sweeps.
+// est[k] = number of interior levels L[1..NL-2] whose bucket is below k, by a
+// sweep over the buckets
 template <int NL>
 constexpr BucketTable<NL> make_buckets(double eps) {
     BucketTable<NL> t{};
     int r = 0;
-    for (int k = 0; k < kKeys; k++) {
-        const float lo = key_lo(k);
-        while (r + 1 <= NL - 2 && level_f(r + 1, NL, eps) <= lo) r++;
-        t.est[2 * k] = (unsigned char)r;
-    }
-    r = 0;
-    for (int k = kKeys - 1; k >= 0; k--) {
-        const float nh = -key_hi(k);
-        while (r + 1 <= NL - 2 && level_f(r + 1, NL, eps) <= nh) r++;
-        t.est[2 * k + 1] = (unsigned char)r;
+    for (int k = 0; k < bucket_count(NL); k++) {
+        while (r + 1 <= NL - 2 && bucket_of<NL>(level_f(r + 1, NL, eps)) < k) r++;
+        t.est[k] = (unsigned char)r;
     }
     return t;
 }
 
-// at most one level boundary inside every bucket (sweeps over the levels)
+// the interior levels fall in strictly increasing buckets (at most one level
+// boundary per bucket)
 template <int NL>
 constexpr bool buckets_hold_one_boundary(double eps) {
-    // positive side: levels in (key_lo(k), key_hi(k))
-    int r = 0;
-    for (int k = 0; k < kKeys; k++) {
-        const float lo = key_lo(k), hi = key_hi(k);
-        while (r < NL && level_f(r, NL, eps) <= lo) r++;
-        int c = 0;
-        for (int q = r; q < NL && level_f(q, NL, eps) < hi; q++) c++;
-        if (c > 1) return false;
-    }
-    // negative side: levels in (-key_hi(k), -key_lo(k)], by a sweep from the
-    // most negative level up (buckets k = kKeys-1 .. 0 cover increasing v)
-    r = 0;
-    for (int k = kKeys - 1; k >= 0; k--) {
-        const float a = -key_hi(k), b = -key_lo(k);
-        while (r < NL && level_f(r, NL, eps) <= a) r++;
-        int c = 0;
-        for (int q = r; q < NL && level_f(q, NL, eps) <= b; q++) c++;
-        if (c > 1) return false;
-    }
+    for (int r = 1; r + 1 <= NL - 2; r++)
+        if (bucket_of<NL>(level_f(r, NL, eps)) >= bucket_of<NL>(level_f(r + 1, NL, eps))) return false;
     return true;
 }
 
@@ -157,8 +148,8 @@ struct alignas(16) SharedTables {
     float cl8[256];
     Pair lw4[15];
     Pair lw8[255];
-    unsigned char b4[2 * kKeys];
-    unsigned char b8[2 * kKeys];
+    unsigned char b4[bucket_count(16)];
+    unsigned char b8[bucket_count(256)];
 };
 static_assert(sizeof(SharedTables) % 16 == 0, "the image is copied in 16-byte pieces");
 

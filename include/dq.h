@@ -231,7 +231,9 @@ typedef enum dq_option_f64 {
      * review's ledger names the level set Q = {f(eps, r)} and notes that the
      * paper never states eps).  Default 1/2; 1 is the uniform grid.  Accepted
      * for eps in (0, 1] when every bucket of the kernels' interval search holds
-     * at most one level boundary (true at least for eps >= 0.01).  The first
+     * at most one level boundary: the search's linear buckets are 1/1023 (4-bit
+     * class) and 1/4095 (8-bit class) of a unit wide, which admits every eps
+     * from 0.0274 up; smaller eps gives DQ_EINVAL.  The first
      * dq_stats of the next round rebuilds the tables in the workspace on the
      * device.  Set it between rounds, not inside one. */
     DQ_OPT_EPS = 0

@@ -296,7 +296,7 @@ def test_level_shapes_bit_exact(eps, topo):
 def test_device_tables_match_the_definition(eps):
     """The tables the plan builds in its workspace: levels and (L, W) pairs
     equal the oracle's; compare levels end in +inf; every bucket entry is
-    the largest r <= NL - 2 whose level is at most the bucket's end."""
+    the number of interior levels in the buckets below it."""
     _need_gpu()
     d = 256 * 64
     grads = [torch.zeros(d, dtype=torch.bfloat16, device=DEV)]
@@ -304,7 +304,7 @@ def test_device_tables_match_the_definition(eps):
     p.stats(0, grads[0])                     # the first stage builds the tables
     torch.cuda.synchronize()
     off = p.layout["tables"]
-    raw = p.workspace[off:off + 11020].cpu().numpy()
+    raw = p.workspace[off:off + 4364 + 8192 + 1024].cpu().numpy()
     f = lambda o, n: raw[o:o + 4 * n].view(np.float32)
     L2, L4, L8, W2 = f(0, 4), f(16, 16), f(80, 256), f(1104, 3)
     CL4, CL8 = f(1116, 16), f(1180, 256)
@@ -318,17 +318,14 @@ def test_device_tables_match_the_definition(eps):
         assert np.array_equal(_bits(CL[:-1]), _bits(Lo[:-1])) and np.isposinf(CL[-1])
         assert np.array_equal(_bits(LW[:, 0]), _bits(Lo[:-1]))
         assert np.array_equal(_bits(LW[:, 1]), _bits(Wo[:len(Lo) - 1]))
-    base, nkeys = 0x3980, 0x4000 - 0x3980
-    k = np.arange(nkeys, dtype=np.uint32)
-    lo = np.where(k == 0, 0, ((np.minimum(k, 0x3F80 - base) + base) << 16)).astype(np.uint32).view(np.float32)
-    hi = np.where(k >= 0x3F80 - base, np.float32(1.0).view(np.uint32),
-                  (k + 1 + base) << 16).astype(np.uint32).view(np.float32)
-    for q, o in ((8, 4364), (4, 4364 + 2 * nkeys)):
-        est = raw[o:o + 2 * nkeys]
-        Lo = po.levels(q, eps)[0][:-1]
-        exp_pos = np.searchsorted(Lo, lo, side="right") - 1
-        exp_neg = np.searchsorted(Lo, -hi, side="right") - 1
-        assert np.array_equal(est[0::2], exp_pos) and np.array_equal(est[1::2], exp_neg)
+    # bucket entries: est[k] = interior levels whose linear bucket
+    # NB/2 + rne(L M) (M = NB/2 - 1) lies below k
+    for q, o, NB in ((8, 4364, 8192), (4, 4364 + 8192, 1024)):
+        est = raw[o:o + NB]
+        Lo = po.levels(q, eps)[0]
+        bl = NB // 2 + np.rint(Lo[1:-1].astype(np.float64) * (NB // 2 - 1)).astype(np.int64)
+        want = np.searchsorted(bl, np.arange(NB), side="left")
+        assert np.array_equal(est.astype(np.int64), want)
 
 
 @pytest.mark.parametrize("n,topo", [(1, dq.RING), (1, dq.BUTTERFLY), (2, dq.RING), (2, dq.BUTTERFLY),

@@ -4,9 +4,13 @@ tables of the reading (generated here and by the oracle), on the CPU.
 1. The kernels skip the clamp of v to [-1, 1]: just above +1 the rounding-up
    threshold P of the last interval already exceeds every d + 0.5 (d < 2^16),
    and just below -1 it is negative, so codes cannot change.
-2. The interval search looks up a bucket of v keyed by the sign, the exponent
-   and 7 mantissa bits of |v| (all |v| < 2^-12 share one bucket): each bucket
-   holds at most one level boundary, for level shapes eps from 0.01 to 1.
+2. The interval search looks up a linear bucket of v, NB/2 + rne(v M) with
+   M = NB/2 - 1 (NB = 1024 buckets for 16 levels, 8192 for 256), computed as
+   the masked bits of fl(fma(v, M, 2^23 + NB/2)): that identity holds for
+   every fp32 v in [-1, 1] and a few ulps beyond (tests/native/
+   bucket_check.c), and the interior levels fall in strictly increasing
+   buckets for level shapes eps from 0.0274 to 1 (the plan refuses smaller
+   eps), so each bucket holds at most one level boundary.
 """
 import os
 
@@ -43,35 +47,57 @@ def test_no_clamp_needed_at_the_ends(q):
     assert np.all(v <= np.nextafter(np.nextafter(one, f32(2)), f32(2)))
 
 
+def _buckets(v, q):
+    NB = 1024 if q == 4 else 8192
+    return NB // 2 + np.rint(v.astype(np.float64) * (NB // 2 - 1)).astype(np.int64)
+
+
 @pytest.mark.parametrize("q", [4, 8])
-@pytest.mark.parametrize("eps", [1.0, 0.75, 0.5, 0.3, 0.1, 0.05, 0.01])
+@pytest.mark.parametrize("eps", [1.0, 0.75, 0.5, 0.3, 0.1, 0.05, 0.03, 0.0274])
 def test_buckets_hold_at_most_one_boundary(q, eps):
-    """Buckets of 7 mantissa bits per exponent of |v|, all |v| < 2^-12 in one
-    bucket: at most one level boundary per bucket, for level shapes from
-    eps = 0.01 to the uniform grid."""
+    """The interior levels L[1..2^q-2] of the oracle's table fall in strictly
+    increasing linear buckets, all inside the table, for level shapes from
+    eps = 0.0274 to the uniform grid."""
     L, _ = po.levels(q, eps)
-    base, kmax = 0x3980, 0x3F80 - 0x3980
-    keys = np.arange(kmax + 1, dtype=np.uint32)
-    lo = ((keys + base) << 16).view(np.float32).copy()
-    lo[0] = 0.0
-    hi = ((keys + 1 + base) << 16).view(np.float32).copy()
-    hi[kmax] = 1.0
-    Lp = L.astype(np.float64)
-    # v >= 0 in [lo, hi): levels strictly inside (lo, hi)
-    inside = ((Lp[None, :] > lo[:, None]) & (Lp[None, :] < hi[:, None])).sum(1)
-    assert inside.max() <= 1
-    # v < 0 in (-hi, -lo]
-    inside = ((Lp[None, :] > -hi[:, None]) & (Lp[None, :] <= -lo[:, None])).sum(1)
-    assert inside.max() <= 1
+    b = _buckets(L[1:-1], q)
+    assert np.all(np.diff(b) > 0)
+    assert b.min() >= 0 and b.max() < (1024 if q == 4 else 8192)
 
 
-def test_higher_tiny_bucket_would_fail_small_shapes():
-    """Were the shared bucket of tiny |v| to end at 2^-9, the 8-bit levels of
-    eps = 0.1 would put two boundaries into it: ending it at 2^-12 is what
-    admits the small shapes."""
-    L, _ = po.levels(8, 0.1)
-    assert ((L > 0) & (L < np.float32(2.0 ** -9))).sum() >= 2
-    assert ((L > 0) & (L < np.float32(2.0 ** -12))).sum() <= 1
+def test_small_level_shapes_are_refused():
+    """Below eps = 0.0273 the two central 8-bit levels share a bucket: the
+    library refuses such a shape (the plan option returns DQ_EINVAL)."""
+    import ctypes as C
+    from compressed_hop_gradient_amd import dq
+    L, _ = po.levels(8, 0.027)
+    b = _buckets(L[1:-1], 8)
+    assert np.any(np.diff(b) == 0)
+    lib = dq.lib()
+    h = C.c_void_p()
+    assert lib.dq_plan_create(256 * 4, 1, dq.RING, C.c_float(5.0), C.byref(h)) == dq.DQ_OK
+    assert lib.dq_plan_set_f64(h, dq.OPT_EPS, C.c_double(0.027)) == dq.DQ_EINVAL
+    assert lib.dq_plan_set_f64(h, dq.OPT_EPS, C.c_double(0.0274)) == dq.DQ_OK
+    lib.dq_plan_destroy(h)
+
+
+def test_linear_bucket_is_one_fma_and_a_mask(tmp_path):
+    """The kernels' bucket, the masked bits of fl(fma(v, M, 2^23 + NB/2)),
+    equals NB/2 + rne(v M) and never decreases, for every fp32 v from
+    -(1 + 16 ulp) to 1 + 16 ulp (both table sizes); NaN and the infinities
+    land inside the table (about 16 s)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = os.path.join(os.path.dirname(__file__), "native", "bucket_check.c")
+    exe = str(tmp_path / "bucket_check")
+    if subprocess.run([cc, "-O2", "-mfma", "-ffp-contract=off", "-o", exe, src, "-lm"]).returncode:
+        subprocess.run([cc, "-O2", "-ffp-contract=off", "-o", exe, src, "-lm"], check=True)
+    out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout.split()
+    checked, bad, dec, special = (int(x) for x in out)
+    assert checked == 2 * (0x3F800000 + 17)
+    assert bad == 0 and dec == 0 and special == 1
 
 
 def test_scale_unit_division_by_255_with_two_fmas(tmp_path):
