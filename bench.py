@@ -126,7 +126,9 @@ def measured_valu(kernel, src_hash, workload):
     if not e or e.get("kernel_source") != src_hash:
         return None
     return {"instr_per_launch": e["valu_instr_per_launch"], "instr_per_s": e["valu_instr_per_s"],
-            "peak_instr_per_s": rec["peak_instr_per_s"], "frac": e["frac_of_valu_roof"]}
+            "peak_instr_per_s": rec["peak_instr_per_s"], "frac": e["frac_of_valu_roof"],
+            "clock_ghz": e.get("clock_ghz"), "frac_at_clock": e.get("frac_of_valu_roof_at_clock"),
+            "valu_busy": e.get("valu_busy")}
 
 
 def cpu_baseline(args, wl_name, budget, device):
@@ -456,11 +458,13 @@ def main():
         del src, dst
 
     # which resource the DAR kernel runs closest to: VALU issue (committed
-    # counters of this kernel source and workload) or the HBM rate its
+    # counters of this kernel source and workload, at the clock the chip held
+    # during the kernel where that was measured) or the HBM rate its
     # read:write mix reaches (measured above)
     valu = measured_valu("hop_grad", src_hash, prof_wl)
     mix_frac = achieved / probe["read4_write1"]
-    limiter = None if valu is None else ("valu_issue" if valu["frac"] > mix_frac else "hbm_mix")
+    vfrac = None if valu is None else (valu["frac_at_clock"] or valu["frac"])
+    limiter = None if valu is None else ("valu_issue" if vfrac > mix_frac else "hbm_mix")
 
     res = {
         "metric": METRIC,
