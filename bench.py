@@ -13,6 +13,12 @@ Printed as one JSON line:
                butterfly): algorithmic bytes per launch / its HIP-event duration
   cpu_baseline the CPU oracle's whole round on a bounded sample of the same
                workload, same unit
+  quality      (after the timed region) vNMSE against the fp64 sum for the
+               rounding modes, the MX codecs in the same schedule, the
+               allocation variants, level shapes, the 16-bit class and the
+               fp32 own-partial butterfly, with round times for the MXFP8,
+               16-bit-class and own-partial rounds and the DDP hook's time
+               per 25 MiB bucket
 """
 import argparse
 import hashlib
@@ -346,19 +352,35 @@ def main():
             v_mode[mode] = vnmse(p_m.allreduce(grads, out=torch.empty_like(out), arena=arena))
             del p_m
         v_ind, v_rank = v_mode[dq.INDEPENDENT], v_mode[dq.CORRELATED]
+        def round_ms(fn, reps=3):
+            """Wall time of one call of fn (a whole round), after one untimed call."""
+            fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                fn()
+            torch.cuda.synchronize()
+            return 1e3 * (time.perf_counter() - t0) / reps
+
         mx_arena = torch.empty(int(dq.lib().dq_mxfp8_arena_bytes(plan.h)), dtype=torch.uint8, device=dev)
-        v_mx = vnmse(plan.mxfp8_allreduce(grads, out=torch.empty_like(out), arena=mx_arena))
+        o_mx = torch.empty_like(out)
+        v_mx = vnmse(plan.mxfp8_allreduce(grads, out=o_mx, arena=mx_arena))
+        mx_ms = round_ms(lambda: plan.mxfp8_allreduce(grads, out=o_mx, arena=mx_arena))
+        del o_mx
         v_mx6a = vnmse(plan.mx_allreduce(dq.MX_FP6_E3M2, grads, out=torch.empty_like(out), arena=mx_arena))
         v_mx6b = vnmse(plan.mx_allreduce(dq.MX_FP6_E2M3, grads, out=torch.empty_like(out), arena=mx_arena))
         v_mx4 = vnmse(plan.mx_allreduce(dq.MX_FP4_E2M1, grads, out=torch.empty_like(out), arena=mx_arena))
         del mx_arena
 
-        def variant(gs, bits, alloc, ref, eps=None, max_width=8):
+        def variant(gs, bits, alloc, ref, eps=None, max_width=8, timed=False):
             p = dq.Plan(wl.d, wl.n, topo, bits, seed=wl.rounding_seed, alloc=alloc, device=dev, eps=eps,
                         max_width=max_width)
             a = torch.empty(p.arena_bytes(), dtype=torch.uint8, device=dev)
             o = p.allreduce(gs, out=torch.empty_like(out), arena=a)
-            return ((o.double() - ref) ** 2).sum().item() / norm
+            v = ((o.double() - ref) ** 2).sum().item() / norm
+            if not timed:
+                return v
+            return {"vnmse": v, "ms_per_round": round_ms(lambda: p.allreduce(gs, out=o, arena=a))}
 
         # allocation variants: the mean-corrected key at the same budget;
         # variable against uniform widths at 4 bits (Table 6's comparison), on
@@ -370,7 +392,7 @@ def main():
                  for e in (0.05, 0.25, 0.5, 0.75, 1.0)}
         # the 16-bit class of the threshold chain (widths {2,4,8,16}) at the
         # workload's budget and at 6 bits, against {2,4,8} at 6 bits
-        v_w16 = {str(bb): variant(grads, bb, dq.ALLOC_THRESHOLD, exact, max_width=16)
+        v_w16 = {str(bb): variant(grads, bb, dq.ALLOC_THRESHOLD, exact, max_width=16, timed=True)
                  for bb in (budget, 6.0)}
         v_w8_6 = variant(grads, 6.0, dq.ALLOC_THRESHOLD, exact)
         v_var4 = variant(grads, 4.0, dq.ALLOC_THRESHOLD, exact)
@@ -400,14 +422,30 @@ def main():
         v_var4_s = variant(shuffled, 4.0, dq.ALLOC_THRESHOLD, exact_s) if shuffled else None
         v_uni4_s = variant(shuffled, 4.0, dq.ALLOC_UNIFORM, exact_s) if shuffled else None
         del shuffled, exact_s
+        # the DDP communication hook on one bucket of DDP's default 25 MiB
+        # (the start of worker 0's gradient), fp32 and bf16: pad, one-worker
+        # round (stats, allocate, reorder, compress, finalize), write back;
+        # the one-rank group it accepts, without a process group
+        from compressed_hop_gradient_amd import ddp_hook
+        hook = {}
+        for dt, dname, esz in ((torch.float32, "fp32", 4), (torch.bfloat16, "bf16", 2)):
+            nb = (25 << 20) // esz
+            flat = grads[0][:nb].to(dt).contiguous()
+            st = ddp_hook.DynamiQHookState(avg_bits=budget)
+            st.world_size = lambda: 1
+            ms = round_ms(lambda: ddp_hook.reduce_bucket(st, flat), reps=10)
+            hook[dname] = {"bucket_mib": 25, "coords": nb, "ms_per_bucket": ms,
+                           "coords_per_s": nb / (ms * 1e-3)}
+            del flat, st
         quality = {"vnmse_stratified": v_strat, "vnmse_independent": v_ind,
-                   "vnmse_rank_correlated": v_rank, "vnmse_mxfp8": v_mx,
+                   "vnmse_rank_correlated": v_rank, "vnmse_mxfp8": v_mx, "mxfp8_ms_per_round": mx_ms,
                    "mxfp8_over_dynamiq": v_mx / v_strat, "achieved_bits": b,
                    "wire_bits_per_coord": b + 0.625, "mxfp8_wire_bits_per_coord": 8.25,
                    "stats_traffic_ratio": 8.0 / (256 * 2), "class_counts": info["class_counts"],
                    "vnmse_mxfp6_e3m2": v_mx6a, "vnmse_mxfp6_e2m3": v_mx6b, "vnmse_mxfp4_e2m1": v_mx4,
                    "vnmse_mean_corrected_alloc": v_mc, "vnmse_by_level_shape_eps": v_eps,
-                   "vnmse_16bit_class_by_budget": v_w16, "vnmse_6bit_without_16bit_class": v_w8_6,
+                   "sixteen_bit_class_by_budget": v_w16, "vnmse_6bit_without_16bit_class": v_w8_6,
+                   "ddp_hook_25mib_bucket": hook,
                    "own_fp32_butterfly": own32,
                    "vnmse_4bit_variable": v_var4, "vnmse_4bit_uniform": v_uni4,
                    "vnmse_4bit_variable_shuffled": v_var4_s, "vnmse_4bit_uniform_shuffled": v_uni4_s}
