@@ -344,13 +344,27 @@ def main():
         def vnmse(o):
             return ((o.double() - exact) ** 2).sum().item() / norm
 
-        # the timed rounds use the default, level-stratified rounding
+        def over_rounds(p, o, a, k=10):
+            """vNMSE over rounds 0..k-1 (fresh dithers per round): mean, std."""
+            vals = []
+            for r in range(k):
+                p.set(dq.OPT_ROUND, r)
+                vals.append(vnmse(p.allreduce(grads, out=o, arena=a)))
+            p.set(dq.OPT_ROUND, 0)
+            m = sum(vals) / k
+            return {"mean": m, "std": (sum((x - m) ** 2 for x in vals) / (k - 1)) ** 0.5, "rounds": k}
+
+        # the timed rounds use the default, level-stratified rounding (round 0)
         v_strat = vnmse(out)
+        o_q = torch.empty_like(out)
+        v_rounds = {"stratified": over_rounds(plan, o_q, arena)}
         v_mode = {}
-        for mode in (dq.INDEPENDENT, dq.CORRELATED):
+        for mode, mname in ((dq.INDEPENDENT, "independent"), (dq.CORRELATED, "rank_correlated")):
             p_m = dq.Plan(wl.d, wl.n, topo, budget, seed=wl.rounding_seed, rounding=mode, device=dev)
-            v_mode[mode] = vnmse(p_m.allreduce(grads, out=torch.empty_like(out), arena=arena))
+            v_mode[mode] = vnmse(p_m.allreduce(grads, out=o_q, arena=arena))
+            v_rounds[mname] = over_rounds(p_m, o_q, arena)
             del p_m
+        del o_q
         v_ind, v_rank = v_mode[dq.INDEPENDENT], v_mode[dq.CORRELATED]
         def round_ms(fn, reps=3):
             """Wall time of one call of fn (a whole round), after one untimed call."""
@@ -438,6 +452,7 @@ def main():
                            "coords_per_s": nb / (ms * 1e-3)}
             del flat, st
         quality = {"vnmse_stratified": v_strat, "vnmse_independent": v_ind,
+                   "vnmse_rounds_0_9": v_rounds,
                    "vnmse_rank_correlated": v_rank, "vnmse_mxfp8": v_mx, "mxfp8_ms_per_round": mx_ms,
                    "mxfp8_over_dynamiq": v_mx / v_strat, "achieved_bits": b,
                    "wire_bits_per_coord": b + 0.625, "mxfp8_wire_bits_per_coord": 8.25,
