@@ -193,13 +193,16 @@ __device__ __forceinline__ uint32_t search_levels(float v, const uint8_t *est_ta
 // 16-bit search over the 65,536 levels in the workspace: r = the largest
 // r <= 65534 with L[r] <= v (v already clamped to [-1, 1], so L[0] = -1 <= v).
 // First guess from the closed form of the levels, |v| = t (eps + (1 - eps) t)
-// and u = (2 r + 1 - Q) / (Q - 1), i.e. r = floor((u + 1) (Q - 1) / 2); then
-// steps of one level until L[r] <= v < L[r+1]; a bisection in the (never
-// expected) case that 32 steps do not settle it.
+// and u = (2 r + 1 - Q) / (Q - 1), i.e. r = floor((u + 1) (Q - 1) / 2), with
+// the hardware square root and a reciprocal (a guess need not be exact);
+// then steps of one level until L[r] <= v < L[r+1]; a bisection in the
+// (never expected) case that 32 steps do not settle it.
 __device__ __forceinline__ uint32_t search_levels16(float v, const float *L, const float *W, float eps,
                                                     float &Lr, float &Wr) {
     const float av = fabsf(v), ce = 1.0f - eps;
-    const float t = ce > 0.0f ? (sqrtf(eps * eps + 4.0f * ce * av) - eps) / (2.0f * ce) : av;
+    const float t = ce > 0.0f
+        ? (__builtin_amdgcn_sqrtf(eps * eps + 4.0f * ce * av) - eps) * __builtin_amdgcn_rcpf(2.0f * ce)
+        : av;
     const float u = v < 0.0f ? -t : t;
     int r = (int)floorf((u + 1.0f) * 32767.5f);
     r = min(max(r, 0), 65534);
@@ -616,22 +619,26 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartU32 &Po, 
 // the fused last hop 4 as its output staging and the tables allow: 33.5 KB of
 // LDS per block); the others 512-thread blocks, 3 per CU.  Measured per kernel: with the packed local the larger
 // blocks are 4.6% faster, with the bf16 local the smaller ones 1-4%.
-template <int MODE, int LOCAL>
+// The instances with the 16-bit class (WIDE) hold six resident waves per
+// SIMD (80 VGPRs), the fused last hop four (128): at the default kernels' seven
+// or eight waves the wider codes and the 65,536-level search spill to scratch.
+template <int MODE, int LOCAL, bool WIDE = false>
 struct CodecShape {
     static constexpr bool kSmall = LOCAL == kLocalBF16 && MODE != kPartial;
     static constexpr int threads = kSmall ? 256 : 512;
     static constexpr int sg_per_block = threads / 16;
-    static constexpr int blocks_per_cu = kSmall ? (MODE == kCompress ? 8 : (MODE == kHopFinal ? 4 : 7)) : 3;
+    static constexpr int blocks_per_cu = WIDE ? (kSmall ? (MODE == kHopFinal ? 4 : 6) : (MODE == kHopFinal ? 2 : 3))
+                                              : (kSmall ? (MODE == kCompress ? 8 : (MODE == kHopFinal ? 4 : 7)) : 3);
     static constexpr int waves_per_simd = blocks_per_cu * threads / 256;   // 4 SIMDs per CU
 };
 
 // WIDE: the plan has the 16-bit class (a fourth class after the 8-bit one);
 // the default kernels are built without its code path.
 template <int MODE, int LOCAL, bool WIDE>
-__global__ __launch_bounds__((CodecShape<MODE, LOCAL>::threads))
-__attribute__((amdgpu_waves_per_eu(CodecShape<MODE, LOCAL>::waves_per_simd)))
+__global__ __launch_bounds__((CodecShape<MODE, LOCAL, WIDE>::threads))
+__attribute__((amdgpu_waves_per_eu(CodecShape<MODE, LOCAL, WIDE>::waves_per_simd)))
 void k_codec(CodecArgs a) {
-    using Shape = CodecShape<MODE, LOCAL>;
+    using Shape = CodecShape<MODE, LOCAL, WIDE>;
     constexpr int kThreads = Shape::threads, kSGPerBlock = Shape::sg_per_block;
     __shared__ SharedTables T;
     {
@@ -1712,7 +1719,7 @@ static dim3 codec_grid(int64_t n, int64_t blocks_per_cu, int64_t sg_per_block) {
 
 template <int MODE, int LOCAL, bool WIDE>
 static hipError_t launch_codec_w(const CodecArgs &a, int64_t max_sg, hipStream_t s) {
-    using Shape = CodecShape<MODE, LOCAL>;
+    using Shape = CodecShape<MODE, LOCAL, WIDE>;
     hipLaunchKernelGGL((k_codec<MODE, LOCAL, WIDE>), codec_grid(max_sg, Shape::blocks_per_cu, Shape::sg_per_block),
                        dim3(Shape::threads), 0, s, a);
     return hipGetLastError();
