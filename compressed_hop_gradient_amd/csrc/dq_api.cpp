@@ -94,11 +94,12 @@ void compute_layout(dq_plan *p) {
     off = align_up(off + sizeof(Ctrl), kAlign);
     off = align_up(off + 4 * kClasses * (size_t)p->nblk, kAlign);
     off = align_up(off + sizeof(PartInfo) * (size_t)part_table_entries(p->n, p->topo), kAlign);
-    // the 16-bit class's 65,536 levels and weights
+    // the 16-bit class's 65,536 levels and weights, then the same as
+    // (level, weight) pairs for the search
     p->lay.tables16 = 0;
     if (p->qmax == 16) {
         p->lay.tables16 = off;
-        off = align_up(off + 2 * 65536 * sizeof(float), kAlign);
+        off = align_up(off + 4 * 65536 * sizeof(float), kAlign);
     }
     p->lay.total = off;
 }
@@ -224,6 +225,7 @@ void fill_common(dq_plan *p, CodecArgs &a) {
     if (p->qmax == 16) {
         a.L16 = f32_at(p, p->lay.tables16);
         a.W16 = a.L16 + 65536;
+        a.LW16 = reinterpret_cast<const Pair *>(a.L16 + 2 * 65536);
     }
     a.eps = (float)p->eps;
 }
@@ -497,7 +499,7 @@ dq_status dq_stats(dq_plan *p, int32_t w, const void *grad, int32_t kind, void *
             e = launch_build_tables(reinterpret_cast<DeviceTables *>(p->ws + p->lay.tables), p->eps, s);
         if (e == hipSuccess && p->tables_dirty && p->qmax == 16) {
             float *L16 = f32_at(p, p->lay.tables16);
-            e = launch_build_tables16(L16, L16 + 65536, p->eps, s);
+            e = launch_build_tables16(L16, L16 + 65536, reinterpret_cast<Pair *>(L16 + 2 * 65536), p->eps, s);
         }
         if (e != hipSuccess) return DQ_EHIP;
         p->tables_dirty = false;

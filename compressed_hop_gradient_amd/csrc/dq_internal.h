@@ -61,6 +61,7 @@ enum Local { kLocalNone = 0, kLocalBF16 = 1, kLocalF32 = 2, kLocalPacked = 3, kL
 // (incoming and own packed) hold the part (m_in, part_in) that contains it
 // (the same part, or its parent when a hop writes the two children).
 struct DeviceTables;
+struct Pair;
 
 struct CodecArgs {
     const DeviceTables *tab;                 // level and bucket tables (plan workspace)
@@ -80,6 +81,7 @@ struct CodecArgs {
     // the 16-bit class: its 65,536 levels and weights (workspace), and the
     // level shape for the first guess of the interval search
     const float *L16, *W16;
+    const Pair *LW16;             // (L16[r], W16[r]) pairs
     float eps;
 };
 
@@ -145,7 +147,7 @@ hipError_t launch_reorder(const ReorderArgs &a, hipStream_t s);
 // wide: the plan has the 16-bit class (kernels with its code path)
 hipError_t launch_codec(const CodecArgs &a, int mode, int local, int64_t max_sg, bool wide, hipStream_t s);
 // the 16-bit class's level and weight tables (65,536 each) for level shape eps
-hipError_t launch_build_tables16(float *L16, float *W16, double eps, hipStream_t s);
+hipError_t launch_build_tables16(float *L16, float *W16, Pair *LW16, double eps, hipStream_t s);
 // part table for the schedule of n workers: ring entry c = part c of n;
 // butterfly entry (m - 2) + c = part c of m for m = 2, 4, .., n; n = 1: one entry
 int32_t part_table_entries(int32_t n, int32_t topology);

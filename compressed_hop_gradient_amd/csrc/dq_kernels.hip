@@ -192,44 +192,40 @@ __device__ __forceinline__ uint32_t search_levels(float v, const uint8_t *est_ta
 
 // 16-bit search over the 65,536 levels in the workspace: r = the largest
 // r <= 65534 with L[r] <= v (v already clamped to [-1, 1], so L[0] = -1 <= v).
-// First guess from the closed form of the levels, |v| = t (eps + (1 - eps) t)
+// First guess r0 from the closed form of the levels, |v| = t (eps + (1 - eps) t)
 // and u = (2 r + 1 - Q) / (Q - 1), i.e. r = floor((u + 1) (Q - 1) / 2), with
-// the hardware square root and a reciprocal (a guess need not be exact);
-// then steps of one level until L[r] <= v < L[r+1]; a bisection in the
-// (never expected) case that 32 steps do not settle it.
-__device__ __forceinline__ uint32_t search_levels16(float v, const float *L, const float *W, float eps,
+// the hardware square root and a reciprocal (off by at most one level in
+// practice).  Then, without a loop: with r0 clamped to [1, 65533], the pairs
+// r0 - 1, r0, r0 + 1 and the level r0 + 2 (independent loads) decide
+// r = r0 - 1 + [v >= L[r0]] + [v >= L[r0 + 1]] whenever L[r0 - 1] <= v <
+// L[r0 + 2] (or r0 + 2 is the last level, which is no boundary); otherwise a
+// bisection over all levels.
+__device__ __forceinline__ uint32_t search_levels16(float v, const float *L, const Pair *LW, float eps,
                                                     float &Lr, float &Wr) {
     const float av = fabsf(v), ce = 1.0f - eps;
     const float t = ce > 0.0f
         ? (__builtin_amdgcn_sqrtf(eps * eps + 4.0f * ce * av) - eps) * __builtin_amdgcn_rcpf(2.0f * ce)
         : av;
     const float u = v < 0.0f ? -t : t;
-    int r = (int)floorf((u + 1.0f) * 32767.5f);
-    r = min(max(r, 0), 65534);
-    int it = 0;
-    for (; it < 32; it++) {
-        if (r < 65534 && L[r + 1] <= v) {
-            r++;
-            continue;
-        }
-        if (r > 0 && L[r] > v) {
-            r--;
-            continue;
-        }
-        break;
+    int r0 = (int)floorf((u + 1.0f) * 32767.5f);
+    r0 = min(max(r0, 1), 65533);
+    const Pair p0 = LW[r0 - 1], p1 = LW[r0], p2 = LW[r0 + 1];
+    const float l3 = L[r0 + 2];
+    if (__builtin_expect(p0.l <= v && (v < l3 || r0 == 65533), 1)) {
+        const int k = (v >= p1.l ? 1 : 0) + (v >= p2.l ? 1 : 0);
+        Lr = k == 0 ? p0.l : (k == 1 ? p1.l : p2.l);
+        Wr = k == 0 ? p0.w : (k == 1 ? p1.w : p2.w);
+        return (uint32_t)(r0 - 1 + k);
     }
-    if (it == 32) {
-        int lo = 0, hi = 65534;
-        while (lo < hi) {
-            const int mid = lo + (hi - lo + 1) / 2;
-            if (L[mid] <= v) lo = mid;
-            else hi = mid - 1;
-        }
-        r = lo;
+    int lo = 0, hi = 65534;
+    while (lo < hi) {
+        const int mid = lo + (hi - lo + 1) / 2;
+        if (L[mid] <= v) lo = mid;
+        else hi = mid - 1;
     }
-    Lr = L[r];
-    Wr = W[r];
-    return (uint32_t)r;
+    Lr = LW[lo].l;
+    Wr = LW[lo].w;
+    return (uint32_t)lo;
 }
 
 // 2-bit search: two compares against the inner levels c1 = L[1], c2 = L[2]
@@ -567,7 +563,7 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartU32 &Po, 
             else {
                 // the clamp of the definition, kept for the 16-bit class
                 v = v < -1.0f ? -1.0f : (v > 1.0f ? 1.0f : v);
-                r = search_levels16(v, a.L16, a.W16, a.eps, Lr, Wr);
+                r = search_levels16(v, a.L16, a.LW16, a.eps, Lr, Wr);
             }
             // round up iff d + 0.5 <= P, i.e. d < floor(P + 0.5)
             const float P = (v - Lr) * Wr;
@@ -1560,15 +1556,17 @@ __global__ __launch_bounds__(256) void k_build_tables(DeviceTables *t, double ep
 // the 16-bit class: L[r] and W[r] = fl32(65536 / (L[r+1] - L[r])) for
 // r < 65,536, from the same fp64 definitions as the narrower classes (W[65535]
 // is unused and set to 0)
-__global__ __launch_bounds__(256) void k_build_tables16(float *L16, float *W16, double eps) {
+__global__ __launch_bounds__(256) void k_build_tables16(float *L16, float *W16, Pair *LW16, double eps) {
     for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < 65536; r += gridDim.x * blockDim.x) {
-        L16[r] = level_f(r, 65536, eps);
-        W16[r] = r < 65535 ? weight_f(r, 65536, eps) : 0.0f;
+        const float l = level_f(r, 65536, eps), w = r < 65535 ? weight_f(r, 65536, eps) : 0.0f;
+        L16[r] = l;
+        W16[r] = w;
+        LW16[r] = Pair{l, w};
     }
 }
 
-hipError_t launch_build_tables16(float *L16, float *W16, double eps, hipStream_t s) {
-    hipLaunchKernelGGL(k_build_tables16, dim3(256), dim3(256), 0, s, L16, W16, eps);
+hipError_t launch_build_tables16(float *L16, float *W16, Pair *LW16, double eps, hipStream_t s) {
+    hipLaunchKernelGGL(k_build_tables16, dim3(256), dim3(256), 0, s, L16, W16, LW16, eps);
     return hipGetLastError();
 }
 

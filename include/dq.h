@@ -185,7 +185,8 @@ typedef struct dq_layout {
     size_t tables;     /* level and bucket tables of the plan's level shape */
     size_t ctrl;       /* control block (counts, rho, flags) */
     size_t total;
-    size_t tables16;   /* float[65536] levels, float[65536] weights of the 16-bit class (0: none) */
+    size_t tables16;   /* float[65536] levels, float[65536] weights of the 16-bit class, then the
+                          same as 65536 (level, weight) pairs (0: none) */
 } dq_layout;
 
 /* Accumulated kernel time per launch kind while DQ_OPT_TIMING is on. */

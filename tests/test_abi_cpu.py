@@ -222,7 +222,7 @@ def test_max_width_option(lib):
     assert lib.dq_region_bytes_max(h, 4) - r8 >= (J // 4) * 256
     lay = dq.dq_layout()
     assert lib.dq_workspace_layout(h, C.byref(lay)) == dq.DQ_OK
-    assert lay.tables16 > 0 and lay.tables16 + 2 * 65536 * 4 <= lay.total
+    assert lay.tables16 > 0 and lay.tables16 + 4 * 65536 * 4 <= lay.total
     # the workspace size changed: the plan is unbound
     g = C.c_void_p(256)
     assert lib.dq_stats(h, 0, g, dq.F32, None) == dq.DQ_EWORKSPACE

@@ -620,7 +620,8 @@ def test_sixteen_bit_class_bit_exact(name, n, topo, budget):
 
 def test_sixteen_bit_class_level_tables_and_eps():
     """The workspace's 65,536 levels and weights equal the oracle's table,
-    for the default shape and another one."""
+    for the default shape and another one; so do the (level, weight) pairs
+    the search reads."""
     _need_gpu()
     for eps in (None, 0.2):
         p = dq.Plan(256 * 64, 2, dq.RING, 10.0, max_width=16, eps=eps)
@@ -629,7 +630,10 @@ def test_sixteen_bit_class_level_tables_and_eps():
         p.stats(1, g[1])
         torch.cuda.synchronize()
         off = p.layout["tables16"]
-        T = p.workspace[off:off + 2 * 65536 * 4].view(torch.float32).cpu().numpy()
+        T = p.workspace[off:off + 4 * 65536 * 4].view(torch.float32).cpu().numpy()
         L, W = po.levels(16, 0.5 if eps is None else eps)
         assert np.array_equal(_bits(T[:65536]), _bits(L))
         assert np.array_equal(_bits(T[65536:65536 + 65535]), _bits(W))
+        pairs = T[2 * 65536:].reshape(65536, 2)
+        assert np.array_equal(_bits(pairs[:, 0]), _bits(L))
+        assert np.array_equal(_bits(pairs[:65535, 1]), _bits(W))
