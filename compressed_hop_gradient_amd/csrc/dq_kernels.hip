@@ -92,6 +92,12 @@ __device__ __forceinline__ void philox4x32_10(uint32_t &x0, uint32_t &x1, uint32
         if (r > 0) {
             k0 += 0x9E3779B9u;
             k1 += 0xBB67AE85u;
+            // keep the round keys as two scalar registers bumped per round
+            // (scalar adds, off the vector pipe): left to itself the compiler
+            // holds all twenty round keys for the whole kernel, which pushes
+            // the codec kernels past the SGPR file and spills into VGPR lanes
+            // read back with v_readlane inside the loop
+            asm volatile("" : "+s"(k0), "+s"(k1));
         }
         const uint64_t pa = (uint64_t)0xD2511F53u * x0;
         const uint64_t pb = (uint64_t)0xCD9E8D57u * x2;
