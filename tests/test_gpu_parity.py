@@ -283,16 +283,18 @@ def test_allocation_variants_bit_exact(alloc, budget, topo):
 
 
 @pytest.mark.parametrize("eps,topo", [(1.0, dq.RING), (0.25, dq.BUTTERFLY), (0.05, dq.RING),
-                                      (0.8, dq.BUTTERFLY)])
+                                      (0.8, dq.BUTTERFLY), (0.03, dq.RING), (0.0274, dq.BUTTERFLY)])
 def test_level_shapes_bit_exact(eps, topo):
     """Other level shapes phi(t) = t (eps + (1 - eps) t): eps = 1 is the
-    uniform grid; smaller eps packs the levels towards zero."""
+    uniform grid; smaller eps packs the levels towards zero, down to the
+    smallest shape whose central 8-bit levels still fall in distinct
+    buckets of the interval search (eps = 0.0274)."""
     _need_gpu()
     grads = _scaled("llama" if topo == dq.RING else "gemma", 1031, workers=range(8))
     full_round(grads, topo, budget=5.0, eps=eps)
 
 
-@pytest.mark.parametrize("eps", [0.5, 1.0, 0.1])
+@pytest.mark.parametrize("eps", [0.5, 1.0, 0.1, 0.0274])
 def test_device_tables_match_the_definition(eps):
     """The tables the plan builds in its workspace: levels and (L, W) pairs
     equal the oracle's; compare levels end in +inf; every bucket entry is
