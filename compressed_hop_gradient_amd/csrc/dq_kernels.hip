@@ -934,13 +934,32 @@ __global__ __launch_bounds__(kStatsThreads) void k_stats(StatsArgs a, int64_t ch
             }
         }
         __syncthreads();
-        for (int64_t j = c0 + threadIdx.x; j < c1; j += kStatsThreads) {
-            const float s = park[0][j - c0], q = park[1][j - c0];
-            const float S = a.first ? s : a.sum[j] + s, F = a.first ? q : a.sumsq[j] + q;
-            __builtin_nontemporal_store(S, a.sum + j);
-            __builtin_nontemporal_store(F, a.sumsq + j);
-            if (!(__builtin_isfinite(S) && __builtin_isfinite(F))) atomicOr(a.nonfinite, 1);
+        // the fold with the earlier workers' running sums: all of this
+        // thread's loads are issued before any is used (one memory round
+        // trip rather than one per element), then the adds and stores
+        constexpr int kTail = (kStatsChunk + kStatsThreads - 1) / kStatsThreads;
+        float ps[kTail], pq[kTail];
+        if (!a.first) {
+#pragma unroll
+            for (int k = 0; k < kTail; k++) {
+                const int64_t j = c0 + threadIdx.x + (int64_t)k * kStatsThreads;
+                ps[k] = j < c1 ? a.sum[j] : 0.0f;
+                pq[k] = j < c1 ? a.sumsq[j] : 0.0f;
+            }
         }
+        bool bad = false;
+#pragma unroll
+        for (int k = 0; k < kTail; k++) {
+            const int64_t j = c0 + threadIdx.x + (int64_t)k * kStatsThreads;
+            if (j < c1) {
+                const float s = park[0][j - c0], q = park[1][j - c0];
+                const float S = a.first ? s : ps[k] + s, F = a.first ? q : pq[k] + q;
+                __builtin_nontemporal_store(S, a.sum + j);
+                __builtin_nontemporal_store(F, a.sumsq + j);
+                bad |= !(__builtin_isfinite(S) && __builtin_isfinite(F));
+            }
+        }
+        if (bad) atomicOr(a.nonfinite, 1);
         __syncthreads();
     }
 }
