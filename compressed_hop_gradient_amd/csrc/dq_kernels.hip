@@ -176,16 +176,24 @@ __device__ __forceinline__ int group_code(float a, float s) {
 }
 
 // Interval search over NL = 16 or 256 levels: r = largest r <= NL-2 with
-// L[r] <= v.  The linear bucket of v (one FMA and one mask: the bits of
-// fl(v M + 2^23 + NB/2) are 2^23 + the bucket) holds at most one level
-// boundary, so its table entry est is r or r - 1; one compare with the next
-// level settles it, and the pair (L[r], W[r]) is read at r.
+// L[r] <= v.  The linear bucket NB/2 + rne(v M) of v, M = NB/2 - 1, holds at
+// most one level boundary, so its table entry est is r or r - 1; one compare
+// with the next level settles it, and the pair (L[r], W[r]) is read at r.
+// The bucket is one FMA on the subnormal grid, where a float's bits are its
+// value in units of 2^-149: fl(v (M 2^-149) + (NB/2) 2^-149) rounds
+// v M + NB/2 to an integer (ties to even) and its bits are that integer, the
+// byte offset of the entry.  The encoder's |v| <= 1 + 2^-22 (1/sigma rounded
+// once, |y| <= sigma) keeps it in [1, NB - 1]; the FMA's clamp to [0, 1]
+// turns the NaN of a non-finite gradient into bucket 0, so no input reads
+// outside the table.
 template <int NL>
 __device__ __forceinline__ uint32_t search_levels(float v, const uint8_t *est_tab, const float *cl,
                                                   const Pair *lw, float &Lr, float &Wr) {
     constexpr int NB = bucket_count(NL);
-    const float x = __builtin_fmaf(v, (float)(NB / 2 - 1), 8388608.0f + (float)(NB / 2));
-    const uint32_t est = est_tab[__float_as_uint(x) & (uint32_t)(NB - 1)];
+    constexpr float kM = __builtin_bit_cast(float, (uint32_t)(NB / 2 - 1));
+    constexpr float kHalf = __builtin_bit_cast(float, (uint32_t)(NB / 2));
+    const float x = __builtin_amdgcn_fmed3f(__builtin_fmaf(v, kM, kHalf), 0.0f, 1.0f);
+    const uint32_t est = est_tab[__float_as_uint(x)];
     uint32_t r = est + (v >= cl[est + 1] ? 1u : 0u);
     // keep r opaque: the code is then formed as r + (round up), one carry-add,
     // rather than re-derived from est and both comparisons
@@ -575,7 +583,12 @@ __device__ __forceinline__ void codec_sg(const CodecArgs &a, const PartU32 &Po, 
             const float P = (v - Lr) * Wr;
             const uint32_t dd = (ii & 1) ? (d[ii >> 1] >> 16) : (d[ii >> 1] & 0xFFFFu);
             const uint32_t code = r + ((int)dd < round_half_up(P) ? 1u : 0u);
-            w[(i * Q) / 32] |= code << ((i * Q) % 32);
+            // pack as one shift-and-or per code, in coordinate order (kept
+            // as a chain: the compiler's own tree of shifts and ORs takes
+            // more instructions)
+            if ((i * Q) % 32 == 0) w[(i * Q) / 32] = code;
+            else w[(i * Q) / 32] |= code << ((i * Q) % 32);
+            asm("" : "+v"(w[(i * Q) / 32]));
         }
     }
 

@@ -65,12 +65,12 @@ constexpr LevelTables kLevelTables = make_tables(kDefaultEps);
 // ---------------------------------------------------------------------------
 // Bucket index for the interval search, linear in v.  Class NL (16 or 256
 // levels) has NB buckets; bucket(v) = NB/2 + rne(v M) with M = NB/2 - 1 and
-// rne the round-to-nearest-even to an integer, so every |v| <= 1 + 2^-21
-// falls in [1, NB - 1].  The kernels compute it in two instructions: x =
-// fl(fma(v, M, 2^23 + NB/2)) lies in [2^23, 2^24), where fp32 values are the
-// integers, so x = 2^23 + bucket(v), and its bits masked to NB - 1 are
-// bucket(v).  The mask keeps every input, NaN and infinities included, inside
-// the table.  bucket() is non-decreasing in v; when the interior levels
+// rne the round-to-nearest-even to an integer, so every |v| <= 1 + 2^-13
+// falls in [1, NB - 1].  The kernels compute it in one instruction: x =
+// fl(fma(v, M 2^-149, (NB/2) 2^-149)) lies on the subnormal grid, where the
+// bits of a float count units of 2^-149, so the bits of x are bucket(v); the
+// FMA's clamp to [0, 1] sends NaN to bucket 0.  bucket() is non-decreasing in
+// v; when the interior levels
 // L[1] < ... < L[NL-2] fall in strictly increasing buckets (checked for the
 // plan's level shape), the entry est[k] = #{interior levels in buckets < k}
 // is r(v) or r(v) - 1 for every v in bucket k, and one compare with

@@ -6,9 +6,10 @@ tables of the reading (generated here and by the oracle), on the CPU.
    and just below -1 it is negative, so codes cannot change.
 2. The interval search looks up a linear bucket of v, NB/2 + rne(v M) with
    M = NB/2 - 1 (NB = 1024 buckets for 16 levels, 8192 for 256), computed as
-   the masked bits of fl(fma(v, M, 2^23 + NB/2)): that identity holds for
-   every fp32 v in [-1, 1] and a few ulps beyond (tests/native/
-   bucket_check.c), and the interior levels fall in strictly increasing
+   the bits of one FMA on the subnormal grid, clamped to [0, 1]:
+   fl(fma(v, M 2^-149, (NB/2) 2^-149)).  That identity holds for every fp32
+   v in [-1, 1] and 1024 ulps beyond, and NaN lands in bucket 0 (tests/
+   native/bucket_check.c); the interior levels fall in strictly increasing
    buckets for level shapes eps from 0.0274 to 1 (the plan refuses smaller
    eps), so each bucket holds at most one level boundary.
 """
@@ -80,11 +81,13 @@ def test_small_level_shapes_are_refused():
     lib.dq_plan_destroy(h)
 
 
-def test_linear_bucket_is_one_fma_and_a_mask(tmp_path):
-    """The kernels' bucket, the masked bits of fl(fma(v, M, 2^23 + NB/2)),
-    equals NB/2 + rne(v M) and never decreases, for every fp32 v from
-    -(1 + 16 ulp) to 1 + 16 ulp (both table sizes); NaN and the infinities
-    land inside the table (about 16 s)."""
+def test_linear_bucket_is_one_subnormal_fma(tmp_path):
+    """The kernels' bucket, the bits of fl(fma(v, M 2^-149, (NB/2) 2^-149))
+    clamped to [0, 1] (the FMA's output modifier; NaN gives +0), equals
+    NB/2 + rne(v M), stays inside the table and never decreases, for v from
+    -(1 + 1024 ulp) to 1 + 1024 ulp (both table sizes; the encoder's |v| is
+    at most 1 + 2^-22): every fp32 v with |v| >= 2^-14 and every 64th bit
+    pattern below, where the key is NB/2.  Every NaN lands in bucket 0."""
     import shutil
     import subprocess
     cc = shutil.which("gcc") or shutil.which("cc")
@@ -92,12 +95,13 @@ def test_linear_bucket_is_one_fma_and_a_mask(tmp_path):
         pytest.skip("no C compiler")
     src = os.path.join(os.path.dirname(__file__), "native", "bucket_check.c")
     exe = str(tmp_path / "bucket_check")
-    if subprocess.run([cc, "-O2", "-mfma", "-ffp-contract=off", "-o", exe, src, "-lm"]).returncode:
-        subprocess.run([cc, "-O2", "-ffp-contract=off", "-o", exe, src, "-lm"], check=True)
+    if subprocess.run([cc, "-O2", "-fopenmp", "-mfma", "-ffp-contract=off", "-o", exe, src, "-lm"]).returncode:
+        subprocess.run([cc, "-O2", "-fopenmp", "-ffp-contract=off", "-o", exe, src, "-lm"], check=True)
     out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout.split()
-    checked, bad, dec, special = (int(x) for x in out)
-    assert checked == 2 * (0x3F800000 + 17)
-    assert bad == 0 and dec == 0 and special == 1
+    checked, bad, dec, outside, nan_ok = (int(x) for x in out)
+    b14, top = 0x38800000, 0x3F800000 + 1024
+    assert checked == 2 * (top - b14 + 1) + 2 * ((b14 + 63) // 64)
+    assert bad == 0 and dec == 0 and outside == 0 and nan_ok == 1
 
 
 def test_scale_unit_division_by_255_with_two_fmas(tmp_path):
