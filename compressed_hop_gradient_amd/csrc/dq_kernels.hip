@@ -1132,6 +1132,13 @@ __global__ __launch_bounds__(256) void k_alloc_decide(AllocArgs a, int pass) {
         if (cs == 0) {              // only at pass 0 (later passes start at a failing value): rho = 0
             c->rho_bits = prefix;
             c->done = 1u;
+        } else if (cs == n && pass == 0) {
+            // not even rho = +inf (the last candidate) meets the budget: only
+            // keys of +inf (overflowed squared norms, which the statistics
+            // flag) keep a width above 2 there.  The search range ends at
+            // +inf, and so does rho; the next passes would step past it.
+            c->rho_bits = 0x7F800000u;
+            c->done = 1u;
         } else if (pass == kRadixPasses - 1) {
             c->rho_bits = prefix + ((uint32_t)cs << shift);
             c->done = 1u;
@@ -1154,7 +1161,11 @@ __global__ __launch_bounds__(256) void k_alloc_final(AllocArgs a) {
     const uint32_t rb = uniform ? 0u : c->rho_bits;
     const float rho = __uint_as_float(rb);
     const float t4 = k24(a.wide) * rho, t8 = k48(a.wide) * rho;
-    const float t16 = a.wide ? kK816 * rho : __builtin_huge_valf();
+    // without the 16-bit class no key reaches class 3, not even F = +inf (a
+    // squared norm that overflowed): the class-3 test is skipped, not given
+    // an infinite threshold that +inf would meet
+    const bool wide = a.wide;
+    const float t16 = kK816 * rho;
     uint32_t cnt[kClasses] = {0u, 0u, 0u, 0u};
     const int64_t j0 = (int64_t)blockIdx.x * kReorderSGPerBlock + threadIdx.x * 4;
     if (j0 + 4 <= a.J) {
@@ -1167,7 +1178,7 @@ __global__ __launch_bounds__(256) void k_alloc_final(AllocArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const float G = alloc_key(a, F[i], S[i]);
-            const int k = uniform ? a.uniform_k : (G >= t16 ? 3 : (G >= t8 ? 2 : (G >= t4 ? 1 : 0)));
+            const int k = uniform ? a.uniform_k : ((wide && G >= t16) ? 3 : (G >= t8 ? 2 : (G >= t4 ? 1 : 0)));
             w |= (2u << k) << (8 * i);
             cnt[k]++;
         }
@@ -1175,7 +1186,7 @@ __global__ __launch_bounds__(256) void k_alloc_final(AllocArgs a) {
     } else {
         for (int64_t j = j0; j < a.J; j++) {
             const float G = alloc_key(a, a.sumsq[j], centred ? a.sum[j] : 0.0f);
-            const int k = uniform ? a.uniform_k : (G >= t16 ? 3 : (G >= t8 ? 2 : (G >= t4 ? 1 : 0)));
+            const int k = uniform ? a.uniform_k : ((wide && G >= t16) ? 3 : (G >= t8 ? 2 : (G >= t4 ? 1 : 0)));
             a.widths[j] = (uint8_t)(2 << k);
             cnt[k]++;
         }

@@ -285,14 +285,18 @@ static void multipliers(int qmax, float K[4]) {
     }
 }
 
-static int width_of(float F, float t4, float t8, float t16) {
-    if (F >= t16) return 16;
+/* Widths {2,4,8} (Fig. 3 caption: the chain stops at 8 unless the 16-bit
+ * class is on): 16 only with that class, so a key of +inf (an overflowed
+ * squared norm) gets 8 and never a width outside the plan's set. */
+static int width_of(float F, float t4, float t8, float t16, int qmax) {
+    if (qmax == 16 && F >= t16) return 16;
     if (F >= t8) return 8;
     if (F >= t4) return 4;
     return 2;
 }
 
-/* the thresholds T24, T48 and T816 (+inf without the 16-bit class) of rho */
+/* the thresholds T24, T48 and T816 of rho (T816 is +inf without the 16-bit
+ * class, and width_of does not consult it then) */
 static void thresholds_of(int qmax, uint32_t rho_bits, float *t4, float *t8, float *t16) {
     float K[4];
     multipliers(qmax, K);
@@ -333,7 +337,7 @@ static int64_t count_bits_on(const float *key, int64_t J, int qmax, uint32_t rho
     thresholds_of(qmax, rho_bits, &t4, &t8, &t16);
     int64_t total = 0;
 #pragma omp parallel for reduction(+ : total) schedule(static)
-    for (int64_t j = 0; j < J; j++) total += width_of(key[j], t4, t8, t16);
+    for (int64_t j = 0; j < J; j++) total += width_of(key[j], t4, t8, t16, qmax);
     return total;
 }
 
@@ -443,7 +447,10 @@ int or_allocate(or_ctx *c) {
     if (count_bits_on(key, c->J, c->qmax, 0u) <= budget) {
         rho = 0u;
     } else {
-        uint32_t lo = 0u, hi = 0x7F800000u; /* +inf: every width is 2 */
+        /* at +inf every finite key has width 2; keys of +inf (overflowed
+         * squared norms) keep theirs, and if the budget is missed even there,
+         * rho stays at the end of the range, +inf */
+        uint32_t lo = 0u, hi = 0x7F800000u;
         while (hi - lo > 1u) {
             uint32_t mid = lo + (hi - lo) / 2u;
             if (count_bits_on(key, c->J, c->qmax, mid) <= budget) hi = mid; else lo = mid;
@@ -454,7 +461,7 @@ int or_allocate(or_ctx *c) {
     float t4, t8, t16;
     thresholds_of(c->qmax, rho, &t4, &t8, &t16);
     for (int64_t j = 0; j < c->J; j++) {
-        int q = width_of(key[j], t4, t8, t16);
+        int q = width_of(key[j], t4, t8, t16, c->qmax);
         c->width[j] = (uint8_t)q;
         c->C[class_of_width(q)]++;
     }

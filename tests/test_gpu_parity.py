@@ -443,6 +443,80 @@ def test_nonfinite_flag():
     assert not p.info()["nonfinite"]
 
 
+@pytest.mark.parametrize("topo,max_width", [(dq.RING, 8), (dq.BUTTERFLY, 8), (dq.BUTTERFLY, 16)],
+                         ids=["ring", "butterfly", "butterfly-16bit"])
+def test_nonfinite_gradients_stay_in_their_super_groups(topo, max_width):
+    """Gradients must be finite, and a round over non-finite ones is flagged
+    (DQ_ENONFINITE).  It still runs to the end with every table read in
+    bounds, and a non-finite value spoils only its own super-group: every
+    super-group that is finite on every worker comes out bit-exact against
+    the oracle.  Planted: +inf, -inf, a NaN, a whole group of NaN, and +inf
+    on one worker against -inf on another in the same coordinate (a NaN
+    sum); with the 16-bit class allowed, the infinite squared norm puts its
+    super-group in that class."""
+    _need_gpu()
+    J, n = 96, 4
+    grads = _scaled("gemma", J, workers=range(n))
+    plants = [(0, 3 * 256 + 5, float("inf")), (1, 10 * 256 + 17, float("nan")),
+              (3, 40 * 256, float("inf")), (1, 40 * 256, float("-inf")),
+              (0, 77 * 256 + 255, float("-inf"))]
+    plants += [(2, 20 * 256 + 32 + i, float("nan")) for i in range(16)]
+    for w, i, x in plants:
+        grads[w][i] = x
+    bad = sorted({i // 256 for _, i, _ in plants})
+    plan = dq.Plan(256 * J, n, topo, 5.0, seed=1, max_width=max_width)
+    out = plan.allreduce(grads)
+    torch.cuda.synchronize()
+    info = plan.info()
+    assert info["nonfinite"] and info["status"] == dq.DQ_ENONFINITE
+    if max_width == 16:
+        assert info["class_counts"][3] >= 1
+    ref = po.Oracle(256 * J, n, topo, 5.0, seed=1, max_width=max_width).allreduce(_grads_np(grads))
+    ok = np.ones(J, bool)
+    ok[bad] = False
+    keep = np.repeat(ok, 256)
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got[keep]))
+    assert np.array_equal(_bits(got[keep]), _bits(ref[keep]))
+
+
+@pytest.mark.parametrize("max_width", [8, 16])
+@pytest.mark.parametrize("budget,n_over", [(5.0, 3), (3.0, 12)], ids=["within-budget", "budget-out-of-reach"])
+def test_overflowed_squared_norms_like_the_oracle(max_width, budget, n_over):
+    """Finite gradients whose squared norms overflow (one entry of 1e20 per
+    super-group): the round is flagged, and rho, every width and the class
+    counts equal the oracle's.  Keys of +inf take the widest width of the
+    plan's set and nothing outside it; when even rho = +inf misses the
+    budget, rho is +inf.  The whole round then runs in bounds and the
+    super-groups that did not overflow come out bit-exact."""
+    _need_gpu()
+    J, n = 16, 2
+    gen = torch.Generator().manual_seed(41)
+    gs = [torch.randn(256 * J, generator=gen).to(DEV) for _ in range(n)]
+    gs[1][0:n_over * 256:256] = 1e20
+    gnp = [g.cpu().numpy() for g in gs]
+    plan = dq.Plan(256 * J, n, dq.RING, budget, max_width=max_width)
+    orc = po.Oracle(256 * J, n, po.RING, budget, max_width=max_width)
+    for w in range(n):
+        plan.stats(w, gs[w])
+        orc.stats(w, gnp[w])
+    plan.allocate()
+    orc.allocate()
+    info = plan.info()
+    assert info["nonfinite"] and info["status"] == dq.DQ_ENONFINITE
+    assert info["rho_bits"] == orc.rho_bits()
+    if n_over == 12:
+        assert orc.rho_bits() == 0x7F800000
+    assert np.array_equal(plan.widths().cpu().numpy(), orc.widths())
+    assert list(info["class_counts"]) == orc.class_counts().tolist()
+    assert sum(info["class_counts"]) == J
+    out = dq.Plan(256 * J, n, dq.RING, budget, max_width=max_width).allreduce(gs)
+    torch.cuda.synchronize()
+    ref = po.Oracle(256 * J, n, po.RING, budget, max_width=max_width).allreduce(gnp)
+    keep = np.repeat(np.arange(J) >= n_over, 256)
+    assert np.array_equal(_bits(out.cpu().numpy()[keep]), _bits(ref[keep]))
+
+
 def test_deterministic_and_native_schedule_matches():
     _need_gpu()
     grads = _scaled("gemma", 2050)

@@ -1425,6 +1425,49 @@ def test_wide_allocation_special_budgets():
         po.Oracle(256, 1, po.RING, 5.0, max_width=12)
 
 
+@pytest.mark.parametrize("max_width", [8, 16])
+def test_overflowed_squared_norms_keep_the_width_set(max_width):
+    """A finite gradient can still overflow its squared norm (|e| above about
+    1.8e19 gives fl(e^2) = +inf; the statistics flag such a round).  A key of
+    +inf meets every finite threshold and takes the widest width of the
+    plan's set: 8 without the 16-bit class (the width set {2,4,8} of the
+    threshold chain, Fig. 3 caption), never a width outside it.  A NaN key
+    meets no threshold and takes 2.  Every super-group lands in a class."""
+    J = 40
+    rng = np.random.default_rng(31)
+    g = rng.standard_normal(256 * J).astype(np.float32)
+    g[5 * 256 + 7] = 1e20
+    g[9 * 256] = 3e19
+    g[12 * 256 + 3] = np.nan
+    o = po.Oracle(256 * J, 1, po.RING, 5.0, max_width=max_width)
+    o.stats(0, g)
+    o.allocate()
+    _, F, _ = o.stats_arrays()
+    assert np.isposinf(F[[5, 9]]).all() and np.isnan(F[12])
+    q = o.widths().astype(int)
+    assert q[5] == q[9] == max_width and q[12] == 2
+    assert set(np.unique(q).tolist()) <= ({2, 4, 8, 16} if max_width == 16 else {2, 4, 8})
+    assert int(o.class_counts().sum()) == J
+    assert q.sum() <= o.budget_bits()
+
+
+@pytest.mark.parametrize("max_width", [8, 16])
+def test_budget_out_of_reach_with_infinite_norms_gives_rho_inf(max_width):
+    """When even rho = +inf misses the budget (keys of +inf keep the widest
+    width at every rho), rho is the end of the search range, +inf: finite
+    keys take 2 bits and the infinite ones the widest width of the set."""
+    J = 16
+    g = np.ones(256 * J, np.float32)
+    g[0:12 * 256:256] = 1e20          # 12 of 16 super-groups overflow
+    o = po.Oracle(256 * J, 1, po.RING, 3.0, max_width=max_width)
+    o.stats(0, g)
+    o.allocate()
+    assert o.rho_bits() == 0x7F800000
+    q = o.widths()
+    assert (q[:12] == max_width).all() and (q[12:] == 2).all()
+    assert int(o.class_counts().sum()) == J
+
+
 def test_level_table_16_bits():
     L, W = po.levels(16)
     assert L.size == 65536 and L[0] == -1.0 and L[-1] == 1.0
