@@ -641,9 +641,24 @@ dq_status hop_impl(dq_plan *p, int32_t w, int32_t step, const void *in, const vo
     const int kindk = final_out ? DQ_K_HOP_FINAL : (want_own ? DQ_K_HOP_PACKED : DQ_K_HOP_GRAD);
     // the child this worker keeps for the next level (own-fp32: written as fp32)
     const int keep = (own32 && sp.two_children) ? (w >> (p->L - step - 1)) & 1 : -1;
-    // one launch per output region: the part itself, or each of its two children
-    const int nout = sp.two_children ? 2 : 1;
     hipError_t e = hipSuccess;
+    if (sp.two_children && keep < 0) {
+        // both children in one launch (the kernel splits its blocks between
+        // them), timed as the parent part they make up together
+        a.part_out = part_entry(p, 2 * sp.m, 2 * sp.part);
+        a.part_out2 = part_entry(p, 2 * sp.m, 2 * sp.part + 1);
+        a.out = static_cast<uint8_t *>(out0);
+        a.out2 = static_cast<uint8_t *>(out1);
+        Launch L;
+        e = timed_begin(p, kindk, sp.m, sp.part, s, L);
+        if (e == hipSuccess)
+            e = launch_codec(a, kHop, local_of_kind(local_kind), max_part_sg(p, 2 * sp.m), p->qmax == 16, s);
+        if (e == hipSuccess) e = timed_end(p, L, s);
+        return hip_status(e);
+    }
+    // one launch per output region: the part itself, or (own-fp32 variant,
+    // whose kept child takes another mode) each of its two children
+    const int nout = sp.two_children ? 2 : 1;
     for (int h = 0; h < nout && e == hipSuccess; h++) {
         const int64_t m_out = sp.two_children ? 2 * sp.m : sp.m;
         const int64_t c_out = sp.two_children ? 2 * sp.part + h : sp.part;

@@ -75,6 +75,12 @@ struct CodecArgs {
     const float *partial_in;                 // own fp32 partial sums (own-fp32 variant)
     float *partial_out;                      // kPartial output: fp32 partial sums of the part
     uint8_t *out;                            // output region of (m_out, part_out)
+    // a hop that writes both children of its part in one launch: the second
+    // child's part entry and region (null: one output); blocks [0, split)
+    // write the first child, the others the second
+    const PartInfo *part_out2;
+    uint8_t *out2;
+    uint32_t split;
     float *out_f32;                          // finalize output, original order
     float n_workers_f;                       // finalize: fl(n * mu)
     uint32_t key0, key1, round, tag, stagger;

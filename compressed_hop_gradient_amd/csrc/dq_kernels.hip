@@ -663,10 +663,17 @@ void k_codec(CodecArgs a) {
         for (int i = threadIdx.x; i < (int)(sizeof(SharedTables) / 16); i += blockDim.x) dst[i] = src[i];
     }
     __syncthreads();
+    // A hop that writes both children of its part runs as one launch, so that
+    // the two share one tail: blocks [0, split) write the first child and the
+    // others the second.  The choice is per block, so the layouts stay in
+    // scalar registers; a launch with one output has split = gridDim.x.
+    const bool second = blockIdx.x >= a.split;
+    const uint32_t blk = second ? blockIdx.x - a.split : blockIdx.x;
+    const uint32_t nblk = second ? gridDim.x - a.split : a.split;
     // part layouts: uniform loads from the per-round part table
-    const PartInfo Po = *a.part_out, Pi = *a.part_in;
+    const PartInfo Po = *(second ? a.part_out2 : a.part_out), Pi = *a.part_in;
     const RegionBase In = region_base(a.region_in, Pi), Own = region_base(a.region_own, Pi);
-    const RegionBase Out = region_base(a.out, Po);
+    const RegionBase Out = region_base(second ? a.out2 : a.out, Po);
     const PartU32 po = part_u32(Po), pi = part_u32(Pi);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -691,10 +698,10 @@ void k_codec(CodecArgs a) {
         return tt < pre1 ? lo0 + tt
                          : (tt < pre2 ? lo1 + (tt - pre1) : (tt < pre3 ? lo2 + (tt - pre2) : lo3 + (tt - pre3)));
     };
-    const uint32_t stride = gridDim.x * kSGPerBlock;
+    const uint32_t stride = nblk * kSGPerBlock;
     constexpr bool kAhead = codec_ahead<MODE, LOCAL>();
     if (kAhead) {
-        const uint32_t t0 = blockIdx.x * kSGPerBlock + wave * 4 + row;
+        const uint32_t t0 = blk * kSGPerBlock + wave * 4 + row;
         if (t0 < N && g == 0) {
             const uint32_t p0 = pos_of(t0);
             *slot_j = (uint32_t)a.perm[p0];
@@ -703,7 +710,7 @@ void k_codec(CodecArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
     }
-    for (uint32_t base = blockIdx.x * kSGPerBlock; base < N; base += stride) {
+    for (uint32_t base = blk * kSGPerBlock; base < N; base += stride) {
         const uint32_t t = base + wave * 4 + row;
         if (t >= N) continue;
         uint32_t j = 0u;
@@ -1764,11 +1771,16 @@ static dim3 codec_grid(int64_t n, int64_t blocks_per_cu, int64_t sg_per_block) {
     return dim3(grid_for(n, sg_per_block, wave * waves));
 }
 
+// With a second output (both children of a hop's part) the grid holds each
+// child's own grid, one after the other, and split marks the boundary.
 template <int MODE, int LOCAL, bool WIDE>
 static hipError_t launch_codec_w(const CodecArgs &a, int64_t max_sg, hipStream_t s) {
     using Shape = CodecShape<MODE, LOCAL, WIDE>;
-    hipLaunchKernelGGL((k_codec<MODE, LOCAL, WIDE>), codec_grid(max_sg, Shape::blocks_per_cu, Shape::sg_per_block),
-                       dim3(Shape::threads), 0, s, a);
+    const dim3 one = codec_grid(max_sg, Shape::blocks_per_cu, Shape::sg_per_block);
+    CodecArgs b = a;
+    b.split = one.x;
+    const dim3 grid(a.out2 ? 2 * one.x : one.x);
+    hipLaunchKernelGGL((k_codec<MODE, LOCAL, WIDE>), grid, dim3(Shape::threads), 0, s, b);
     return hipGetLastError();
 }
 

@@ -548,6 +548,24 @@ def test_timing_counts_coordinates():
     assert all(v["ms"] >= 0 for v in t.values())
 
 
+@pytest.mark.parametrize("own,per_level", [(dq.OWN_PACKED, 8), (dq.OWN_F32, 16)], ids=["packed-own", "fp32-own"])
+def test_timing_counts_butterfly_launches(own, per_level):
+    """A hop that writes both children of its part is one launch, timed as
+    the parent part; the fp32 own-partial variant writes its kept child in
+    another mode and keeps a launch per child.  Per round of 8 workers:
+    level 1 covers 4 J super-groups, level 2 covers 2 J, level 3 covers J."""
+    _need_gpu()
+    grads = _scaled("gemma", 999)
+    p = dq.Plan(grads[0].numel(), 8, dq.BUTTERFLY, 5.0, own=own, timing=True)
+    p.allreduce(grads)
+    t = p.timing()
+    J = p.J
+    assert t["compress"]["launches"] == 8 and t["compress"]["coords"] == 4 * J * 256
+    assert t["hop_grad"]["launches"] == per_level and t["hop_grad"]["coords"] == 4 * J * 256
+    assert t["hop_packed"]["launches"] == per_level and t["hop_packed"]["coords"] == 2 * J * 256
+    assert t["hop_final"]["launches"] == 8 and t["hop_final"]["coords"] == J * 256
+
+
 # ---------------------------------------------------------------------------
 # butterfly variant: the kept child stays fp32 (DQ_OWN_F32)
 # ---------------------------------------------------------------------------
