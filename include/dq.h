@@ -296,8 +296,10 @@ dq_status dq_compress(dq_plan *plan, int32_t worker, int32_t step, const void *d
  *     written as fp32 partial sums (>= dq_partial_bytes_max of its m) instead of
  *     a region, and the local at s >= 2 is that buffer (kind DQ_F32_PARTIAL).
  * d_region_in is the region of the same part produced by the previous hop (or
- * compress) of the sending worker.  Errors: DQ_ENULL, DQ_EINVAL, DQ_ESTATE,
- * DQ_EHIP. */
+ * compress) of the sending worker.  A step that writes two child regions is
+ * one kernel launch (DQ_OPT_TIMING records it once, as the parent part), except
+ * under DQ_OWN_F32, where each child is a launch of its own.  Errors: DQ_ENULL,
+ * DQ_EINVAL, DQ_ESTATE, DQ_EHIP. */
 dq_status dq_hop(dq_plan *plan, int32_t worker, int32_t step, const void *d_region_in,
                  const void *d_local, int32_t local_kind, void *d_region_out0,
                  void *d_region_out1, void *stream);
