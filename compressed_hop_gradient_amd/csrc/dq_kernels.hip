@@ -223,23 +223,31 @@ __device__ __forceinline__ uint32_t search_levels16(float v, const float *L, con
     const float u = v < 0.0f ? -t : t;
     int r0 = (int)floorf((u + 1.0f) * 32767.5f);
     r0 = min(max(r0, 1), 65533);
+    // The window's answer and its test are formed without a branch, so that
+    // all four loads are needed up front and go out together (one memory
+    // round trip); with a short-circuit test the compiler sank them into
+    // the branches and waited for each in turn.
     const Pair p0 = LW[r0 - 1], p1 = LW[r0], p2 = LW[r0 + 1];
     const float l3 = L[r0 + 2];
-    if (__builtin_expect(p0.l <= v && (v < l3 || r0 == 65533), 1)) {
-        const int k = (v >= p1.l ? 1 : 0) + (v >= p2.l ? 1 : 0);
-        Lr = k == 0 ? p0.l : (k == 1 ? p1.l : p2.l);
-        Wr = k == 0 ? p0.w : (k == 1 ? p1.w : p2.w);
-        return (uint32_t)(r0 - 1 + k);
+    const int k = (v >= p1.l ? 1 : 0) + (v >= p2.l ? 1 : 0);
+    float Lc = k == 0 ? p0.l : (k == 1 ? p1.l : p2.l);
+    float Wc = k == 0 ? p0.w : (k == 1 ? p1.w : p2.w);
+    int r = r0 - 1 + k;
+    const bool in_window = (p0.l <= v) & ((v < l3) | (r0 == 65533));
+    if (__builtin_expect(!in_window, 0)) {
+        int lo = 0, hi = 65534;
+        while (lo < hi) {
+            const int mid = lo + (hi - lo + 1) / 2;
+            if (L[mid] <= v) lo = mid;
+            else hi = mid - 1;
+        }
+        r = lo;
+        Lc = LW[lo].l;
+        Wc = LW[lo].w;
     }
-    int lo = 0, hi = 65534;
-    while (lo < hi) {
-        const int mid = lo + (hi - lo + 1) / 2;
-        if (L[mid] <= v) lo = mid;
-        else hi = mid - 1;
-    }
-    Lr = LW[lo].l;
-    Wr = LW[lo].w;
-    return (uint32_t)lo;
+    Lr = Lc;
+    Wr = Wc;
+    return (uint32_t)r;
 }
 
 // 2-bit search: two compares against the inner levels c1 = L[1], c2 = L[2]
